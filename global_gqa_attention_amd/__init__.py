@@ -1,0 +1,184 @@
+"""MiMo-V2.6-Flash attention on AMD Instinct MI355X (gfx950): thin Python binding of libmimo_attn.so.
+
+Every function here only checks shapes and dtypes, allocates outputs with torch (device memory and
+streams are torch's), and passes raw pointers to the C ABI declared in ``include/mimo_attn.h``.  All
+arithmetic runs in the HIP kernels of ``csrc/``.  There is no fallback: if the library is missing or the
+tensors are not on a GPU, the call raises.
+
+Layer (miles docs "MiMo-V2.6-Flash" sections 1, 5.1, 5.4; miles PR "feat(models): add MiMo-V2.6-Flash-RL
+support"): GQA with 192-dim Q/K and 128-dim V, V scaled by 0.707, partial RoPE on the first 64 dims
+(base 1e4 on sliding-window layers, 1e7 on global layers), sliding window of the query plus 128 previous
+keys with a per-head sink on the sliding-window layers, plain causal attention on global layers, THD
+packing through cu_seqlens.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmimo_attn.so")
+DQK = 192
+DV = 128
+
+MIMO_OK = 0
+_lib = None
+
+
+class MimoAttnError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded C library (loads it on first use; raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MimoAttnError(f"{LIB_PATH} is missing: build it with `python -m global_gqa_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, f64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
+        L.mimo_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P]
+        L.mimo_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mimo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
+        L.mimo_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mimo_attn_decode.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
+        L.mimo_attn_status_string.argtypes = [ctypes.c_int]
+        L.mimo_attn_last_error.argtypes = []
+        L.mimo_attn_release.argtypes = []
+        for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode"):
+            getattr(L, f).restype = ctypes.c_int
+        L.mimo_attn_bwd_workspace_size.restype = sz
+        L.mimo_attn_decode_workspace_size.restype = sz
+        L.mimo_attn_status_string.restype = ctypes.c_char_p
+        L.mimo_attn_last_error.restype = ctypes.c_char_p
+        L.mimo_attn_release.restype = None
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != MIMO_OK:
+        L = lib()
+        raise MimoAttnError(f"{what}: {L.mimo_attn_status_string(rc).decode()}: {L.mimo_attn_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise MimoAttnError(f"{name} must be on a GPU (there is no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _layer_checks(q, k, v, sink, cu_seqlens):
+    _need(q, "q", torch.bfloat16)
+    T, hq = q.shape[0], q.shape[1]
+    _need(k, "k", torch.bfloat16)
+    hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16, (T, hq, DQK))
+    _need(k, "k", torch.bfloat16, (T, hkv, DQK))
+    _need(v, "v", torch.bfloat16, (T, hkv, DV))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (hq,))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of batch+1 entries")
+    return T, hq, hkv, cu_seqlens.numel() - 1
+
+
+def fwd(q, k, v, sink, cu_seqlens, max_seqlen, window, rope_base, out=None, lse=None, return_lse=True):
+    """Forward of one layer.  Returns (out bf16 [T,hq,128], lse fp32 [hq,T] or None)."""
+    T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
+    if out is None:
+        out = torch.empty((T, hq, DV), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (T, hq, DV))
+    if return_lse and lse is None:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (hq, T))
+    rc = lib().mimo_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(cu_seqlens), batch, T, int(max_seqlen),
+                             int(window), float(rope_base), hq, hkv, _ptr(out), _ptr(lse), _stream(q.device))
+    _check(rc, "mimo_attn_fwd")
+    return out, lse
+
+
+def bwd_workspace_size(total_tokens, n_q_heads, n_kv_heads, window) -> int:
+    return int(lib().mimo_attn_bwd_workspace_size(int(total_tokens), int(n_q_heads), int(n_kv_heads), int(window)))
+
+
+def bwd(q, k, v, sink, out, lse, dout, cu_seqlens, max_seqlen, window, rope_base, workspace=None, grads=None):
+    """Backward of one layer.  Returns (dq, dk, dv, dsink or None)."""
+    T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
+    _need(out, "out", torch.bfloat16, (T, hq, DV))
+    _need(dout, "dout", torch.bfloat16, (T, hq, DV))
+    _need(lse, "lse", torch.float32, (hq, T))
+    if grads is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        dsink = torch.empty((hq,), dtype=torch.float32, device=q.device) if sink is not None else None
+    else:
+        dq, dk, dv, dsink = grads
+    need = bwd_workspace_size(T, hq, hkv, window)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    rc = lib().mimo_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout),
+                             _ptr(cu_seqlens), batch, T, int(max_seqlen), int(window), float(rope_base), hq, hkv,
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), _ptr(workspace), workspace.numel(),
+                             _stream(q.device))
+    _check(rc, "mimo_attn_bwd")
+    return dq, dk, dv, dsink
+
+
+def decode_workspace_size(batch, max_cache_len, n_q_heads, window) -> int:
+    return int(lib().mimo_attn_decode_workspace_size(int(batch), int(max_cache_len), int(n_q_heads), int(window)))
+
+
+def decode(q, k_new, v_new, k_cache, v_cache, cu_cache, positions, sink, max_cache_len, window, rope_base,
+           out=None, workspace=None):
+    """One decode step.  Returns out bf16 [batch, hq, 128]."""
+    _need(q, "q", torch.bfloat16)
+    B, hq = q.shape[0], q.shape[1]
+    hkv = k_new.shape[1]
+    _need(q, "q", torch.bfloat16, (B, hq, DQK))
+    _need(k_new, "k_new", torch.bfloat16, (B, hkv, DQK))
+    _need(v_new, "v_new", torch.bfloat16, (B, hkv, DV))
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16)
+    if k_cache.dim() != 3 or k_cache.shape[1:] != (hkv, DQK) or v_cache.shape != (k_cache.shape[0], hkv, DV):
+        raise ValueError("cache shapes must be [rows, n_kv_heads, 192] and [rows, n_kv_heads, 128]")
+    _need(cu_cache, "cu_cache", torch.int32, (B + 1,))
+    _need(positions, "positions", torch.int32, (B,))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (hq,))
+    if out is None:
+        out = torch.empty((B, hq, DV), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, hq, DV))
+    need = decode_workspace_size(B, max_cache_len, hq, window)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    rc = lib().mimo_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cu_cache),
+                                _ptr(positions), _ptr(sink), B, int(max_cache_len), int(window), float(rope_base),
+                                hq, hkv, _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(rc, "mimo_attn_decode")
+    return out
+
+
+def release():
+    """Free the library's cached RoPE tables."""
+    lib().mimo_attn_release()

@@ -1,0 +1,299 @@
+// api.hip -- the extern "C" entry points declared in include/mimo_attn.h.
+//
+// Host-only argument checks (no device data is read), the per-device RoPE cos/sin table cache, workspace
+// carving, and dispatch to the kernel launchers.  Nothing here allocates per call; the only allocation is
+// a RoPE table the first time a (device, rope_base) pair needs more positions than cached.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "internal.hpp"
+#include "mimo_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mimo_status_t fail(mimo_status_t s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+mimo_status_t ok()
+{
+    g_last_error.clear();
+    return MIMO_OK;
+}
+
+mimo_status_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(MIMO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- RoPE table cache: key (device, bits of rope_base) -> table of at least npos positions.
+struct Table {
+    float2 *ptr = nullptr;
+    int npos = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, uint64_t>, Table> g_tables;
+std::vector<std::pair<int, void *>> g_retired;  // grown-out tables, kept until release (may be in use)
+
+mimo_status_t rope_table(double base, int need, hipStream_t stream, const float2 **out, int *npos)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    uint64_t bits;
+    memcpy(&bits, &base, sizeof bits);
+    std::lock_guard<std::mutex> lock(g_mu);
+    Table &t = g_tables[{dev, bits}];
+    if (t.npos < need) {
+        int n = 4096;
+        while (n < need) n = n < (1 << 30) ? n * 2 : need;
+        float2 *p = nullptr;
+        e = hipMalloc(&p, (size_t)n * 32 * sizeof(float2));
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(rope table)");
+        e = mimo::launch_rope_table(p, n, base, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);  // other streams may use it right away
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "building the rope table");
+        }
+        if (t.ptr) g_retired.push_back({dev, t.ptr});
+        t.ptr = p;
+        t.npos = n;
+    }
+    *out = t.ptr;
+    *npos = t.npos;
+    return MIMO_OK;
+}
+
+constexpr int kDQK = 192, kDV = 128;
+
+mimo_status_t check_layer(const void *q, const void *k, const void *v, const int32_t *cu, int32_t batch,
+                          int32_t T, int32_t max_seqlen, int32_t window, double rope_base, int32_t hq,
+                          int32_t hkv)
+{
+    if (batch < 0) return fail(MIMO_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+    if (T < 0) return fail(MIMO_ERR_INVALID_ARG, "total_tokens must be >= 0 (got %d)", T);
+    if (max_seqlen < 0) return fail(MIMO_ERR_INVALID_ARG, "max_seqlen must be >= 0 (got %d)", max_seqlen);
+    if (T > 0 && max_seqlen == 0) return fail(MIMO_ERR_INVALID_ARG, "max_seqlen is 0 but total_tokens > 0");
+    if (T > 0 && batch == 0) return fail(MIMO_ERR_INVALID_ARG, "total_tokens > 0 with batch 0");
+    if (window < -1) return fail(MIMO_ERR_INVALID_ARG, "window must be -1 or >= 0 (got %d)", window);
+    if (hq <= 0 || hkv <= 0) return fail(MIMO_ERR_INVALID_ARG, "head counts must be positive");
+    if (hq % hkv != 0) return fail(MIMO_ERR_INVALID_ARG, "n_q_heads (%d) %% n_kv_heads (%d) != 0", hq, hkv);
+    if (!(rope_base > 1.0) || !isfinite(rope_base))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_base must be finite and > 1 (got %g)", rope_base);
+    if (T > 0 && (!q || !k || !v || !cu)) return fail(MIMO_ERR_INVALID_ARG, "null input pointer");
+    if (batch > 0 && !cu) return fail(MIMO_ERR_INVALID_ARG, "cu_seqlens is null");
+    if ((long long)T * hq * kDQK > (1LL << 40)) return fail(MIMO_ERR_UNSUPPORTED, "tensor too large");
+    return MIMO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mimo_attn_status_string(mimo_status_t s)
+{
+    switch (s) {
+    case MIMO_OK: return "MIMO_OK";
+    case MIMO_ERR_INVALID_ARG: return "MIMO_ERR_INVALID_ARG";
+    case MIMO_ERR_UNSUPPORTED: return "MIMO_ERR_UNSUPPORTED";
+    case MIMO_ERR_HIP: return "MIMO_ERR_HIP";
+    case MIMO_ERR_WORKSPACE: return "MIMO_ERR_WORKSPACE";
+    }
+    return "MIMO_ERR_UNKNOWN";
+}
+
+const char *mimo_attn_last_error(void) { return g_last_error.c_str(); }
+
+void mimo_attn_release(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (auto &kv : g_tables) {
+        if (kv.second.ptr) {
+            (void)hipSetDevice(kv.first.first);
+            (void)hipFree(kv.second.ptr);
+        }
+    }
+    for (auto &r : g_retired) {
+        (void)hipSetDevice(r.first);
+        (void)hipFree(r.second);
+    }
+    (void)hipSetDevice(cur);
+    g_tables.clear();
+    g_retired.clear();
+}
+
+mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
+                            const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
+                            int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
+                            int32_t n_kv_heads, void *out, float *lse, void *stream)
+{
+    mimo_status_t s = check_layer(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base,
+                                  n_q_heads, n_kv_heads);
+    if (s != MIMO_OK) return s;
+    if (total_tokens > 0 && !out) return fail(MIMO_ERR_INVALID_ARG, "out is null");
+    if (!mimo::fwd_group_supported(n_q_heads / n_kv_heads))
+        return fail(MIMO_ERR_UNSUPPORTED, "no forward kernel for group size %d", n_q_heads / n_kv_heads);
+    if (total_tokens == 0) return ok();
+    hipStream_t st = (hipStream_t)stream;
+    mimo::FwdArgs a{};
+    s = rope_table(rope_base, max_seqlen, st, &a.L.rope, &a.L.rope_len);
+    if (s != MIMO_OK) return s;
+    a.L.q = (const uint16_t *)q;
+    a.L.k = (const uint16_t *)k;
+    a.L.v = (const uint16_t *)v;
+    a.L.sink = sink;
+    a.L.cu = cu_seqlens;
+    a.L.batch = batch;
+    a.L.T = total_tokens;
+    a.L.window = window;
+    a.L.hq = n_q_heads;
+    a.L.hkv = n_kv_heads;
+    a.L.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kDQK));
+    a.out = (uint16_t *)out;
+    a.lse = lse;
+    hipError_t e = mimo::launch_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return ok();
+}
+
+size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t window)
+{
+    if (total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
+    return mimo::bwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
+}
+
+mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const float *sink,
+                            const void *out, const float *lse, const void *dout,
+                            const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
+                            int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
+                            int32_t n_kv_heads, void *dq, void *dk, void *dv, float *dsink,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    mimo_status_t s = check_layer(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base,
+                                  n_q_heads, n_kv_heads);
+    if (s != MIMO_OK) return s;
+    if ((sink == nullptr) != (dsink == nullptr))
+        return fail(MIMO_ERR_INVALID_ARG, "dsink must be given exactly when sink is given");
+    if (total_tokens > 0 && (!out || !lse || !dout || !dq || !dk || !dv))
+        return fail(MIMO_ERR_INVALID_ARG, "null pointer among out/lse/dout/dq/dk/dv");
+    if (!mimo::bwd_group_supported(n_q_heads / n_kv_heads))
+        return fail(MIMO_ERR_UNSUPPORTED, "no backward kernel for group size %d", n_q_heads / n_kv_heads);
+    const size_t need = mimo::bwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
+    if (total_tokens > 0 && (!workspace || workspace_bytes < need))
+        return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    if (total_tokens == 0) {
+        if (dsink) {
+            hipError_t e = hipMemsetAsync(dsink, 0, sizeof(float) * n_q_heads, st);
+            if (e != hipSuccess) return hip_fail(e, "clearing dsink");
+        }
+        return ok();
+    }
+    mimo::BwdArgs a{};
+    s = rope_table(rope_base, max_seqlen, st, &a.L.rope, &a.L.rope_len);
+    if (s != MIMO_OK) return s;
+    a.L.q = (const uint16_t *)q;
+    a.L.k = (const uint16_t *)k;
+    a.L.v = (const uint16_t *)v;
+    a.L.sink = sink;
+    a.L.cu = cu_seqlens;
+    a.L.batch = batch;
+    a.L.T = total_tokens;
+    a.L.window = window;
+    a.L.hq = n_q_heads;
+    a.L.hkv = n_kv_heads;
+    a.L.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kDQK));
+    a.out = (const uint16_t *)out;
+    a.dout = (const uint16_t *)dout;
+    a.lse = lse;
+    a.dq = (uint16_t *)dq;
+    a.dk = (uint16_t *)dk;
+    a.dv = (uint16_t *)dv;
+    a.dsink = dsink;
+    // workspace: D [hq, T] fp32, then the dsink partials
+    char *ws = (char *)workspace;
+    a.delta = (float *)ws;
+    size_t off = ((size_t)n_q_heads * total_tokens * sizeof(float) + 255) & ~(size_t)255;
+    a.dsink_part = (float *)(ws + off);
+    hipError_t e = mimo::launch_bwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return ok();
+}
+
+size_t mimo_attn_decode_workspace_size(int32_t batch, int32_t max_cache_len, int32_t n_q_heads,
+                                       int32_t window)
+{
+    if (batch < 0 || max_cache_len < 0 || n_q_heads <= 0) return 0;
+    return mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, window);
+}
+
+mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                               const void *v_cache, const int32_t *cu_cache, const int32_t *positions,
+                               const float *sink, int32_t batch, int32_t max_cache_len, int32_t window,
+                               double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (batch < 0) return fail(MIMO_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+    if (max_cache_len < 0) return fail(MIMO_ERR_INVALID_ARG, "max_cache_len must be >= 0");
+    if (window < -1) return fail(MIMO_ERR_INVALID_ARG, "window must be -1 or >= 0 (got %d)", window);
+    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+        return fail(MIMO_ERR_INVALID_ARG, "bad head counts %d / %d", n_q_heads, n_kv_heads);
+    if (!(rope_base > 1.0) || !isfinite(rope_base))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_base must be finite and > 1 (got %g)", rope_base);
+    if (batch == 0) return ok();
+    if (!q || !k_new || !v_new || !cu_cache || !positions || !out)
+        return fail(MIMO_ERR_INVALID_ARG, "null pointer among q/k_new/v_new/cu_cache/positions/out");
+    if (max_cache_len > 0 && (!k_cache || !v_cache)) return fail(MIMO_ERR_INVALID_ARG, "null cache pointer");
+    if (!mimo::decode_group_supported(n_q_heads / n_kv_heads))
+        return fail(MIMO_ERR_UNSUPPORTED, "no decode kernel for group size %d", n_q_heads / n_kv_heads);
+    const size_t need = mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, window);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    mimo::DecodeArgs a{};
+    a.q = (const uint16_t *)q;
+    a.k_new = (const uint16_t *)k_new;
+    a.v_new = (const uint16_t *)v_new;
+    a.k_cache = (const uint16_t *)k_cache;
+    a.v_cache = (const uint16_t *)v_cache;
+    a.cu_cache = cu_cache;
+    a.positions = positions;
+    a.sink = sink;
+    a.out = (uint16_t *)out;
+    a.batch = batch;
+    a.window = window;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.rope_base = rope_base;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kDQK));
+    mimo::decode_split_plan(batch, max_cache_len, n_q_heads, n_kv_heads, window, &a.splits, &a.split_len);
+    char *ws = (char *)workspace;
+    a.part_o = (float *)ws;
+    size_t off = ((size_t)batch * n_q_heads * a.splits * kDV * sizeof(float) + 255) & ~(size_t)255;
+    a.part_ml = (float *)(ws + off);
+    hipError_t e = mimo::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+}  // extern "C"

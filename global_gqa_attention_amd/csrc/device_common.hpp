@@ -1,0 +1,67 @@
+// device_common.hpp -- small gfx950 building blocks shared by the attention kernels.
+//
+// MFMA lane layouts used throughout (checked on gfx950 for v_mfma_f32_32x32x16_bf16):
+//   A operand (32 x 16): lane l holds row l % 32, k = 8 * (l / 32) + t for t = 0..7
+//   B operand (16 x 32): lane l holds column l % 32, k = 8 * (l / 32) + t
+//   C / D     (32 x 32): lane l holds column l % 32, slot j = row 8 * (j / 4) + 4 * (l / 32) + j % 4
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mimo {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int DQK = 192;    // Q/K head width
+constexpr int DVV = 128;    // V head width
+constexpr int NHALF = 32;   // rotary pairs: dims (d, d + 32) for d < 32; 64 rotated dims in all
+constexpr float VSCALE = 0.707f;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+__device__ __forceinline__ __bf16 f2bf(float x) { return (__bf16)x; }  // round to nearest even
+
+__device__ __forceinline__ bf16x8 ld16(const u16 *p) { return __builtin_bit_cast(bf16x8, *(const uint4 *)p); }
+__device__ __forceinline__ uint4 ldu4(const u16 *p) { return *(const uint4 *)p; }
+__device__ __forceinline__ void st16(u16 *p, bf16x8 x) { *(uint4 *)p = __builtin_bit_cast(uint4, x); }
+__device__ __forceinline__ void st16u(u16 *p, uint4 x) { *(uint4 *)p = x; }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Values of lanes l and l ^ 32 combined: v_permlane32_swap gives every lane the lower-half value in .x and
+// the upper-half value in .y of its pair.
+__device__ __forceinline__ float pair_max(float v)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Rotate-half RoPE of one 8-wide chunk pair: x0 holds dims d..d+7 (d < 32), x1 dims d+32..d+39, cs the
+// (cos, sin) of the 8 matching frequencies.  Rounded back to bf16 (the MFMA operand precision).
+__device__ __forceinline__ void rope_pair(bf16x8 &x0, bf16x8 &x1, const float2 *cs)
+{
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        float a = bf2f(x0[t]), b = bf2f(x1[t]);
+        float c = cs[t].x, s = cs[t].y;
+        x0[t] = f2bf(a * c - b * s);
+        x1[t] = f2bf(b * c + a * s);
+    }
+}
+
+}  // namespace mimo

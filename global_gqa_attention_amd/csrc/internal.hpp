@@ -1,0 +1,62 @@
+// internal.hpp -- argument blocks and launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mimo {
+
+// One prefill layer (forward or backward).  All pointers are device pointers.
+struct LayerArgs {
+    const uint16_t *q, *k, *v;     // bf16 [T,hq,192], [T,hkv,192], [T,hkv,128]
+    const float *sink;             // [hq] or nullptr
+    const int32_t *cu;             // [batch+1]
+    const float2 *rope;            // (cos, sin) [rope_len, 32]
+    int batch, T, window, hq, hkv, rope_len;
+    float scale_log2;              // log2(e) / sqrt(192)
+};
+
+struct FwdArgs {
+    LayerArgs L;
+    uint16_t *out;                 // bf16 [T,hq,128]
+    float *lse;                    // fp32 [hq,T] or nullptr
+};
+
+struct BwdArgs {
+    LayerArgs L;
+    const uint16_t *out, *dout;    // bf16 [T,hq,128]
+    const float *lse;              // [hq,T]
+    uint16_t *dq, *dk, *dv;        // bf16 outputs
+    float *dsink;                  // [hq] or nullptr
+    float *delta;                  // workspace: D = rowsum(dO * O) [hq,T]
+    float *dsink_part;             // workspace: per-block partial dsink sums
+    int dsink_blocks;              // number of partial blocks per head
+};
+
+struct DecodeArgs {
+    const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
+    const int32_t *cu_cache, *positions;
+    const float *sink;
+    uint16_t *out;
+    float *part_o;                 // workspace [batch, hq, splits, 128]
+    float *part_ml;                // workspace [batch, hq, splits, 2] (max in log2 units, sum)
+    int batch, window, hq, hkv, splits, split_len;
+    double rope_base;
+    float scale_log2;
+};
+
+// Returns hipSuccess or the launch error.  Each launcher picks its kernel variant from the arguments.
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_rope_table(float2 *table, int npos, double base, hipStream_t stream);
+
+// Head-group sizes (n_q_heads / n_kv_heads) with compiled kernels.
+bool fwd_group_supported(int group);
+bool bwd_group_supported(int group);
+bool decode_group_supported(int group);
+
+size_t bwd_workspace_bytes(int T, int hq, int hkv, int window);
+size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window);
+void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window, int *splits, int *split_len);
+
+}  // namespace mimo

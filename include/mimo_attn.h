@@ -1,0 +1,134 @@
+/*
+ * mimo_attn.h -- C ABI of the MiMo-V2.6-Flash attention layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources, cited by page title and section):
+ *   - miles docs "MiMo-V2.6-Flash", section 1 "Model Introduction": hybrid attention with 39 sliding-window
+ *     layers (window 128, learnable attention sink) and 9 global layers, 8 vs 4 KV heads, RoPE bases 1e4 vs
+ *     1e7; 192-dim Q/K and 128-dim V, V scaled by 0.707, partial RoPE on 64 of 192 dims.
+ *   - miles docs "MiMo-V2.6-Flash", section 5.4 "Notable quirks": a sliding-window query sees itself plus
+ *     the 128 previous keys (129 in total), window_size = (128, 0); section 5.1 "Parallelism": THD packing of
+ *     variable-length samples.
+ *   - miles pull request "feat(models): add MiMo-V2.6-Flash-RL support", PR body and commit messages: the
+ *     core attention receives (k_channels, v_channels) = (192, 128) and the sink setting, and scales V.
+ *
+ * What every call computes, for query token i of sequence b (position p = i - cu_seqlens[b]) and query
+ * head h, with G = n_q_heads / n_kv_heads and kv = h / G:
+ *   q' = RoPE(q[i,h], p), k'_j = RoPE(k[j,kv], p_j): dims 0..63 rotated in rotate-half pairs (d, d+32) by
+ *   angle p * rope_base^(-d/32), d = 0..31; dims 64..191 pass through.
+ *   s_j = q'.k'_j / sqrt(192) for keys j of the same sequence with j <= i and, when window >= 0,
+ *   j >= i - window (window = 128 gives 129 keys); window = -1 is plain causal attention.
+ *   LSE = ln(exp(sink[h]) + sum_j exp(s_j))   (the sink term is absent when sink == NULL)
+ *   out[i,h] = sum_j exp(s_j - LSE) * 0.707 * v[j,kv]
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous, row-major, in the shapes given.
+ *     bf16 means IEEE bfloat16 bit patterns (uint16 storage).  Outputs are fully overwritten.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null stream).  There is
+ *     no host synchronisation and no device-data validation: cu_seqlens must be non-decreasing with
+ *     cu_seqlens[0] = 0 and cu_seqlens[batch] = total_tokens, and no sequence may be longer than max_seqlen.
+ *   - Argument checks happen on the host before anything is launched; a failing check returns
+ *     MIMO_ERR_INVALID_ARG or MIMO_ERR_UNSUPPORTED and launches nothing.  A launch failure returns
+ *     MIMO_ERR_HIP.  mimo_attn_last_error() gives a human-readable reason (thread-local).
+ *   - The library keeps one RoPE cos/sin table per (device, rope_base) that grows to the largest
+ *     max_seqlen seen; it is allocated on first use and freed by mimo_attn_release().
+ *   - Head dims are fixed at 192 (Q/K) and 128 (V); n_q_heads % n_kv_heads must be 0.
+ */
+#ifndef MIMO_ATTN_H
+#define MIMO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MIMO_OK = 0,
+    MIMO_ERR_INVALID_ARG = 1,   /* a null pointer, a negative size, heads not divisible, window < -1 ... */
+    MIMO_ERR_UNSUPPORTED = 2,   /* valid but not built: e.g. a GQA group size this build has no kernel for */
+    MIMO_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
+    MIMO_ERR_WORKSPACE = 4      /* workspace NULL or smaller than the matching *_workspace_size() */
+} mimo_status_t;
+
+/* Forward attention of one layer over a THD-packed batch (the training / prefill forward).
+ *   q     bf16 [total_tokens, n_q_heads, 192]   un-rotated (RoPE is applied inside)
+ *   k     bf16 [total_tokens, n_kv_heads, 192]  un-rotated
+ *   v     bf16 [total_tokens, n_kv_heads, 128]  unscaled (the 0.707 factor is applied inside)
+ *   sink  fp32 [n_q_heads] learnable sink logits (unscaled; may be -inf), or NULL for no sink
+ *   cu_seqlens int32 [batch + 1] device; batch >= 0; max_seqlen >= every sequence length
+ *   window   -1 (causal) or >= 0 (the query plus `window` previous keys)
+ *   out   bf16 [total_tokens, n_q_heads, 128]
+ *   lse   fp32 [n_q_heads, total_tokens] natural-log softmax denominator incl. the sink, or NULL
+ * Source: miles docs "MiMo-V2.6-Flash" sections 1, 5.1, 5.4; miles PR "feat(models): add MiMo-V2.6-Flash-RL
+ * support" (core attention with asymmetric channels, sink, V scale). */
+mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
+                            const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
+                            int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
+                            int32_t n_kv_heads, void *out, float *lse, void *stream);
+
+/* Bytes of device workspace mimo_attn_bwd needs for these sizes (0 is never returned for valid sizes). */
+size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t window);
+
+/* Backward of mimo_attn_fwd (the training backward, "given the forward outputs").
+ *   q, k, v, sink, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base, heads: as the forward
+ *   out   bf16 [total_tokens, n_q_heads, 128]  forward output (used for D = rowsum(dO * O))
+ *   lse   fp32 [n_q_heads, total_tokens]       forward LSE
+ *   dout  bf16 [total_tokens, n_q_heads, 128]  upstream gradient dO
+ *   dq    bf16 [total_tokens, n_q_heads, 192]  gradient w.r.t. the un-rotated q
+ *   dk    bf16 [total_tokens, n_kv_heads, 192] gradient w.r.t. the un-rotated k (summed over the group)
+ *   dv    bf16 [total_tokens, n_kv_heads, 128] gradient w.r.t. the unscaled v (summed over the group)
+ *   dsink fp32 [n_q_heads] gradient of the sink logits; must be non-NULL exactly when sink is non-NULL
+ *   workspace: device memory of at least mimo_attn_bwd_workspace_size() bytes, owned by the caller,
+ *   needs no initialisation, and must not be shared with a concurrent call.
+ * dsink is summed in a fixed order (no float atomics), so it is bitwise repeatable.
+ * Source: the exact gradient of the forward above; miles docs "MiMo-V2.6-Flash" section 5.4 (the trainer's
+ * fused attention carries the sink in training). */
+mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const float *sink,
+                            const void *out, const float *lse, const void *dout,
+                            const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
+                            int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
+                            int32_t n_kv_heads, void *dq, void *dk, void *dv, float *dsink,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace mimo_attn_decode needs. */
+size_t mimo_attn_decode_workspace_size(int32_t batch, int32_t max_cache_len, int32_t n_q_heads,
+                                       int32_t window);
+
+/* One decode step: each of `batch` sequences has one new token at position positions[b].
+ *   q      bf16 [batch, n_q_heads, 192]   un-rotated query of the new token
+ *   k_new  bf16 [batch, n_kv_heads, 192]  un-rotated key of the new token
+ *   v_new  bf16 [batch, n_kv_heads, 128]  value of the new token (unscaled)
+ *   k_cache bf16 [rows, n_kv_heads, 192]  cached keys, ALREADY rotated at their own positions
+ *   v_cache bf16 [rows, n_kv_heads, 128]  cached values, unscaled
+ *   cu_cache int32 [batch + 1] device: sequence b owns cache rows cu_cache[b] .. cu_cache[b+1]-1, oldest
+ *            first; max_cache_len >= every cu_cache[b+1] - cu_cache[b]
+ *   positions int32 [batch] device: position of the new token (used to rotate q and k_new)
+ *   sink   fp32 [n_q_heads] or NULL; window -1 (all cached rows) or >= 0 (the last min(n_b, window) rows)
+ *   out    bf16 [batch, n_q_heads, 128]
+ *   workspace: at least mimo_attn_decode_workspace_size() bytes of device memory (split-KV partials).
+ * The cache is read, never written.  A 128-entry ring cache with window 128 is attended whole, so the ring
+ * order does not matter (softmax does not depend on the order of its keys).
+ * Source: miles PR "feat(models): add MiMo-V2.6-Flash-RL support", commit message on the rollout engine's
+ * window (query + 128 previous keys); miles docs section 3.2 (separate sliding-window KV pools). */
+mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                               const void *v_cache, const int32_t *cu_cache, const int32_t *positions,
+                               const float *sink, int32_t batch, int32_t max_cache_len, int32_t window,
+                               double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Name of a status code. */
+const char *mimo_attn_status_string(mimo_status_t s);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *mimo_attn_last_error(void);
+
+/* Frees the cached RoPE tables of every device.  No call may be in flight. */
+void mimo_attn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIMO_ATTN_H */

@@ -1,0 +1,117 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every declared symbol, and rejects bad
+arguments on the host before launching anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mimo_attn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mimo_attn_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import global_gqa_attention_amd as ga
+
+    if not os.path.exists(ga.LIB_PATH):
+        pytest.fail("libmimo_attn.so is not built (run __graft_entry__.build())")
+    return ga.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_bwd_workspace_size",
+              "mimo_attn_decode_workspace_size", "mimo_attn_status_string", "mimo_attn_last_error",
+              "mimo_attn_release"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in [(0, b"MIMO_OK"), (1, b"MIMO_ERR_INVALID_ARG"), (2, b"MIMO_ERR_UNSUPPORTED"),
+                       (3, b"MIMO_ERR_HIP"), (4, b"MIMO_ERR_WORKSPACE")]:
+        assert L.mimo_attn_status_string(code) == name
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails host validation first
+
+
+def fwd(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sink=None, cu=FAKE, batch=1, T=16, max_seqlen=16, window=128,
+             base=1e4, hq=64, hkv=8, out=FAKE, lse=None)
+    a.update(kw)
+    return L.mimo_attn_fwd(a["q"], a["k"], a["v"], a["sink"], a["cu"], a["batch"], a["T"], a["max_seqlen"],
+                           a["window"], a["base"], a["hq"], a["hkv"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hkv=7), 1), (dict(window=-2), 1), (dict(batch=-1), 1), (dict(T=-5), 1), (dict(q=None), 1),
+    (dict(out=None), 1), (dict(base=0.5), 1), (dict(base=float("inf")), 1), (dict(max_seqlen=0), 1),
+    (dict(batch=0), 1), (dict(hq=0), 1), (dict(cu=None), 1),
+])
+def test_fwd_rejects_bad_arguments(L, kw, code):
+    assert fwd(L, **kw) == code
+    assert L.mimo_attn_last_error() != b""
+
+
+def test_empty_batch_is_a_no_op(L):
+    assert fwd(L, batch=0, T=0, q=None, k=None, v=None, cu=FAKE, out=None) == 0
+
+
+def bwd(L, **kw):
+    a = dict(sink=None, dsink=None, ws=FAKE, wsb=1 << 30, hkv=8, T=16, window=128)
+    a.update(kw)
+    return L.mimo_attn_bwd(FAKE, FAKE, FAKE, a["sink"], FAKE, FAKE, FAKE, FAKE, 1, a["T"], 16, a["window"], 1e4,
+                           64, a["hkv"], FAKE, FAKE, FAKE, a["dsink"], a["ws"], a["wsb"], None)
+
+
+def test_bwd_rejects_bad_arguments(L):
+    assert bwd(L, sink=FAKE, dsink=None) == 1          # dsink must come with sink
+    assert bwd(L, sink=None, dsink=FAKE) == 1
+    assert bwd(L, ws=None) == 4                         # workspace missing
+    assert bwd(L, wsb=16) == 4                          # workspace too small
+    assert bwd(L, hkv=3) == 1
+
+
+def test_workspace_sizes(L):
+    n = L.mimo_attn_bwd_workspace_size(32768, 64, 8, 128)
+    assert n >= 32768 * 64 * 4
+    assert L.mimo_attn_decode_workspace_size(64, 131072, 64, -1) > 0
+    assert L.mimo_attn_bwd_workspace_size(-1, 64, 8, 128) == 0
+
+
+def test_decode_rejects_bad_arguments(L):
+    def dec(**kw):
+        a = dict(batch=4, hq=64, hkv=8, window=128, ws=FAKE, wsb=1 << 30, q=FAKE)
+        a.update(kw)
+        return L.mimo_attn_decode(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, a["batch"], 128, a["window"],
+                                  1e4, a["hq"], a["hkv"], FAKE, a["ws"], a["wsb"], None)
+    assert dec(hkv=5) == 1
+    assert dec(window=-3) == 1
+    assert dec(q=None) == 1
+    assert dec(ws=None) == 4
+    assert dec(batch=0) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    import global_gqa_attention_amd as ga
+
+    q = torch.zeros(4, 8, 192, dtype=torch.bfloat16)
+    k = torch.zeros(4, 8, 192, dtype=torch.bfloat16)
+    v = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ga.MimoAttnError):
+        ga.fwd(q, k, v, None, cu, 4, 128, 1e4)
