@@ -1,0 +1,260 @@
+"""Benchmark: attention TFLOP/s (forward + backward, SWA+sink and global layers) on the 32768-token THD batch.
+
+One step = the whole hot path of one training pass over the synthetic batch: the sliding-window layer
+(64 Q / 8 KV heads, window 128, sink, RoPE base 1e4) forward and backward, then the global layer (64 Q /
+4 KV heads, causal, base 1e7) forward and backward, with dO ~ N(0,1).  Inputs are resident in HBM before
+the timed region.  FLOPs are algorithmic: attended (query, key) pairs x 640 (forward) and x 1664 (backward).
+
+The decode step (batch 64, SWA ring of 128 + sink; global cache lengths in [8192, 131072]) is timed in the
+same run and reported as GB/s of cache traffic under "decode"; it is not part of the step's value.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, published
+FWD_FLOP_PER_PAIR = 2 * (192 + 128)
+BWD_FLOP_PER_PAIR = 2 * (3 * 192 + 2 * 128)
+# per-kernel algorithmic work: the dK/dV kernel does S, dP, dV, dK (2*(192+128+128+192) per pair); the dQ
+# kernel's new work is dQ (2*192 per pair; its S and dP are recomputation)
+KERNEL_FLOP_PER_PAIR = {"attn_fwd": FWD_FLOP_PER_PAIR, "bwd_dkdv": 2 * (192 + 128 + 128 + 192), "bwd_dq": 2 * 192}
+
+
+def pairs_per_head(lengths, window):
+    tot = 0
+    for L in lengths:
+        if window < 0 or L <= window + 1:
+            tot += L * (L + 1) // 2
+        else:
+            tot += (window + 1) * L - window * (window + 1) // 2
+    return tot
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "global_gqa_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if data.get("source_hash") != kernel_source_hash():
+        return None
+    rec = data.get("kernels", {}).get(kernel)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def cpu_baseline(thd, dout, nthreads):
+    """The fp64 oracle on a bounded sample of the same workload: the first two sequences of the batch for the
+    sliding-window layer and the first 1024 tokens of the first sequence for the global layer, forward and
+    backward, all 64 heads."""
+    import torch
+
+    import mimo_inputs as mi
+    import oracle
+
+    flops, secs, parts = 0.0, 0.0, []
+    for name, d, n_tok, lens in (
+        ("swa", thd["swa"], sum(thd["swa"]["lengths"][:2]), thd["swa"]["lengths"][:2]),
+        ("glb", thd["glb"], 1024, [1024]),
+    ):
+        q, k, v = d["q"][:n_tok], d["k"][:n_tok], d["v"][:n_tok]
+        cu = mi.cu_from_lengths(lens)
+        dO = dout[:n_tok]
+        t0 = time.perf_counter()
+        o, _ = oracle.prefill(q, k, v, d["sink"], cu, d["window"], d["rope_base"], nthreads=nthreads)
+        og = torch.from_numpy(o).to(torch.bfloat16)
+        oracle.prefill_bwd(q, k, v, d["sink"], dO, cu, d["window"], d["rope_base"], out_given=og,
+                           nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        p = pairs_per_head(lens, d["window"]) * q.shape[1]
+        flops += p * (FWD_FLOP_PER_PAIR + BWD_FLOP_PER_PAIR)
+        secs += dt
+        parts.append(f"{name}: {n_tok} tokens x 64 heads fwd+bwd in {dt:.1f}s")
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": "; ".join(parts) + " (fp64 C oracle, algorithmic FLOPs as the GPU line)"}
+
+
+def run_decode(ga, torch, mi, reps=20):
+    res = {}
+    for name, gen in (("swa", mi.decode_swa), ("global", mi.decode_global)):
+        d = gen(device="cuda")
+        cu = d["cu_cache"].cpu()
+        lens = (cu[1:] - cu[:-1]).tolist()
+        max_len = max(lens)
+        ws = torch.empty(ga.decode_workspace_size(64, max_len, 64, d["window"]), dtype=torch.uint8, device="cuda")
+        out = torch.empty(64, 64, 128, dtype=torch.bfloat16, device="cuda")
+        call = lambda: ga.decode(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["cu_cache"],  # noqa
+                                 d["positions"], d["sink"], max_len, d["window"], d["rope_base"], out, ws)
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")   # 512 MiB: evicts L2 and MALL
+        for _ in range(3):
+            call()
+        times = []
+        for _ in range(reps):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        hkv = d["n_kv_heads"]
+        rows = sum(min(n, d["window"]) if d["window"] >= 0 else n for n in lens)
+        cache_bytes = rows * hkv * (192 + 128) * 2
+        io_bytes = 64 * 64 * (192 + 128) * 2 + 64 * hkv * (192 + 128) * 2
+        keys = rows * (64 // hkv) + 64 * 64
+        res[name] = {"ms": round(ms, 4), "GB/s": round((cache_bytes + io_bytes) / ms / 1e6, 1),
+                     "hbm_frac": round((cache_bytes + io_bytes) / ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "TFLOP/s": round(keys * FWD_FLOP_PER_PAIR / ms / 1e9, 2), "cache_rows": rows}
+        del d, flush
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs the attention layer on a single MI355X and "
+              f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import global_gqa_attention_amd as ga
+    import mimo_inputs as mi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    thd = mi.thd_32k()
+    dout_cpu = mi.dout_like(32768, 4)
+    layers = {}
+    for name in ("swa", "glb"):
+        d = thd[name]
+        g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+        T, hq, hkv = g["q"].shape[0], g["q"].shape[1], g["k"].shape[1]
+        g["max_seqlen"] = max(d["lengths"])
+        g["out"] = torch.empty(T, hq, 128, dtype=torch.bfloat16, device=dev)
+        g["lse"] = torch.empty(hq, T, dtype=torch.float32, device=dev)
+        g["grads"] = (torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"]),
+                      torch.empty(hq, dtype=torch.float32, device=dev) if g["sink"] is not None else None)
+        g["ws"] = torch.empty(ga.bwd_workspace_size(T, hq, hkv, g["window"]), dtype=torch.uint8, device=dev)
+        g["pairs"] = pairs_per_head(d["lengths"], d["window"]) * hq
+        layers[name] = g
+    dout = dout_cpu.to(dev)
+
+    def step():
+        for g in layers.values():
+            ga.fwd(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], g["max_seqlen"], g["window"], g["rope_base"],
+                   out=g["out"], lse=g["lse"])
+            ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], dout, g["cu_seqlens"], g["max_seqlen"],
+                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ga.trace_read(clear=True)
+
+    ga.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ga.trace_enable(False)
+    trace = ga.trace_read(clear=True)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    flops = sum(g["pairs"] * (FWD_FLOP_PER_PAIR + BWD_FLOP_PER_PAIR) for g in layers.values())
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    # per-kernel averages over the timed region (HIP events on the launch stream)
+    per = {}
+    for name, ms in trace:
+        per.setdefault(name, []).append(ms)
+    kernels = {}
+    for name, v in per.items():
+        layer = "swa" if name.endswith("_swa") else ("glb" if name.endswith("_global") else None)
+        base = name.rsplit("_", 1)[0] if layer else name
+        avg = sum(v) / len(v)
+        rec = {"avg_ms": round(avg, 4), "launches": len(v)}
+        if layer and base in KERNEL_FLOP_PER_PAIR:
+            rec["TFLOP/s"] = round(layers[layer]["pairs"] * KERNEL_FLOP_PER_PAIR[base] / (avg * 1e-3) / 1e12, 1)
+        kernels[name] = rec
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    drec = kernels[dom]
+    layer = "swa" if dom.endswith("_swa") else "glb"
+    base = dom.rsplit("_", 1)[0]
+    ach = layers[layer]["pairs"] * KERNEL_FLOP_PER_PAIR.get(base, 0) / (drec["avg_ms"] * 1e-3) / 1e12
+    traffic = measured_traffic(dom)
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+
+    layer_tflops = {}
+    for lname, g in layers.items():
+        suf = "swa" if lname == "swa" else "global"
+        fwd_ms = kernels.get(f"attn_fwd_{suf}", {}).get("avg_ms")
+        bwd_ms = sum(kernels.get(f"{k}_{suf}", {}).get("avg_ms", 0.0) for k in ("bwd_dkdv", "bwd_dq"))
+        bwd_ms += (kernels.get("bwd_pre", {}).get("avg_ms", 0.0) + kernels.get("bwd_dsink", {}).get("avg_ms", 0.0)
+                   * (1 if lname == "swa" else 0))
+        layer_tflops[lname] = {
+            "fwd_TFLOP/s": round(g["pairs"] * FWD_FLOP_PER_PAIR / (fwd_ms * 1e-3) / 1e12, 1) if fwd_ms else None,
+            "fwd_frac": round(g["pairs"] * FWD_FLOP_PER_PAIR / (fwd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+            if fwd_ms else None,
+            "bwd_TFLOP/s": round(g["pairs"] * BWD_FLOP_PER_PAIR / (bwd_ms * 1e-3) / 1e12, 1) if bwd_ms else None,
+            "pairs": g["pairs"]}
+
+    line = {
+        "metric": "attention TFLOP/s fwd+bwd (SWA+sink, global) at 32K THD tokens; % bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "THD prefill fwd+bwd, 32768 tokens (16 x U[1024,2048] + pad), SWA layer "
+                               "(64q/8kv, window 128, sink, base 1e4) + global layer (64q/4kv, causal, base 1e7)",
+                   "global_batch": len(thd["swa"]["lengths"]), "seq_len": 32768, "parallelism": "none (1 GPU)"},
+        "frac_of_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "layers": layer_tflops, "kernels": kernels, "roofline": roofline,
+    }
+    if not args.no_decode:
+        line["decode"] = run_decode(ga, torch, mi)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(thd, dout_cpu, args.cpu_threads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

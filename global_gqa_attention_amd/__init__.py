@@ -47,6 +47,14 @@ def lib():
         L.mimo_attn_status_string.argtypes = [ctypes.c_int]
         L.mimo_attn_last_error.argtypes = []
         L.mimo_attn_release.argtypes = []
+        L.mimo_attn_trace_enable.argtypes = [ctypes.c_int]
+        L.mimo_attn_trace_count.argtypes = []
+        L.mimo_attn_trace_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+        L.mimo_attn_trace_clear.argtypes = []
+        L.mimo_attn_trace_enable.restype = ctypes.c_int
+        L.mimo_attn_trace_count.restype = i32
+        L.mimo_attn_trace_read.restype = ctypes.c_int
+        L.mimo_attn_trace_clear.restype = None
         for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode"):
             getattr(L, f).restype = ctypes.c_int
         L.mimo_attn_bwd_workspace_size.restype = sz
@@ -182,3 +190,21 @@ def decode(q, k_new, v_new, k_cache, v_cache, cu_cache, positions, sink, max_cac
 def release():
     """Free the library's cached RoPE tables."""
     lib().mimo_attn_release()
+
+
+def trace_enable(on: bool = True):
+    """Record a HIP event pair around every kernel the library launches (on the caller's stream)."""
+    _check(lib().mimo_attn_trace_enable(1 if on else 0), "mimo_attn_trace_enable")
+
+
+def trace_read(clear: bool = True):
+    """[(kernel name, milliseconds)] for every kernel launched while tracing was on (waits for them)."""
+    L = lib()
+    out = []
+    for i in range(L.mimo_attn_trace_count()):
+        name, ms = ctypes.c_char_p(), ctypes.c_float()
+        _check(L.mimo_attn_trace_read(i, ctypes.byref(name), ctypes.byref(ms)), "mimo_attn_trace_read")
+        out.append((name.value.decode(), float(ms.value)))
+    if clear:
+        L.mimo_attn_trace_clear()
+    return out

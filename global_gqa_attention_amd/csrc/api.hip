@@ -82,6 +82,29 @@ mimo_status_t rope_table(double base, int need, hipStream_t stream, const float2
     return MIMO_OK;
 }
 
+// ---- tracing: (name, start event, end event) per launched kernel
+struct TraceRec {
+    const char *name;
+    hipEvent_t start, stop;
+};
+bool g_trace_on = false;
+std::vector<TraceRec> g_trace;
+std::vector<hipEvent_t> g_event_pool;
+const char *g_trace_pending = nullptr;
+hipEvent_t g_trace_start = nullptr;
+
+hipEvent_t pool_event()
+{
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
 constexpr int kDQK = 192, kDV = 128;
 
 mimo_status_t check_layer(const void *q, const void *k, const void *v, const int32_t *cu, int32_t batch,
@@ -106,7 +129,57 @@ mimo_status_t check_layer(const void *q, const void *k, const void *v, const int
 
 }  // namespace
 
+namespace mimo {
+void trace_begin(const char *name, hipStream_t stream)
+{
+    if (!g_trace_on) return;
+    g_trace_start = pool_event();
+    g_trace_pending = name;
+    if (g_trace_start) (void)hipEventRecord(g_trace_start, stream);
+}
+
+void trace_end(hipStream_t stream)
+{
+    if (!g_trace_on || !g_trace_start) return;
+    hipEvent_t stop = pool_event();
+    if (!stop) return;
+    (void)hipEventRecord(stop, stream);
+    g_trace.push_back({g_trace_pending, g_trace_start, stop});
+    g_trace_start = nullptr;
+}
+}  // namespace mimo
+
 extern "C" {
+
+mimo_status_t mimo_attn_trace_enable(int enable)
+{
+    g_trace_on = enable != 0;
+    return ok();
+}
+
+int32_t mimo_attn_trace_count(void) { return (int32_t)g_trace.size(); }
+
+mimo_status_t mimo_attn_trace_read(int32_t i, const char **name, float *ms)
+{
+    if (i < 0 || i >= (int32_t)g_trace.size() || !name || !ms)
+        return fail(MIMO_ERR_INVALID_ARG, "trace record %d out of range", i);
+    TraceRec &r = g_trace[i];
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "reading a trace event");
+    *name = r.name;
+    return ok();
+}
+
+void mimo_attn_trace_clear(void)
+{
+    for (auto &r : g_trace) {
+        (void)hipEventSynchronize(r.stop);
+        g_event_pool.push_back(r.start);
+        g_event_pool.push_back(r.stop);
+    }
+    g_trace.clear();
+}
 
 const char *mimo_attn_status_string(mimo_status_t s)
 {
@@ -205,7 +278,7 @@ mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const f
     hipStream_t st = (hipStream_t)stream;
     if (total_tokens == 0) {
         if (dsink) {
-            hipError_t e = hipMemsetAsync(dsink, 0, sizeof(float) * n_q_heads, st);
+            hipError_t e = mimo::launch_zero_f32(dsink, n_q_heads, st);
             if (e != hipSuccess) return hip_fail(e, "clearing dsink");
         }
         return ok();

@@ -520,14 +520,23 @@ hipError_t launch_dq(const BwdArgs &A, hipStream_t stream)
     const long tiles = (long)(a.T + TT - 1) / TT + a.batch;
     const long grid = tiles * (G / GP) * a.hkv;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    trace_begin(a.window >= 0 ? "bwd_dq_swa" : "bwd_dq_global", stream);
     if (a.window >= 0) bwd_dq_kernel<GP, true><<<(unsigned)grid, 256, 0, stream>>>(A);
     else bwd_dq_kernel<GP, false><<<(unsigned)grid, 256, 0, stream>>>(A);
+    trace_end(stream);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool bwd_group_supported(int group) { return group >= 1; }
+
+hipError_t launch_zero_f32(float *p, int n, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    zero_kernel<<<(n + 255) / 256, 256, 0, stream>>>(p, n);
+    return hipGetLastError();
+}
 
 size_t bwd_workspace_bytes(int T, int hq, int hkv, int window)
 {
@@ -543,20 +552,26 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     const long rows = (long)a.T * a.hq;
     const long pre_blocks = (rows + 63) / 64;
     if (pre_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    trace_begin("bwd_pre", stream);
     bwd_pre_kernel<<<(unsigned)pre_blocks, 256, 0, stream>>>(A);
+    trace_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (A.dsink) {
+        trace_begin("bwd_dsink", stream);
         if (a.T > 0) bwd_dsink_kernel<<<a.hq, 256, 0, stream>>>(A);
         else zero_kernel<<<(a.hq + 255) / 256, 256, 0, stream>>>(A.dsink, a.hq);
+        trace_end(stream);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const long kv_tiles = (long)(a.T + NKB - 1) / NKB + a.batch;
     const long kv_grid = kv_tiles * a.hkv;
     if (kv_grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    trace_begin(a.window >= 0 ? "bwd_dkdv_swa" : "bwd_dkdv_global", stream);
     if (a.window >= 0) bwd_dkdv_kernel<true><<<(unsigned)kv_grid, 256, 0, stream>>>(A);
     else bwd_dkdv_kernel<false><<<(unsigned)kv_grid, 256, 0, stream>>>(A);
+    trace_end(stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int G = a.hq / a.hkv;

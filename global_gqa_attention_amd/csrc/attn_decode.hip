@@ -36,9 +36,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     __shared__ __attribute__((aligned(16))) u16 sVT[DVV * VTS];
     const int lane = threadIdx.x, hh = lane >> 5, c = lane & 31;
     const int G = A.hq / A.hkv;
+    const int ngrp = (G + 31) / 32;          // the group's query heads in blocks of 32 MFMA columns
     int w = blockIdx.x;
     const int split = w % A.splits;
     w /= A.splits;
+    const int hgrp = w % ngrp;
+    w /= ngrp;
     const int kvh = w % A.hkv;
     const int b = w / A.hkv;
     if (b >= A.batch) return;
@@ -49,12 +52,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     const int n = c1 - c0;
     const int ks = split * A.split_len;
     const int ke = min(n, ks + A.split_len);
-    const int hcol = c < G ? c : G - 1;     // MFMA columns beyond the group repeat its last head
-    const int h = kvh * G + hcol;
+    const int gi = hgrp * 32 + c;            // this lane's head inside the group
+    const bool hvalid = gi < G;
+    const int h = kvh * G + (hvalid ? gi : G - 1);   // spare MFMA columns repeat the group's last head
     const size_t part = ((size_t)b * A.hq + h) * A.splits + split;
 
     if (ks >= ke) {                          // nothing cached in this split: an empty partial
-        if (c < G) {
+        if (hvalid) {
             if (hh == 0) {
                 A.part_ml[part * 2 + 0] = -INFINITY;
                 A.part_ml[part * 2 + 1] = 0.f;
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     }
 
     const float l_tot = pair_sum(l_run);
-    if (c < G) {
+    if (hvalid) {
         if (hh == 0) {
             A.part_ml[part * 2 + 0] = m_run;
             A.part_ml[part * 2 + 1] = l_tot;
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs A)
 
 }  // namespace
 
-bool decode_group_supported(int group) { return group >= 1 && group <= 32; }
+bool decode_group_supported(int group) { return group >= 1; }
 
 void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window, int *splits, int *split_len)
 {
@@ -262,12 +266,17 @@ size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window)
 
 hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)
 {
-    const long waves = (long)A.batch * A.hkv * A.splits;
+    const int G = A.hq / A.hkv;
+    const long waves = (long)A.batch * A.hkv * ((G + 31) / 32) * A.splits;
     if (waves > 0x7fffffffL || (long)A.batch * A.hq > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    trace_begin(A.window >= 0 ? "decode_split_swa" : "decode_split_global", stream);
     decode_split_kernel<<<(unsigned)waves, 64, 0, stream>>>(A);
+    trace_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    trace_begin("decode_combine", stream);
     decode_combine_kernel<<<(unsigned)(A.batch * A.hq), 64, 0, stream>>>(A);
+    trace_end(stream);
     return hipGetLastError();
 }
 

@@ -253,10 +253,12 @@ hipError_t launch_gp(const FwdArgs &A, hipStream_t stream)
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     const bool sink = a.sink != nullptr, win = a.window >= 0;
+    trace_begin(win ? "attn_fwd_swa" : "attn_fwd_global", stream);
     if (sink && win) attn_fwd_kernel<GP, true, true><<<(unsigned)grid, 256, 0, stream>>>(A);
     else if (sink) attn_fwd_kernel<GP, true, false><<<(unsigned)grid, 256, 0, stream>>>(A);
     else if (win) attn_fwd_kernel<GP, false, true><<<(unsigned)grid, 256, 0, stream>>>(A);
     else attn_fwd_kernel<GP, false, false><<<(unsigned)grid, 256, 0, stream>>>(A);
+    trace_end(stream);
     return hipGetLastError();
 }
 

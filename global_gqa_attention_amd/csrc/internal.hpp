@@ -44,11 +44,16 @@ struct DecodeArgs {
     float scale_log2;
 };
 
+// Tracing hooks (no-ops unless tracing is enabled): bracket one kernel launch on `stream`.
+void trace_begin(const char *name, hipStream_t stream);
+void trace_end(hipStream_t stream);
+
 // Returns hipSuccess or the launch error.  Each launcher picks its kernel variant from the arguments.
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_rope_table(float2 *table, int npos, double base, hipStream_t stream);
+hipError_t launch_zero_f32(float *p, int n, hipStream_t stream);   // a fill kernel (no memset nodes)
 
 // Head-group sizes (n_q_heads / n_kv_heads) with compiled kernels.
 bool fwd_group_supported(int group);

@@ -118,6 +118,16 @@ mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_n
                                double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Per-kernel tracing.  While enabled, every entry point records a HIP event on the caller's stream before
+ * and after each kernel it launches (the events only mark the stream; nothing is synchronised).  The
+ * records accumulate until mimo_attn_trace_clear(); reading one waits for its end event.  Not thread-safe
+ * with concurrent calls on other threads while enabled. */
+mimo_status_t mimo_attn_trace_enable(int enable);
+int32_t mimo_attn_trace_count(void);
+/* Name of kernel record i (static string) and its duration in milliseconds. */
+mimo_status_t mimo_attn_trace_read(int32_t i, const char **name, float *ms);
+void mimo_attn_trace_clear(void);
+
 /* Name of a status code. */
 const char *mimo_attn_status_string(mimo_status_t s);
 

@@ -1,0 +1,131 @@
+"""GPU backward parity against the fp64 oracle.
+
+The backward is given the forward outputs; both sides receive the same O (the oracle's forward rounded to
+bf16) and LSE (rounded to fp32), so D = rowsum(dO * O) uses the same O on both sides.  dq/dk/dv: max-abs
+2e-2 (widened by a bf16 half-ulp of |ref| where |ref| >= 8), mean-abs 2e-3; dsink: 1e-2 relative per head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mimo_inputs as mi
+import oracle
+from parity import compare, compare_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu():
+    import global_gqa_attention_amd as ga
+
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the -m gpu tests")
+    return ga
+
+
+def _given_outputs(d, rows=None):
+    """Oracle forward (all rows) rounded to the forward's output types: O bf16 [T,hq,128], LSE fp32 [hq,T]."""
+    o, l = oracle.prefill(d["q"], d["k"], d["v"], d["sink"], d["cu_seqlens"], d["window"], d["rope_base"])
+    return torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(l).to(torch.float32)
+
+
+def _run_bwd(ga, d, O, L, dO):
+    dev = "cuda"
+    sink = None if d["sink"] is None else d["sink"].to(dev)
+    g = ga.bwd(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), sink, O.to(dev), L.to(dev), dO.to(dev),
+               d["cu_seqlens"].to(dev), max(d["lengths"] + [1]), d["window"], d["rope_base"])
+    torch.cuda.synchronize()
+    return [None if x is None else x.cpu() for x in g]
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,window,base,sink", [
+    ([512], 64, 8, 128, 1e4, True),
+    ([1, 5, 63, 64, 65, 129, 200, 0, 300], 64, 8, 128, 1e4, True),
+    ([1, 5, 63, 64, 65, 129, 200, 0, 300], 64, 4, -1, 1e7, False),
+    ([17, 130, 1], 64, 4, -1, 1e7, True),
+    ([70, 33, 257], 16, 8, 0, 1e4, True),
+    ([100, 29], 12, 4, 40, 1e4, True),
+    ([100, 29], 8, 1, -1, 1e4, False),
+])
+def test_bwd_small_full(lengths, hq, hkv, window, base, sink):
+    ga = _gpu()
+    d = mi.make_layer(lengths, hq, hkv, 9, sink)
+    d.update(window=window, rope_base=base)
+    print(f"case lengths={lengths} hq={hq} hkv={hkv} window={window} sink={sink}", flush=True)
+    O, L = _given_outputs(d)
+    dO = mi.dout_like(sum(lengths), 4, hq)
+    dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO)
+    rq, rk, rv, rs = oracle.prefill_bwd(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], window, base,
+                                        out_given=O)
+    compare("dq", dq, rq, bf16_halfulp=True)
+    compare("dk", dk, rk, bf16_halfulp=True)
+    compare("dv", dv, rv, bf16_halfulp=True)
+    if sink:
+        compare_rel("dsink", ds, rs)
+    else:
+        assert ds is None
+
+
+def test_bwd_deterministic():
+    ga = _gpu()
+    d = mi.make_layer([700, 333], 64, 8, 10, True)
+    d.update(window=128, rope_base=1e4)
+    O, L = _given_outputs(d)
+    dO = mi.dout_like(1033, 4)
+    a = _run_bwd(ga, d, O, L, dO)
+    b = _run_bwd(ga, d, O, L, dO)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def _sampled_bwd(ga, d, dO, nq, nk, heads, seed):
+    """Full-size backward: the oracle computes the forward rows it needs, and then sampled dq rows, dk/dv rows
+    near the ends of sequences (few queries see them under causal attention), and dsink for a few heads."""
+    rng = np.random.default_rng(seed)
+    T, hq, hkv = d["q"].shape[0], d["q"].shape[1], d["k"].shape[1]
+    starts = np.concatenate([[0], np.cumsum(d["lengths"])])
+    # the given forward outputs on every row (the GPU needs them all): oracle rows in chunks
+    O = torch.empty(T, hq, 128, dtype=torch.bfloat16)
+    L = torch.empty(hq, T, dtype=torch.float32)
+    o, l = oracle.prefill_rows(d["q"], d["k"], d["v"], d["sink"], d["cu_seqlens"], d["window"], d["rope_base"])
+    O[:] = torch.from_numpy(o.reshape(T, hq, 128)).to(torch.bfloat16)
+    L[:] = torch.from_numpy(l.reshape(T, hq).T.copy()).to(torch.float32)
+    dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO)
+    qrows = rng.integers(0, T * hq, nq)
+    rq = oracle.bwd_dq_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"], d["rope_base"],
+                            qrows, out_given=O)
+    compare("dq (sampled)", dq.reshape(-1, 192)[qrows], rq, bf16_halfulp=True)
+    toks = []
+    for b in range(len(d["lengths"])):
+        if d["lengths"][b]:
+            end = starts[b + 1]
+            toks += [end - 1, end - 2, max(starts[b], end - 50)] + rng.integers(starts[b], end, 1).tolist()
+    toks = np.array(sorted(set(toks)))[:nk]
+    krows = toks * hkv + rng.integers(0, hkv, len(toks))
+    rk, rv = oracle.bwd_dkv_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"],
+                                 d["rope_base"], krows, out_given=O)
+    compare("dk (sampled)", dk.reshape(-1, 192)[krows], rk, bf16_halfulp=True)
+    compare("dv (sampled)", dv.reshape(-1, 128)[krows], rv, bf16_halfulp=True)
+    if d["sink"] is not None:
+        rs = oracle.bwd_dsink_heads(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"],
+                                    d["rope_base"], heads, out_given=O)
+        compare_rel("dsink (sampled heads)", ds[heads], rs)
+
+
+def test_bwd_thd_32k_swa_sampled():
+    """SWA layer of the 32768-token THD batch with dO ~ N(0,1) seed 4: sampled rows, 4 full dsink heads."""
+    ga = _gpu()
+    d = mi.thd_32k()["swa"]
+    dO = mi.dout_like(32768, 4)
+    print("case thd_32k swa bwd", flush=True)
+    _sampled_bwd(ga, d, dO, 400, 60, [0, 17, 40, 63], 3)
+
+
+def test_bwd_global_small_batch_sampled():
+    """Global layer on a 2 x 2048 batch (the oracle's full forward stays fast): sampled rows."""
+    ga = _gpu()
+    d = mi.make_layer([2048, 1999], 64, 4, 11, False)
+    d.update(window=-1, rope_base=1e7)
+    dO = mi.dout_like(4047, 4)
+    print("case global 2048+1999 bwd", flush=True)
+    _sampled_bwd(ga, d, dO, 300, 40, [], 4)
