@@ -39,7 +39,9 @@ def lib():
             raise MimoAttnError(f"{LIB_PATH} is missing: build it with `python -m global_gqa_attention_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
-        L.mimo_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P]
+        L.mimo_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, sz, P]
+        L.mimo_attn_fwd_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mimo_attn_fwd_workspace_size.restype = sz
         L.mimo_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
         L.mimo_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -109,9 +111,17 @@ def _layer_checks(q, k, v, sink, cu_seqlens):
     return T, hq, hkv, cu_seqlens.numel() - 1
 
 
-def fwd(q, k, v, sink, cu_seqlens, max_seqlen, window, rope_base, out=None, lse=None, return_lse=True):
+def fwd_workspace_size(total_tokens, n_q_heads, n_kv_heads, window) -> int:
+    return int(lib().mimo_attn_fwd_workspace_size(int(total_tokens), int(n_q_heads), int(n_kv_heads), int(window)))
+
+
+def fwd(q, k, v, sink, cu_seqlens, max_seqlen, window, rope_base, out=None, lse=None, return_lse=True,
+        workspace=None):
     """Forward of one layer.  Returns (out bf16 [T,hq,128], lse fp32 [hq,T] or None)."""
     T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
+    if workspace is None:
+        workspace = torch.empty((max(fwd_workspace_size(T, hq, hkv, window), 1),), dtype=torch.uint8,
+                                device=q.device)
     if out is None:
         out = torch.empty((T, hq, DV), dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, (T, hq, DV))
@@ -120,7 +130,8 @@ def fwd(q, k, v, sink, cu_seqlens, max_seqlen, window, rope_base, out=None, lse=
     if lse is not None:
         _need(lse, "lse", torch.float32, (hq, T))
     rc = lib().mimo_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(cu_seqlens), batch, T, int(max_seqlen),
-                             int(window), float(rope_base), hq, hkv, _ptr(out), _ptr(lse), _stream(q.device))
+                             int(window), float(rope_base), hq, hkv, _ptr(out), _ptr(lse), _ptr(workspace),
+                             workspace.numel(), _stream(q.device))
     _check(rc, "mimo_attn_fwd")
     return out, lse
 

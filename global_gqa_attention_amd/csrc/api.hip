@@ -218,7 +218,8 @@ void mimo_attn_release(void)
 mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
-                            int32_t n_kv_heads, void *out, float *lse, void *stream)
+                            int32_t n_kv_heads, void *out, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream)
 {
     mimo_status_t s = check_layer(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base,
                                   n_q_heads, n_kv_heads);
@@ -227,8 +228,12 @@ mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const f
     if (!mimo::fwd_group_supported(n_q_heads / n_kv_heads))
         return fail(MIMO_ERR_UNSUPPORTED, "no forward kernel for group size %d", n_q_heads / n_kv_heads);
     if (total_tokens == 0) return ok();
+    const size_t need = mimo::fwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
+    if (!workspace || workspace_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     hipStream_t st = (hipStream_t)stream;
     mimo::FwdArgs a{};
+    mimo::prep_carve(workspace, total_tokens, n_kv_heads, &a.P);
     s = rope_table(rope_base, max_seqlen, st, &a.L.rope, &a.L.rope_len);
     if (s != MIMO_OK) return s;
     a.L.q = (const uint16_t *)q;
@@ -247,6 +252,13 @@ mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const f
     hipError_t e = mimo::launch_fwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return ok();
+}
+
+size_t mimo_attn_fwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t window)
+{
+    if (total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
+    return mimo::fwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
 }
 
 size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,

@@ -8,46 +8,54 @@
 // "feat(models): add MiMo-V2.6-Flash-RL support" (asymmetric Q/K vs V channels, sink on SWA layers).
 //
 // Design (gfx950, wave64):
-//   * A workgroup of 4 waves owns 128 query rows: TT = 128 / GP consecutive tokens x GP query heads that
-//     share one KV head.  Packing heads keeps a sliding-window tile's key span short (16 tokens + 128 keys
-//     back) and lets all GP heads reuse each K/V tile staged in LDS.
-//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: the query is the MFMA column, so each lane owns one query
+//   * A workgroup of 4 waves owns 256 query rows: TT = 256 / GP consecutive tokens x GP query heads that
+//     share one KV head; each wave owns 64 rows as two 32-row MFMA column blocks, so every K/V operand
+//     read from LDS feeds two MFMAs (32 rows per wave would make LDS bandwidth, not MFMA, the limit).
+//     Packing heads keeps a sliding-window tile's key span short and lets all GP heads reuse each K/V
+//     tile staged in LDS; 32-key blocks that no row of a wave can see are skipped.
+//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: the query is the MFMA column, so each lane owns a query
 //     (lanes l and l ^ 32 split its keys); row max and row sum need one permlane32 swap, and the rescale of
 //     the output accumulator is per lane.  O^T = V^T . P^T reuses the score registers as the B operand.
 //   * K tiles are rotated while being staged into LDS (cos/sin from a table built in fp64); Q is rotated
 //     once in registers.  V is staged transposed, with its 4-key chunks permuted so that the keys a lane
-//     needs for P^T come out of LDS as one 16-byte read.
+//     needs for P^T come out of LDS as one 16-byte read.  LDS is double-buffered: one barrier per tile,
+//     and the next tile's HBM loads are in flight while the current tile is computed.
 //   * Online softmax in base 2 (scale folded into one multiply); the sink starts the running max and sum.
-//     Only tiles that cross the causal or window boundary evaluate the mask.  Key tiles outside the
-//     window are never visited.
+//     The reference max moves only when a block's max exceeds it by 2^8, so most blocks skip the rescale
+//     of the accumulator (the result is exact either way: numerator and denominator share the reference).
+//     Only blocks that cross the causal or window boundary evaluate the mask.
 #include "device_common.hpp"
 #include "internal.hpp"
 
 namespace mimo {
 namespace {
 
-constexpr int BM = 128;        // query rows per workgroup
+constexpr int BM = 128;        // query rows per workgroup (32 per wave: one MFMA column block)
 constexpr int BN = 64;         // keys per tile
-constexpr int KS = DQK + 8;    // LDS row stride of the K tile (elements)
-constexpr int VS = BN + 8;     // LDS row stride of the V^T tile (elements)
+constexpr int KCH = DQK / 8;   // 16-byte chunks per K row (24)
+constexpr int VCH = BN / 8;    // 16-byte chunks per V^T row (8)
+constexpr int KLOADS = BN * KCH / 256;    // global_load_lds per thread per K tile (6)
+constexpr int VLOADS = DVV * VCH / 256;   // ... per V^T tile (4)
+constexpr float RESCALE_TH = 8.f;         // keep a stale running max until the true one exceeds it by 2^8
 
-// LDS column chunk of a 4-key chunk inside a 16-key group: swaps the two chunk bits so that lane half hh
-// reads keys {4hh..4hh+3, 8+4hh..8+4hh+3} as 8 consecutive elements.
-__device__ __forceinline__ int vcol(int key4)
-{
-    int c4 = (key4 >> 2) & 3;
-    return (key4 & ~15) | ((((c4 & 1) << 1) | (c4 >> 1)) << 2);
-}
+// K tile in LDS: row r (key), 24 chunks of 16 B; logical chunk q sits at position q ^ (r & 7) inside its
+// group of 8, so the 8 lanes of an MFMA operand read (8 consecutive rows, same logical chunk) hit 8
+// different bank groups.  V^T tile: row d (dim), 8 chunks, position q ^ (d & 7).
+__device__ __forceinline__ int kpos(int r, int q) { return (q & ~7) | ((q & 7) ^ (r & 7)); }
+__device__ __forceinline__ int vpos(int d, int q) { return q ^ (d & 7); }
 
 template <int GP, bool SINK, bool WIN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdArgs A)
 {
     const LayerArgs &a = A.L;
-    __shared__ __attribute__((aligned(16))) u16 sK[BN * KS];
-    __shared__ __attribute__((aligned(16))) u16 sV[DVV * VS];
+    __shared__ __attribute__((aligned(16))) uint4 sK0[BN * KCH];
+    __shared__ __attribute__((aligned(16))) uint4 sV0[DVV * VCH];
+    __shared__ __attribute__((aligned(16))) uint4 sK1[BN * KCH];
+    __shared__ __attribute__((aligned(16))) uint4 sV1[DVV * VCH];
 
     constexpr int TT = BM / GP;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) by construction
     const int hh = lane >> 5, c = lane & 31;
     const int G = a.hq / a.hkv;
     const int n_hg = G / GP;
@@ -75,15 +83,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdArgs A)
     const int t_last = min(t0 + TT - 1, seq_end - 1);
     const int h0 = kvh * G + hgi * GP;
 
-    // ---- this lane's query row
+    // ---- key range: tiles start on a 16-token boundary (the V^T chunk order is per 16 tokens); keys of a
+    // previous sequence that this brings in are masked
+    const int klo = WIN ? max(seq_start, t0 - a.window) : seq_start;
+    const int kstart = klo & ~15;
+    const int khi = t_last;
+    const int nkt = (khi - kstart + BN) / BN;
+
+    // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = 256 j + tid of each array)
+    const u16 *kr_base = A.P.kr + (size_t)kvh * DQK;
+    const size_t kr_row = (size_t)a.hkv * DQK;
+    const u16 *vt_base = A.P.vt + (size_t)kvh * DVV * A.P.T_pad;
+    auto issue_tile = [&](int k0, uint4 *sk, uint4 *sv) {
+#pragma unroll
+        for (int j = 0; j < KLOADS; ++j) {
+            const int slot = 256 * j + tid;
+            const int r = slot / KCH, p = slot % KCH;
+            const u16 *src = kr_base + (size_t)(k0 + r) * kr_row + 8 * kpos(r, p);   // kpos is an involution
+            lds_dma16(src, sk + 256 * j + 64 * wave);
+        }
+#pragma unroll
+        for (int j = 0; j < VLOADS; ++j) {
+            const int slot = 256 * j + tid;
+            const int d = slot / VCH, p = slot % VCH;
+            const u16 *src = vt_base + (size_t)d * A.P.T_pad + k0 + 8 * vpos(d, p);
+            lds_dma16(src, sv + 256 * j + 64 * wave);
+        }
+    };
+    issue_tile(kstart, sK0, sV0);
+
+    // ---- this lane's query row, rotated in registers
     const int r = wave * 32 + c;
     const int qt = t0 + r / GP;
     const int qh = h0 + r % GP;
     const bool qvalid = qt < seq_end;
-    const int qtl = qvalid ? qt : t_last;
-
     bf16x8 qf[12];
     {
+        const int qtl = qvalid ? qt : t_last;
         const u16 *qp = a.q + ((size_t)qtl * a.hq + qh) * DQK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
@@ -98,10 +134,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdArgs A)
         rope_pair(qf[1], qf[3], c1);
     }
 
-    // ---- key range of the tile
-    const int klo = WIN ? max(seq_start, t0 - a.window) : seq_start;
-    const int khi = t_last;
-    const int nkt = (khi - klo + BN) / BN;
+    // this wave's rows span tokens [wt0, wt1]; 32-key blocks outside [wklo, wkhi] are skipped
+    const int wt0 = t0 + (wave * 32) / GP;
+    const int wt1 = min(t0 + (wave * 32 + 31) / GP, seq_end - 1);
+    const int wklo = WIN ? max(seq_start, wt0 - a.window) : seq_start;
+    const int wkhi = wt1;
 
     float m_run = -INFINITY, l_run = 0.f;
     if (SINK) {
@@ -115,112 +152,84 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdArgs A)
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-    // ---- staging registers (next tile prefetched while the current one is computed)
-    uint4 kreg[6], vreg[4];
-    float2 kcs[8];
-    const int kk = tid >> 2, cg = tid & 3;       // K staging: key kk, chunks cg, cg+4 (rotated), 8+cg+4i
-    const int vdc = tid & 15, vkc = tid >> 4;    // V staging: dims 8vdc..+7, keys 4vkc..+3
-
-    auto load_tile = [&](int k0) {
-        const int key = min(k0 + kk, khi);
-        const u16 *kp = a.k + ((size_t)key * a.hkv + kvh) * DQK;
-        kreg[0] = ldu4(kp + 8 * cg);
-        kreg[1] = ldu4(kp + 8 * (cg + 4));
+    // ---- one tile: S^T = K Q^T, online softmax, O^T += V^T P^T (two 32-key blocks)
+    auto compute_tile = [&](int k0, const uint4 *skb, const uint4 *svb) {
+        const u16 *kt = (const u16 *)skb;
+        const u16 *vtt = (const u16 *)svb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kreg[2 + i] = ldu4(kp + 8 * (8 + cg + 4 * i));
-        const float2 *cs = a.rope + (size_t)min(key - seq_start, a.rope_len - 1) * NHALF + 8 * cg;
+        for (int kb = 0; kb < 2; ++kb) {
+            const int kbase = k0 + 32 * kb;
+            if (kbase > wkhi || kbase + 31 < wklo) continue;     // no row of this wave sees these 32 keys
+            const int kr_ = 32 * kb + c;
+            f32x16 sacc = f32x16{};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) kcs[t] = cs[t];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int vkey = min(k0 + 4 * vkc + i, khi);
-            vreg[i] = ldu4(a.v + ((size_t)vkey * a.hkv + kvh) * DVV + 8 * vdc);
-        }
-    };
-    auto store_tile = [&]() {
-        bf16x8 x0 = __builtin_bit_cast(bf16x8, kreg[0]);
-        bf16x8 x1 = __builtin_bit_cast(bf16x8, kreg[1]);
-        rope_pair(x0, x1, kcs);
-        u16 *kd = sK + kk * KS;
-        st16(kd + 8 * cg, x0);
-        st16(kd + 8 * (cg + 4), x1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st16u(kd + 8 * (8 + cg + 4 * i), kreg[2 + i]);
-        const int col = vcol(4 * vkc);
-        const u16 *v0 = (const u16 *)&vreg[0], *v1 = (const u16 *)&vreg[1];
-        const u16 *v2 = (const u16 *)&vreg[2], *v3 = (const u16 *)&vreg[3];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint2 w;
-            w.x = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
-            w.y = (uint32_t)v2[e] | ((uint32_t)v3[e] << 16);
-            *(uint2 *)(sV + (8 * vdc + e) * VS + col) = w;
-        }
-    };
-
-    load_tile(klo);
-    for (int it = 0; it < nkt; ++it) {
-        const int k0 = klo + it * BN;
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (it + 1 < nkt) load_tile(k0 + BN);
-
-        // S^T = K Q^T: two 32-key blocks x 12 k-steps of 16 dims
-        f32x16 sacc[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            sacc[b] = f32x16{};
-            const u16 *kr = sK + (32 * b + c) * KS + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 12; ++s) sacc[b] = mfma32(ld16(kr + 16 * s), qf[s], sacc[b]);
-        }
-
-        // mask (only on tiles that cross a boundary), online softmax in base 2
-        const bool need_mask = (k0 + BN - 1 > t0) || (WIN && k0 < t_last - a.window);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
+            for (int s = 0; s < 12; ++s)
+                sacc = mfma32(ld16(kt + (kr_ * KCH + kpos(kr_, 2 * s + hh)) * 8), qf[s], sacc);
+            const bool need_mask = (kbase + 31 > wt0) || (kbase < seq_start) || (WIN && kbase < wt1 - a.window);
+            float mx = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                float s = sacc[b][j] * a.scale_log2;
+                float sv = sacc[j] * a.scale_log2;
                 if (need_mask) {
-                    const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    const bool ok = key <= qt && (!WIN || key >= qt - a.window);
-                    s = ok ? s : -INFINITY;
+                    const int key = kbase + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    const bool ok = key <= qt && key >= seq_start && (!WIN || key >= qt - a.window);
+                    sv = ok ? sv : -INFINITY;
                 }
-                sacc[b][j] = s;
-                mx = fmaxf(mx, s);
+                sacc[j] = sv;
+                mx = fmaxf(mx, sv);
             }
-        }
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.f;
-        bf16x8 pf[4];
+            mx = pair_max(mx);
+            // lazy rescale: move the reference max only when the block max exceeds it by 2^8; the branch is
+            // wave-uniform so the accumulators are touched only when some row needs it
+            const bool grow = mx > m_run + RESCALE_TH;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+                l_run *= alpha;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+                for (int i = 0; i < 4; ++i) o[i] *= alpha;
+                m_run = grow ? mx : m_run;
+            }
+            const float mref = m_run == -INFINITY ? 0.f : m_run;
+            float psum = 0.f;
+            bf16x8 pf[2];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float p = fast_exp2(sacc[b][j] - m_use);
+                const float p = fast_exp2(sacc[j] - mref);
                 psum += p;
-                pf[2 * b + (j >> 3)][j & 7] = f2bf(p);
+                pf[j >> 3][j & 7] = f2bf(p);
+            }
+            l_run += psum;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = 32 * i + c;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    o[i] = mfma32(ld16(vtt + (d * VCH + vpos(d, 4 * kb + 2 * s + hh)) * 8), pf[s], o[i]);
             }
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    };
 
-        // O^T += V^T P^T: four 32-dim blocks x four 16-key steps
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u16 *vr = sV + (32 * i + c) * VS + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) o[i] = mfma32(ld16(vr + 16 * s), pf[s], o[i]);
-        }
+    // ---- double-buffered loop, unrolled by two so each half names its own buffers.  Every half issues
+    // exactly one tile (the last valid tile again once the range is exhausted), so the number of loads in
+    // flight is the same on every path: the wait for a buffer is always "all but the 10 newest loads".  The
+    // LDS tiles are written only by these direct loads, so a plain s_barrier suffices: each wave waits
+    // (vmcnt) for its own loads of the tile it reads next, and reaches the following barrier only after
+    // its MFMAs consumed every LDS read of the buffer that is refilled next.
+    const int klast = kstart + (nkt - 1) * BN;
+    for (int it = 0; it < nkt; it += 2) {
+        const int k0 = kstart + it * BN;
+        issue_tile(min(k0 + BN, klast), sK1, sV1);
+        wait_vmcnt<KLOADS + VLOADS>();
+        __builtin_amdgcn_s_barrier();       // tile it is in buffer 0 for every wave
+        compute_tile(k0, sK0, sV0);
+        __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 0
+        issue_tile(min(k0 + 2 * BN, klast), sK0, sV0);
+        wait_vmcnt<KLOADS + VLOADS>();
+        __builtin_amdgcn_s_barrier();       // tile it+1 is in buffer 1 for every wave
+        if (it + 1 < nkt) compute_tile(k0 + BN, sK1, sV1);
+        __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 1
     }
+    wait_vmcnt<0>();                        // no load may still target this workgroup's LDS at exit
 
     // ---- epilogue: out = 0.707 * O / l, LSE = ln(l) + max
     const float l_tot = pair_sum(l_run);
@@ -280,13 +289,22 @@ bool fwd_group_supported(int group) { return group >= 1; }
 hipError_t launch_fwd(const FwdArgs &A, hipStream_t stream)
 {
     const LayerArgs &a = A.L;
+    hipError_t e = launch_kv_prep(a, A.P, stream);
+    if (e != hipSuccess) return e;
     const int G = a.hq / a.hkv;
-    // pack up to 8 heads of a group: 16 tokens x 8 heads per workgroup for sliding-window layers (short key
+    // pack up to 8 heads of a group: 32 tokens x 8 heads per workgroup for sliding-window layers (short key
     // span), and the same for causal layers (each K/V tile serves 8 heads; little waste on the diagonal).
     if (G % 8 == 0) return launch_gp<8>(A, stream);
     if (G % 4 == 0) return launch_gp<4>(A, stream);
     if (G % 2 == 0) return launch_gp<2>(A, stream);
     return launch_gp<1>(A, stream);
+}
+
+size_t fwd_workspace_bytes(int T, int hq, int hkv, int window)
+{
+    (void)hq;
+    (void)window;
+    return prep_bytes(T, hkv);
 }
 
 hipError_t launch_rope_table(float2 *table, int npos, double base, hipStream_t stream)

@@ -1,0 +1,125 @@
+// attn_prep.hip -- per-call K/V preparation for the attention kernels (gfx950).
+//
+// Writes two workspace tensors that let the hot loops move K and V from HBM straight into LDS with
+// global_load_lds (no register staging, no per-tile arithmetic):
+//   kr [T_pad, hkv, 192] bf16: k with RoPE applied to dims 0..63 at each token's position inside its own
+//                              sequence (rotate-half pairs (d, d+32), angle p * base^(-d/32)), i.e. the k'
+//                              of miles docs "MiMo-V2.6-Flash" section 1 (partial RoPE on 64 of 192 dims);
+//   vt [hkv, 128, T_pad] bf16: v transposed per KV head, with the 4-token chunks of every 16-token group
+//                              stored in the order (0, 2, 1, 3): an MFMA operand read of 8 consecutive
+//                              elements then returns the keys in the order the score registers hold them.
+// Tokens T .. T_pad-1 are written as zeros (tiles may read them; they are masked, and zero values keep the
+// masked products finite).
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace mimo {
+namespace {
+
+constexpr int PT = 64;   // tokens per workgroup
+
+__device__ __forceinline__ int seq_start_of(const int32_t *cu, int batch, int t)
+{
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return cu[lo];
+}
+
+__device__ __forceinline__ int vperm16(int t)   // column of token t inside its 16-token group
+{
+    const int c4 = (t >> 2) & 3;
+    return (t & ~15) | ((((c4 & 1) << 1) | (c4 >> 1)) << 2) | (t & 3);
+}
+
+__global__ __launch_bounds__(256) void kv_prep_kernel(const LayerArgs a, KVPrep p)
+{
+    __shared__ __attribute__((aligned(16))) u16 sV[PT * (DVV + 8)];
+    const int tid = threadIdx.x;
+    const int kvh = blockIdx.y;
+    const int t0 = blockIdx.x * PT;
+
+    // ---- K: token t0 + tid/4, chunk group tid%4 (chunks cg, cg+4 rotated; 8+cg+4i copied)
+    {
+        const int t = t0 + (tid >> 2), cg = tid & 3;
+        u16 *dst = p.kr + ((size_t)t * a.hkv + kvh) * DQK;
+        if (t < a.T) {
+            const u16 *src = a.k + ((size_t)t * a.hkv + kvh) * DQK;
+            bf16x8 x0 = ld16(src + 8 * cg), x1 = ld16(src + 8 * (cg + 4));
+            const int pos = t - seq_start_of(a.cu, a.batch, t);
+            const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;
+            float2 c8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c8[i] = cs[i];
+            rope_pair(x0, x1, c8);
+            st16(dst + 8 * cg, x0);
+            st16(dst + 8 * (cg + 4), x1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), ldu4(src + 8 * (8 + cg + 4 * i)));
+        } else if (t < p.T_pad) {
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            st16u(dst + 8 * cg, z);
+            st16u(dst + 8 * (cg + 4), z);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), z);
+        }
+    }
+    // ---- V^T: stage 64 tokens x 128 dims in LDS, then write rows of 8 tokens (permuted order)
+    {
+        const int r = tid >> 2, cg = tid & 3;
+        const int t = t0 + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = cg + 4 * i;
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (t < a.T) x = ldu4(a.v + ((size_t)t * a.hkv + kvh) * DVV + 8 * ch);
+            *(uint4 *)(sV + r * (DVV + 8) + 8 * ch) = x;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int item = tid + 256 * i;          // 128 dims x 8 column chunks
+        const int d = item >> 3, cc = item & 7;  // cc: columns 8cc..8cc+7 of the tile
+        if (t0 + 8 * cc >= p.T_pad) continue;
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // column 8cc+e holds the token whose permuted column is 8cc+e (the permutation is an involution)
+            const int tok = vperm16(8 * cc + e);
+            w[e] = __builtin_bit_cast(__bf16, sV[tok * (DVV + 8) + d]);
+        }
+        st16(p.vt + ((size_t)kvh * DVV + d) * p.T_pad + t0 + 8 * cc, w);
+    }
+}
+
+}  // namespace
+
+size_t prep_bytes(int T, int hkv)
+{
+    const size_t tp = (size_t)prep_tpad(T);
+    const size_t kr = (tp * hkv * DQK * 2 + 255) & ~(size_t)255;
+    const size_t vt = (tp * hkv * DVV * 2 + 255) & ~(size_t)255;
+    return kr + vt;
+}
+
+void prep_carve(void *ws, int T, int hkv, KVPrep *p)
+{
+    p->T_pad = prep_tpad(T);
+    p->kr = (uint16_t *)ws;
+    const size_t kr = ((size_t)p->T_pad * hkv * DQK * 2 + 255) & ~(size_t)255;
+    p->vt = (uint16_t *)((char *)ws + kr);
+}
+
+hipError_t launch_kv_prep(const LayerArgs &a, const KVPrep &p, hipStream_t stream)
+{
+    dim3 grid((p.T_pad + PT - 1) / PT, a.hkv);
+    trace_begin("kv_prep", stream);
+    kv_prep_kernel<<<grid, 256, 0, stream>>>(a, p);
+    trace_end(stream);
+    return hipGetLastError();
+}
+
+}  // namespace mimo

@@ -51,6 +51,28 @@ __device__ __forceinline__ float pair_sum(float v)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct HBM -> LDS copy of 16 bytes per lane: lane i's bytes land at lds_wave_base + 16 i (lds_wave_base
+// must be wave-uniform).  Issued through inline asm so that the compiler adds no automatic wait for it
+// before later LDS reads; the caller orders it with wait_vmcnt<N>() and barriers.  It has no register
+// output, so nothing can be overwritten by the load in flight.
+__device__ __forceinline__ void lds_dma16(const void *gsrc, void *lds_wave_base)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0), "v"(gsrc)
+                 : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory loads are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Rotate-half RoPE of one 8-wide chunk pair: x0 holds dims d..d+7 (d < 32), x1 dims d+32..d+39, cs the
 // (cos, sin) of the 8 matching frequencies.  Rounded back to bf16 (the MFMA operand precision).
 __device__ __forceinline__ void rope_pair(bf16x8 &x0, bf16x8 &x1, const float2 *cs)

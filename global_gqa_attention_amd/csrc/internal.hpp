@@ -15,8 +15,19 @@ struct LayerArgs {
     float scale_log2;              // log2(e) / sqrt(192)
 };
 
+// Prepared K/V in the workspace (written by kv_prep, read by the hot loops through global_load_lds).
+struct KVPrep {
+    uint16_t *kr;                  // bf16 [T_pad, hkv, 192]: K with RoPE applied
+    uint16_t *vt;                  // bf16 [hkv, 128, T_pad]: V transposed, 4-token chunks permuted
+    int T_pad;                     // tokens rounded up to 16, plus 64 zero-filled
+};
+inline int prep_tpad(int T) { return (T + 15) / 16 * 16 + 64; }
+size_t prep_bytes(int T, int hkv);
+void prep_carve(void *ws, int T, int hkv, KVPrep *p);
+
 struct FwdArgs {
     LayerArgs L;
+    KVPrep P;
     uint16_t *out;                 // bf16 [T,hq,128]
     float *lse;                    // fp32 [hq,T] or nullptr
 };
@@ -49,6 +60,7 @@ void trace_begin(const char *name, hipStream_t stream);
 void trace_end(hipStream_t stream);
 
 // Returns hipSuccess or the launch error.  Each launcher picks its kernel variant from the arguments.
+hipError_t launch_kv_prep(const LayerArgs &a, const KVPrep &p, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -60,6 +72,7 @@ bool fwd_group_supported(int group);
 bool bwd_group_supported(int group);
 bool decode_group_supported(int group);
 
+size_t fwd_workspace_bytes(int T, int hq, int hkv, int window);
 size_t bwd_workspace_bytes(int T, int hq, int hkv, int window);
 size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window);
 void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window, int *splits, int *split_len);

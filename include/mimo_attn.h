@@ -60,12 +60,20 @@ typedef enum {
  *   window   -1 (causal) or >= 0 (the query plus `window` previous keys)
  *   out   bf16 [total_tokens, n_q_heads, 128]
  *   lse   fp32 [n_q_heads, total_tokens] natural-log softmax denominator incl. the sink, or NULL
+ *   workspace: device memory of at least mimo_attn_fwd_workspace_size() bytes, owned by the caller; needs
+ *   no initialisation and must not be shared with a concurrent call.
  * Source: miles docs "MiMo-V2.6-Flash" sections 1, 5.1, 5.4; miles PR "feat(models): add MiMo-V2.6-Flash-RL
  * support" (core attention with asymmetric channels, sink, V scale). */
 mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
-                            int32_t n_kv_heads, void *out, float *lse, void *stream);
+                            int32_t n_kv_heads, void *out, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace mimo_attn_fwd needs: RoPE-rotated K and per-head transposed V (about
+ * 640 * n_kv_heads bytes per token), which the kernels then stream from HBM straight into LDS. */
+size_t mimo_attn_fwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t window);
 
 /* Bytes of device workspace mimo_attn_bwd needs for these sizes (0 is never returned for valid sizes). */
 size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,

@@ -27,7 +27,8 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_bwd_workspace_size",
+    for n in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_fwd_workspace_size",
+              "mimo_attn_bwd_workspace_size",
               "mimo_attn_decode_workspace_size", "mimo_attn_status_string", "mimo_attn_last_error",
               "mimo_attn_release"):
         assert n in names
@@ -49,16 +50,16 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails ho
 
 def fwd(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, sink=None, cu=FAKE, batch=1, T=16, max_seqlen=16, window=128,
-             base=1e4, hq=64, hkv=8, out=FAKE, lse=None)
+             base=1e4, hq=64, hkv=8, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return L.mimo_attn_fwd(a["q"], a["k"], a["v"], a["sink"], a["cu"], a["batch"], a["T"], a["max_seqlen"],
-                           a["window"], a["base"], a["hq"], a["hkv"], a["out"], a["lse"], None)
+                           a["window"], a["base"], a["hq"], a["hkv"], a["out"], a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(hkv=7), 1), (dict(window=-2), 1), (dict(batch=-1), 1), (dict(T=-5), 1), (dict(q=None), 1),
     (dict(out=None), 1), (dict(base=0.5), 1), (dict(base=float("inf")), 1), (dict(max_seqlen=0), 1),
-    (dict(batch=0), 1), (dict(hq=0), 1), (dict(cu=None), 1),
+    (dict(batch=0), 1), (dict(hq=0), 1), (dict(cu=None), 1), (dict(ws=None), 4), (dict(wsb=64), 4),
 ])
 def test_fwd_rejects_bad_arguments(L, kw, code):
     assert fwd(L, **kw) == code
@@ -85,6 +86,7 @@ def test_bwd_rejects_bad_arguments(L):
 
 
 def test_workspace_sizes(L):
+    assert L.mimo_attn_fwd_workspace_size(32768, 64, 8, 128) >= 32768 * 8 * 640
     n = L.mimo_attn_bwd_workspace_size(32768, 64, 8, 128)
     assert n >= 32768 * 64 * 4
     assert L.mimo_attn_decode_workspace_size(64, 131072, 64, -1) > 0
