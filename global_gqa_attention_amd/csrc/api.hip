@@ -316,11 +316,7 @@ mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const f
     a.dk = (uint16_t *)dk;
     a.dv = (uint16_t *)dv;
     a.dsink = dsink;
-    // workspace: D [hq, T] fp32, then the dsink partials
-    char *ws = (char *)workspace;
-    a.delta = (float *)ws;
-    size_t off = ((size_t)n_q_heads * total_tokens * sizeof(float) + 255) & ~(size_t)255;
-    a.dsink_part = (float *)(ws + off);
+    mimo::bwd_carve(workspace, total_tokens, n_q_heads, n_kv_heads, &a);
     hipError_t e = mimo::launch_bwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return ok();

@@ -11,15 +11,21 @@
 //
 // Kernels, all on the caller's stream, no atomics (every output is written by exactly one workgroup and
 // dsink is summed in a fixed order, so results are bitwise repeatable):
-//   1. bwd_pre:   D for every (token, head) row.
+//   1. bwd_pre:   D and LSE * log2(e) for every (head, token), zero-padded to T_pad.
 //   2. bwd_dsink: one workgroup per head, fixed-order tree sum (only when a sink is given).
-//   3. bwd_dkdv:  key-major.  A workgroup owns 128 keys of one KV head (32 per wave, the key is the MFMA
-//                 column so each lane owns one key) and walks every (query head of the group, 64-query
-//                 tile) that sees them: S = Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and
-//                 dK^T += Q^T dS with K/V resident in registers and Q/dO staged in LDS in both layouts.
-//   4. bwd_dq:    query-major, laid out like the forward: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then
-//                 dQ^T += K^T dS^T with K staged in LDS row-major and transposed.
-// RoPE is applied when Q/K are loaded and undone (transposed rotation) in the dq/dk epilogues.
+//   3. row_prep:  DMA-ready copies in the workspace: q' (rotated) row-major and transposed, dO transposed,
+//                 k' (rotated) row-major and transposed.  Transposed copies keep each 16-token group's
+//                 4-token chunks in the order (0, 2, 1, 3), the order in which the score registers hold
+//                 tokens, so an MFMA operand read of 8 consecutive elements is one 16-byte LDS read.
+//   4. bwd_dkdv:  key-major.  A workgroup owns 128 keys of one KV head (32 per wave; the key is the MFMA
+//                 column, so each lane owns one key with its rotated k and v resident in registers) and
+//                 walks every (query head of the group, 32-query tile) that sees them: S = Q'K'^T, P,
+//                 dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q'^T dS.  The four query-side tiles
+//                 (q' both layouts, dO both layouts) and LSE/D stream HBM -> LDS with global_load_lds,
+//                 double-buffered and XOR-swizzled (conflict-free operand reads).
+//   5. bwd_dq:    query-major, shaped like the forward: S^T = K'Q'^T, P^T, dP^T = V dO^T, dS^T, then
+//                 dQ^T += K'^T dS^T with k' (both layouts) and v streamed HBM -> LDS.
+// dq and dk leave through the transposed rotation in their epilogues.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -28,35 +34,21 @@ namespace {
 
 constexpr float RSQRT_DQK = 0.07216878364870322f;   // 1 / sqrt(192)
 
-__device__ __forceinline__ int vcol(int r4)
+__device__ __forceinline__ int seq_start_of(const int32_t *cu, int batch, int t)
 {
-    const int c4 = (r4 >> 2) & 3;
-    return (r4 & ~15) | ((((c4 & 1) << 1) | (c4 >> 1)) << 2);
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return cu[lo];
 }
 
-// Copy a row-major R x C bf16 tile into its transpose (C rows of R), with the 4-row chunks of every 16-row
-// group permuted as vcol() says, so that an MFMA A-operand read of 8 consecutive elements returns the rows
-// in the order the score registers hold them.
-template <int R, int C, int SS, int DS>
-__device__ __forceinline__ void transpose_tile(const u16 *src, u16 *dst, int tid)
+// column of token t inside its 16-token group in the transposed copies: 4-token chunks (0, 2, 1, 3)
+__device__ __forceinline__ int tperm16(int t)
 {
-    constexpr int NB = (R / 4) * (C / 8);
-    for (int blk = tid; blk < NB; blk += 256) {
-        const int r4 = blk % (R / 4), c8 = blk / (R / 4);
-        uint4 x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = *(const uint4 *)(src + (4 * r4 + i) * SS + 8 * c8);
-        const u16 *p0 = (const u16 *)&x[0], *p1 = (const u16 *)&x[1];
-        const u16 *p2 = (const u16 *)&x[2], *p3 = (const u16 *)&x[3];
-        const int col = vcol(4 * r4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint2 w;
-            w.x = (uint32_t)p0[e] | ((uint32_t)p1[e] << 16);
-            w.y = (uint32_t)p2[e] | ((uint32_t)p3[e] << 16);
-            *(uint2 *)(dst + (8 * c8 + e) * DS + col) = w;
-        }
-    }
+    const int c4 = (t >> 2) & 3;
+    return (t & ~15) | ((((c4 & 1) << 1) | (c4 >> 1)) << 2) | (t & 3);
 }
 
 // Transposed RoPE of a 32-dim block pair held in C layout: x0 = dims 8(j/4)+4hh+j%4, x1 the same dims + 32.
@@ -71,27 +63,39 @@ __device__ __forceinline__ void rope_back(f32x16 &x0, f32x16 &x1, const float2 *
     }
 }
 
+// LDS swizzles (position of logical 16-byte chunk q in row r):
+//   rows of 8k chunks (row-major q', k', dO, v tiles; 64-token transposed tiles): q ^ (r & 7) in each 8-group
+//   rows of 4 chunks (32-token transposed tiles):                                 q ^ ((r >> 1) & 3)
+// Each makes the 8 lanes of an MFMA operand read (8 consecutive rows, one logical chunk) hit 8 different
+// bank groups.  Both are involutions, so the same function maps positions back to logical chunks.
+__device__ __forceinline__ int swz8(int r, int q) { return (q & ~7) | ((q & 7) ^ (r & 7)); }
+__device__ __forceinline__ int swz4(int r, int q) { return q ^ ((r >> 1) & 3); }
+
 // ------------------------------------------------------------------------------------------------------
-// 1. D = rowsum(dO * O)
+// 1. D = rowsum(dO * O) and LSE * log2(e), both [hq, T_pad] with zero padding
 // ------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A)
 {
     const int tid = threadIdx.x, g = tid >> 4, sub = tid & 15;
-    const long rows = (long)A.L.T * A.L.hq;
+    const long rows = (long)A.T_pad * A.L.hq;
     const long r0 = (long)blockIdx.x * 64;
     for (long r = r0 + g; r < rows && r < r0 + 64; r += 16) {
-        const bf16x8 a = ld16(A.dout + r * DVV + 8 * sub);
-        const bf16x8 b = ld16(A.out + r * DVV + 8 * sub);
-        float s = 0.f;
+        const int t = (int)(r / A.L.hq), h = (int)(r % A.L.hq);
+        float s = 0.f, l2 = 0.f;
+        if (t < A.L.T) {
+            const bf16x8 x = ld16(A.dout + r * DVV + 8 * sub);
+            const bf16x8 y = ld16(A.out + r * DVV + 8 * sub);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += bf2f(a[e]) * bf2f(b[e]);
+            for (int e = 0; e < 8; ++e) s += bf2f(x[e]) * bf2f(y[e]);
+            l2 = A.lse[(size_t)h * A.L.T + t] * LOG2E;
+        }
         s += __shfl_xor(s, 8, 16);
         s += __shfl_xor(s, 4, 16);
         s += __shfl_xor(s, 2, 16);
         s += __shfl_xor(s, 1, 16);
         if (sub == 0) {
-            const int t = (int)(r / A.L.hq), h = (int)(r % A.L.hq);
-            A.delta[(size_t)h * A.L.T + t] = s;
+            A.delta[(size_t)h * A.T_pad + t] = s;
+            A.lse2[(size_t)h * A.T_pad + t] = l2;
         }
     }
 }
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(256) void bwd_dsink_kernel(const BwdArgs A)
     const float sk = A.L.sink[h];
     float acc = 0.f;
     if (sk > -INFINITY) {
-        const float *lse = A.lse + (size_t)h * A.L.T, *dl = A.delta + (size_t)h * A.L.T;
+        const float *lse = A.lse + (size_t)h * A.L.T, *dl = A.delta + (size_t)h * A.T_pad;
         for (int t = tid; t < A.L.T; t += 256) acc -= expf(sk - lse[t]) * dl[t];
     }
     red[tid] = acc;
@@ -125,26 +129,78 @@ __global__ void zero_kernel(float *p, int n)
 }
 
 // ------------------------------------------------------------------------------------------------------
-// 3. dK, dV (key-major)
+// 3. row_prep: for 64 tokens of head h of x [T, H, D]: optional rotation of dims 0..63, then a row-major
+//    copy rm [T_pad, H, D] and/or a transposed copy tr [H, D, T_pad] (tokens in tperm16 order), zero-filled
+//    for tokens T .. T_pad-1.
 // ------------------------------------------------------------------------------------------------------
-constexpr int NKB = 128;        // keys per workgroup (32 per wave)
-constexpr int MQ = 64;          // queries per step
-constexpr int QS = DQK + 8;     // row-major Q stride
-constexpr int OS = DVV + 8;     // row-major dO stride
-constexpr int TS = MQ + 8;      // transposed tiles: stride over queries
+template <int D, bool ROPE>
+__global__ __launch_bounds__(256) void row_prep_kernel(const u16 *x, int H, u16 *rm, u16 *tr, LayerArgs a, int T_pad)
+{
+    __shared__ __attribute__((aligned(16))) u16 sX[64 * (D + 8)];
+    constexpr int CH = D / 8;
+    const int tid = threadIdx.x, h = blockIdx.y, t0 = blockIdx.x * 64;
+    // load (and rotate) 64 rows: thread handles row tid/4, chunks cg, cg+4, cg+8, ...
+    {
+        const int rr = tid >> 2, cg = tid & 3, t = t0 + rr;
+        bf16x8 v[CH / 4];
+        const u16 *src = x + ((size_t)t * H + h) * D;
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i)
+            v[i] = t < a.T ? ld16(src + 8 * (cg + 4 * i)) : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        if (ROPE && t < a.T) {
+            const int pos = t - seq_start_of(a.cu, a.batch, t);
+            const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;
+            float2 c8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c8[e] = cs[e];
+            rope_pair(v[0], v[1], c8);     // chunks cg and cg + 4: dims d and d + 32
+        }
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i) {
+            st16(sX + rr * (D + 8) + 8 * (cg + 4 * i), v[i]);
+            if (rm && t < T_pad) st16(rm + ((size_t)t * H + h) * D + 8 * (cg + 4 * i), v[i]);
+        }
+    }
+    if (!tr) return;
+    __syncthreads();
+    // transposed rows: D dims x 8 chunks of 8 tokens
+    for (int item = tid; item < D * 8; item += 256) {
+        const int d = item >> 3, cc = item & 7;
+        if (t0 + 8 * cc >= T_pad) continue;
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = __builtin_bit_cast(__bf16, sX[tperm16(8 * cc + e) * (D + 8) + d]);
+        st16(tr + ((size_t)h * D + d) * T_pad + t0 + 8 * cc, w);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------
+// 4. dK, dV (key-major)
+// ------------------------------------------------------------------------------------------------------
+constexpr int NKB = 128;                 // keys per workgroup (32 per wave)
+constexpr int MQ = 32;                   // queries per step
+constexpr int QCH = DQK / 8;             // 24 chunks per q' row
+constexpr int OCH = DVV / 8;             // 16 chunks per dO row
+constexpr int TCH = MQ / 8;              // 4 chunks per transposed row
+constexpr int DK_QR = MQ * QCH / 256;    // DMAs per thread per step: q' rows (3)
+constexpr int DK_QT = DQK * TCH / 256;   // q'^T (3)
+constexpr int DK_OR = MQ * OCH / 256;    // dO rows (2)
+constexpr int DK_OT = DVV * TCH / 256;   // dO^T (2)
+constexpr int DK_LOADS = DK_QR + DK_QT + DK_OR + DK_OT + 1;   // + LSE/D (one per wave)
+
+struct DkdvTile {
+    uint4 qr[MQ * QCH], qt[DQK * TCH], orow[MQ * OCH], ot[DVV * TCH];
+    float ld[2 * MQ];                    // LSE * log2(e) [MQ], then D [MQ]
+};
 
 template <bool WIN>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
-    __shared__ __attribute__((aligned(16))) u16 sQ[MQ * QS];
-    __shared__ __attribute__((aligned(16))) u16 sQT[DQK * TS];
-    __shared__ __attribute__((aligned(16))) u16 sO[MQ * OS];
-    __shared__ __attribute__((aligned(16))) u16 sOT[DVV * TS];
-    __shared__ __attribute__((aligned(16))) float sL[MQ];
-    __shared__ __attribute__((aligned(16))) float sD[MQ];
+    __shared__ __attribute__((aligned(16))) DkdvTile t0s, t1s;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c = lane & 31;
     const int G = a.hq / a.hkv;
 
@@ -168,28 +224,58 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int kb0 = seq_start + tile * NKB;
     const int kb_last = min(kb0 + NKB - 1, seq_end - 1);
 
-    // ---- this lane's key, K (rotated) and V as B operands
+    // ---- query steps: tiles of 32 queries from kb0 (aligned down to 16 for the transposed chunk order)
+    const int q_lo = kb0 & ~15;
+    const int q_hi = WIN ? min(seq_end - 1, kb_last + a.window) : seq_end - 1;
+    const int nq = (q_hi - q_lo + MQ) / MQ;
+    const int nsteps = nq * G;
+
+    const size_t qr_row = (size_t)a.hq * DQK, o_row = (size_t)a.hq * DVV;
+    auto issue = [&](int step, DkdvTile &T) {
+        const int h = kvh * G + step / nq;
+        const int q0 = q_lo + (step % nq) * MQ;
+#pragma unroll
+        for (int j = 0; j < DK_QR; ++j) {
+            const int slot = 256 * j + tid, r = slot / QCH, p = slot % QCH;
+            lds_dma16(A.W.qr + (size_t)(q0 + r) * qr_row + (size_t)h * DQK + 8 * swz8(r, p), T.qr + 256 * j + 64 * wave);
+        }
+#pragma unroll
+        for (int j = 0; j < DK_QT; ++j) {
+            const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
+            lds_dma16(A.W.qrt + ((size_t)h * DQK + d) * A.T_pad + q0 + 8 * swz4(d, p), T.qt + 256 * j + 64 * wave);
+        }
+#pragma unroll
+        for (int j = 0; j < DK_OR; ++j) {
+            const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
+            const int row = min(q0 + r, a.T - 1);     // dO is not padded: rows past the end are masked
+            lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz8(r, p), T.orow + 256 * j + 64 * wave);
+        }
+#pragma unroll
+        for (int j = 0; j < DK_OT; ++j) {
+            const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
+            lds_dma16(A.W.dot + ((size_t)h * DVV + d) * A.T_pad + q0 + 8 * swz4(d, p), T.ot + 256 * j + 64 * wave);
+        }
+        {   // LSE*log2e and D: 2 x 128 bytes = 16 chunks, 4 per wave (lanes 0..3 active)
+            const int ch = 4 * wave + (lane & 3);
+            const float *src = (ch < 8 ? A.lse2 + (size_t)h * A.T_pad + q0 + 4 * ch
+                                       : A.delta + (size_t)h * A.T_pad + q0 + 4 * (ch - 8));
+            if (lane < 4) lds_dma16(src, (uint4 *)T.ld + 4 * wave);
+        }
+    };
+
+    // ---- this lane's key: rotated k and v as B operands
     const int kw0 = kb0 + 32 * wave;
     const int kj = kw0 + c;
     const bool kvalid = kj <= kb_last;
     const int kjl = kvalid ? kj : kb_last;
     bf16x8 kf[12], vf[8];
     {
-        const u16 *kp = a.k + ((size_t)kjl * a.hkv + kvh) * DQK + 8 * hh;
+        const u16 *kp = A.W.kr + ((size_t)kjl * a.hkv + kvh) * DQK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 12; ++s) kf[s] = ld16(kp + 16 * s);
         const u16 *vp = a.v + ((size_t)kjl * a.hkv + kvh) * DVV + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 8; ++s) vf[s] = ld16(vp + 16 * s);
-        const float2 *cs = a.rope + (size_t)min(kjl - seq_start, a.rope_len - 1) * NHALF + 8 * hh;
-        float2 c0[8], c1[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            c0[t] = cs[t];
-            c1[t] = cs[16 + t];
-        }
-        rope_pair(kf[0], kf[2], c0);
-        rope_pair(kf[1], kf[3], c1);
     }
 
     f32x16 dk[6], dv[4];
@@ -198,118 +284,70 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
 
-    const int q_lo = kb0;
-    const int q_hi = WIN ? min(seq_end - 1, kb_last + a.window) : seq_end - 1;
-    const int nq = (q_hi - q_lo + MQ) / MQ;
-    const int nsteps = nq * G;
-
-    // ---- staging: Q row (rotated) + dO row + LSE/D for step (h, q0)
-    uint4 qreg[6], oreg[4];
-    float2 qcs[8];
-    float ld_val = 0.f;
-    const int sr = tid >> 2, cg = tid & 3;
-    auto load_step = [&](int step) {
-        const int h = kvh * G + step / nq;
+    auto compute = [&](int step, const DkdvTile &T) {
         const int q0 = q_lo + (step % nq) * MQ;
-        const int qi = min(q0 + sr, q_hi);
-        const u16 *qp = a.q + ((size_t)qi * a.hq + h) * DQK;
-        qreg[0] = ldu4(qp + 8 * cg);
-        qreg[1] = ldu4(qp + 8 * (cg + 4));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qreg[2 + i] = ldu4(qp + 8 * (8 + cg + 4 * i));
-        const float2 *cs = a.rope + (size_t)min(qi - seq_start, a.rope_len - 1) * NHALF + 8 * cg;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) qcs[t] = cs[t];
-        const u16 *op = A.dout + ((size_t)qi * a.hq + h) * DVV;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oreg[i] = ldu4(op + 8 * (cg + 4 * i));
-        if (tid < MQ) ld_val = A.lse[(size_t)h * a.T + min(q0 + tid, q_hi)] * LOG2E;
-        else if (tid < 2 * MQ) ld_val = A.delta[(size_t)h * a.T + min(q0 + tid - MQ, q_hi)];
-    };
-    auto store_step = [&]() {
-        bf16x8 x0 = __builtin_bit_cast(bf16x8, qreg[0]);
-        bf16x8 x1 = __builtin_bit_cast(bf16x8, qreg[1]);
-        rope_pair(x0, x1, qcs);
-        u16 *qd = sQ + sr * QS;
-        st16(qd + 8 * cg, x0);
-        st16(qd + 8 * (cg + 4), x1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st16u(qd + 8 * (8 + cg + 4 * i), qreg[2 + i]);
-        u16 *od = sO + sr * OS;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st16u(od + 8 * (cg + 4 * i), oreg[i]);
-        if (tid < MQ) sL[tid] = ld_val;
-        else if (tid < 2 * MQ) sD[tid - MQ] = ld_val;
-    };
-
-    if (nsteps > 0) load_step(0);
-    for (int step = 0; step < nsteps; ++step) {
-        const int q0 = q_lo + (step % nq) * MQ;
-        __syncthreads();
-        store_step();
-        __syncthreads();
-        transpose_tile<MQ, DQK, QS, TS>(sQ, sQT, tid);
-        transpose_tile<MQ, DVV, OS, TS>(sO, sOT, tid);
-        __syncthreads();
-        if (step + 1 < nsteps) load_step(step + 1);
-
         // does any query of this step see any key of this wave?
-        const bool active = (q0 + MQ - 1 >= kw0) && (kw0 <= kb_last) && (!WIN || q0 <= kw0 + 31 + a.window);
-        if (!active) continue;
-        const bool need_mask = (q0 < kw0 + 31) || (q0 + MQ - 1 > q_hi) ||
-                               (WIN && q0 + MQ - 1 > kw0 + a.window) || (kw0 + 31 > kb_last);
-
-        f32x16 sacc[2], dpacc[2];
+        if (q0 + MQ - 1 < kw0 || kw0 > kb_last || (WIN && q0 > kw0 + 31 + a.window)) return;
+        const bool need_mask = (q0 < kw0 + 31) || (q0 + MQ - 1 > q_hi) || (WIN && q0 + MQ - 1 > kw0 + a.window) ||
+                               (kw0 + 31 > kb_last);
+        const u16 *qr = (const u16 *)T.qr, *orr = (const u16 *)T.orow;
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            sacc[qb] = f32x16{};
-            dpacc[qb] = f32x16{};
-            const u16 *qr = sQ + (32 * qb + c) * QS + 8 * hh;
+        for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(qr + (c * QCH + swz8(c, 2 * s + hh)) * 8), kf[s], sacc);
 #pragma unroll
-            for (int s = 0; s < 12; ++s) sacc[qb] = mfma32(ld16(qr + 16 * s), kf[s], sacc[qb]);
-            const u16 *orow = sO + (32 * qb + c) * OS + 8 * hh;
+        for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(orr + (c * OCH + swz8(c, 2 * s + hh)) * 8), vf[s], dpacc);
+        bf16x8 pb[2], sb[2];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) dpacc[qb] = mfma32(ld16(orow + 16 * s), vf[s], dpacc[qb]);
-        }
-        bf16x8 pb[4], sb[4];
+        for (int jj = 0; jj < 4; ++jj) {
+            const int ql = 8 * jj + 4 * hh;
+            const float4 L4 = *(const float4 *)(T.ld + ql);
+            const float4 D4 = *(const float4 *)(T.ld + MQ + ql);
+            const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+            const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int ql = 32 * qb + 8 * jj + 4 * hh;
-                const float4 L4 = *(const float4 *)(sL + ql);
-                const float4 D4 = *(const float4 *)(sD + ql);
-                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-                const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int j = 4 * jj + t;
-                    float p = fast_exp2(sacc[qb][j] * a.scale_log2 - Lv[t]);
-                    if (need_mask) {
-                        const int qi = q0 + ql + t;
-                        const bool ok = kvalid && qi >= kj && qi <= q_hi && (!WIN || qi - kj <= a.window);
-                        p = ok ? p : 0.f;
-                    }
-                    const float ds = p * (VSCALE * dpacc[qb][j] - Dv[t]);
-                    pb[2 * qb + (j >> 3)][j & 7] = f2bf(p);
-                    sb[2 * qb + (j >> 3)][j & 7] = f2bf(ds);
+            for (int t = 0; t < 4; ++t) {
+                const int j = 4 * jj + t;
+                float p = fast_exp2(sacc[j] * a.scale_log2 - Lv[t]);
+                if (need_mask) {
+                    const int qi = q0 + ql + t;
+                    const bool ok = kvalid && qi >= kj && qi <= q_hi && (!WIN || qi - kj <= a.window);
+                    p = ok ? p : 0.f;
                 }
+                pb[j >> 3][j & 7] = f2bf(p);
+                sb[j >> 3][j & 7] = f2bf(p * (VSCALE * dpacc[j] - Dv[t]));
             }
         }
-        // dV^T += dO^T P,  dK^T += Q^T dS
+        // dV^T += dO^T P,  dK^T += Q'^T dS  (two 16-query k-steps)
+        const u16 *ot = (const u16 *)T.ot, *qt = (const u16 *)T.qt;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const u16 *tr = sOT + (32 * i + c) * TS + 8 * hh;
+            const int d = 32 * i + c;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) dv[i] = mfma32(ld16(tr + 16 * s), pb[s], dv[i]);
+            for (int s = 0; s < 2; ++s) dv[i] = mfma32(ld16(ot + (d * TCH + swz4(d, 2 * s + hh)) * 8), pb[s], dv[i]);
         }
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
-            const u16 *tr = sQT + (32 * i + c) * TS + 8 * hh;
+            const int d = 32 * i + c;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) dk[i] = mfma32(ld16(tr + 16 * s), sb[s], dk[i]);
+            for (int s = 0; s < 2; ++s) dk[i] = mfma32(ld16(qt + (d * TCH + swz4(d, 2 * s + hh)) * 8), sb[s], dk[i]);
         }
+    };
+
+    // ---- double-buffered step loop (same load/wait/barrier pattern as the forward)
+    issue(0, t0s);
+    for (int st = 0; st < nsteps; st += 2) {
+        issue(min(st + 1, nsteps - 1), t1s);
+        wait_vmcnt<DK_LOADS>();
+        __builtin_amdgcn_s_barrier();
+        compute(st, t0s);
+        __builtin_amdgcn_s_barrier();
+        issue(min(st + 2, nsteps - 1), t0s);
+        wait_vmcnt<DK_LOADS>();
+        __builtin_amdgcn_s_barrier();
+        if (st + 1 < nsteps) compute(st + 1, t1s);
+        __builtin_amdgcn_s_barrier();
     }
+    wait_vmcnt<0>();
 
     // ---- epilogue: dv = 0.707 * dV^T, dk = R^T dK^T / sqrt(192)
     if (kvalid) {
@@ -341,24 +379,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
 }
 
 // ------------------------------------------------------------------------------------------------------
-// 4. dQ (query-major)
+// 5. dQ (query-major)
 // ------------------------------------------------------------------------------------------------------
-constexpr int BM = 128;        // query rows per workgroup
-constexpr int BN = 64;         // keys per tile
-constexpr int KS = DQK + 8;
-constexpr int VS = DVV + 8;
-constexpr int KTS = BN + 8;
+constexpr int BN = 64;                   // keys per tile
+constexpr int KCH = DQK / 8;             // 24 chunks per k' row
+constexpr int VCH = DVV / 8;             // 16 chunks per v row
+constexpr int KTCH = BN / 8;             // 8 chunks per k'^T row
 
-template <int GP, bool WIN>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdArgs A)
+struct DqTile {
+    uint4 kr[BN * KCH], kt[DQK * KTCH], vr[BN * VCH];
+};
+
+template <int NW, int GP, bool WIN>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
-    __shared__ __attribute__((aligned(16))) u16 sK[BN * KS];
-    __shared__ __attribute__((aligned(16))) u16 sKT[DQK * KTS];
-    __shared__ __attribute__((aligned(16))) u16 sV[BN * VS];
+    constexpr int NT = 64 * NW, BM = 32 * NW, TT = BM / GP;
+    constexpr int L_KR = BN * KCH / NT, L_KT = DQK * KTCH / NT, L_VR = BN * VCH / NT;
+    constexpr int DQ_LOADS = L_KR + L_KT + L_VR;
+    __shared__ __attribute__((aligned(16))) DqTile t0s, t1s;
 
-    constexpr int TT = BM / GP;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c = lane & 31;
     const int G = a.hq / a.hkv;
     const int n_hg = G / GP;
@@ -384,116 +426,109 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdArgs A)
     const int t_last = min(t0 + TT - 1, seq_end - 1);
     const int h0 = kvh * G + hgi * GP;
 
+    const int klo = WIN ? max(seq_start, t0 - a.window) : seq_start;
+    const int kstart = klo & ~15;
+    const int khi = t_last;
+    const int nkt = (khi - kstart + BN) / BN;
+
+    const u16 *kr_g = A.W.kr + (size_t)kvh * DQK, *kt_g = A.W.krt + (size_t)kvh * DQK * A.T_pad;
+    const size_t kr_row = (size_t)a.hkv * DQK, v_row = (size_t)a.hkv * DVV;
+    auto issue = [&](int k0, DqTile &T) {
+#pragma unroll
+        for (int j = 0; j < L_KR; ++j) {
+            const int slot = NT * j + tid, r = slot / KCH, p = slot % KCH;
+            lds_dma16(kr_g + (size_t)(k0 + r) * kr_row + 8 * swz8(r, p), T.kr + NT * j + 64 * wave);
+        }
+#pragma unroll
+        for (int j = 0; j < L_KT; ++j) {
+            const int slot = NT * j + tid, d = slot / KTCH, p = slot % KTCH;
+            lds_dma16(kt_g + (size_t)d * A.T_pad + k0 + 8 * swz8(d, p), T.kt + NT * j + 64 * wave);
+        }
+#pragma unroll
+        for (int j = 0; j < L_VR; ++j) {
+            const int slot = NT * j + tid, r = slot / VCH, p = slot % VCH;
+            const int row = min(k0 + r, a.T - 1);     // v is not padded: rows past the end are masked
+            lds_dma16(a.v + (size_t)row * v_row + (size_t)kvh * DVV + 8 * swz8(r, p), T.vr + NT * j + 64 * wave);
+        }
+    };
+    issue(kstart, t0s);
+
     const int r = wave * 32 + c;
     const int qt = t0 + r / GP;
     const int qh = h0 + r % GP;
     const bool qvalid = qt < seq_end;
     const int qtl = qvalid ? qt : t_last;
-
     bf16x8 qf[12], of[8];
     const float2 *qcs = a.rope + (size_t)min(qtl - seq_start, a.rope_len - 1) * NHALF;
     {
-        const u16 *qp = a.q + ((size_t)qtl * a.hq + qh) * DQK + 8 * hh;
+        const u16 *qp = A.W.qr + ((size_t)qtl * a.hq + qh) * DQK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
         const u16 *op = A.dout + ((size_t)qtl * a.hq + qh) * DVV + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 8; ++s) of[s] = ld16(op + 16 * s);
-        float2 c0[8], c1[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            c0[t] = qcs[8 * hh + t];
-            c1[t] = qcs[16 + 8 * hh + t];
-        }
-        rope_pair(qf[0], qf[2], c0);
-        rope_pair(qf[1], qf[3], c1);
     }
-    const float Lq = A.lse[(size_t)qh * a.T + qtl] * LOG2E;
-    const float Dq = A.delta[(size_t)qh * a.T + qtl];
+    const float Lq = A.lse2[(size_t)qh * A.T_pad + qtl];
+    const float Dq = A.delta[(size_t)qh * A.T_pad + qtl];
 
-    const int klo = WIN ? max(seq_start, t0 - a.window) : seq_start;
-    const int khi = t_last;
-    const int nkt = (khi - klo + BN) / BN;
+    const int wt0 = t0 + (wave * 32) / GP;
+    const int wt1 = min(t0 + (wave * 32 + 31) / GP, seq_end - 1);
+    const int wklo = WIN ? max(seq_start, wt0 - a.window) : seq_start;
+    const int wkhi = wt1;
 
     f32x16 dq[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) dq[i] = f32x16{};
 
-    uint4 kreg[6], vreg[4];
-    float2 kcs[8];
-    const int kk = tid >> 2, cg = tid & 3;
-    auto load_tile = [&](int k0) {
-        const int key = min(k0 + kk, khi);
-        const u16 *kp = a.k + ((size_t)key * a.hkv + kvh) * DQK;
-        kreg[0] = ldu4(kp + 8 * cg);
-        kreg[1] = ldu4(kp + 8 * (cg + 4));
+    auto compute = [&](int k0, const DqTile &T) {
+        const u16 *kr = (const u16 *)T.kr, *kt = (const u16 *)T.kt, *vr = (const u16 *)T.vr;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kreg[2 + i] = ldu4(kp + 8 * (8 + cg + 4 * i));
-        const float2 *cs = a.rope + (size_t)min(key - seq_start, a.rope_len - 1) * NHALF + 8 * cg;
+        for (int kb = 0; kb < 2; ++kb) {
+            const int kbase = k0 + 32 * kb;
+            if (kbase > wkhi || kbase + 31 < wklo) continue;
+            const int rr = 32 * kb + c;
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) kcs[t] = cs[t];
-        const u16 *vp = a.v + ((size_t)key * a.hkv + kvh) * DVV;
+            for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(kr + (rr * KCH + swz8(rr, 2 * s + hh)) * 8), qf[s], sacc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vreg[i] = ldu4(vp + 8 * (cg + 4 * i));
-    };
-    auto store_tile = [&]() {
-        bf16x8 x0 = __builtin_bit_cast(bf16x8, kreg[0]);
-        bf16x8 x1 = __builtin_bit_cast(bf16x8, kreg[1]);
-        rope_pair(x0, x1, kcs);
-        u16 *kd = sK + kk * KS;
-        st16(kd + 8 * cg, x0);
-        st16(kd + 8 * (cg + 4), x1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st16u(kd + 8 * (8 + cg + 4 * i), kreg[2 + i]);
-        u16 *vd = sV + kk * VS;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st16u(vd + 8 * (cg + 4 * i), vreg[i]);
-    };
-
-    load_tile(klo);
-    for (int it = 0; it < nkt; ++it) {
-        const int k0 = klo + it * BN;
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        transpose_tile<BN, DQK, KS, KTS>(sK, sKT, tid);
-        __syncthreads();
-        if (it + 1 < nkt) load_tile(k0 + BN);
-
-        const bool need_mask = (k0 + BN - 1 > t0) || (WIN && k0 < t_last - a.window);
-        f32x16 sacc[2], dpacc[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            sacc[b] = f32x16{};
-            dpacc[b] = f32x16{};
-            const u16 *kr = sK + (32 * b + c) * KS + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 12; ++s) sacc[b] = mfma32(ld16(kr + 16 * s), qf[s], sacc[b]);
-            const u16 *vr = sV + (32 * b + c) * VS + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) dpacc[b] = mfma32(ld16(vr + 16 * s), of[s], dpacc[b]);
-        }
-        bf16x8 sb[4];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
+            for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(vr + (rr * VCH + swz8(rr, 2 * s + hh)) * 8), of[s], dpacc);
+            const bool need_mask = (kbase + 31 > wt0) || (kbase < seq_start) || (WIN && kbase < wt1 - a.window);
+            bf16x8 sb[2];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                float p = fast_exp2(sacc[b][j] * a.scale_log2 - Lq);
+                float p = fast_exp2(sacc[j] * a.scale_log2 - Lq);
                 if (need_mask) {
-                    const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    const bool ok = key <= qt && key <= khi && (!WIN || key >= qt - a.window);
+                    const int key = kbase + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    const bool ok = key <= qt && key >= seq_start && (!WIN || key >= qt - a.window);
                     p = ok ? p : 0.f;
                 }
-                sb[2 * b + (j >> 3)][j & 7] = f2bf(p * (VSCALE * dpacc[b][j] - Dq));
+                sb[j >> 3][j & 7] = f2bf(p * (VSCALE * dpacc[j] - Dq));
+            }
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int d = 32 * i + c;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    dq[i] = mfma32(ld16(kt + (d * KTCH + swz8(d, 4 * kb + 2 * s + hh)) * 8), sb[s], dq[i]);
             }
         }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const u16 *tr = sKT + (32 * i + c) * KTS + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) dq[i] = mfma32(ld16(tr + 16 * s), sb[s], dq[i]);
-        }
+    };
+
+    const int klast = kstart + (nkt - 1) * BN;
+    for (int it = 0; it < nkt; it += 2) {
+        const int k0 = kstart + it * BN;
+        issue(min(k0 + BN, klast), t1s);
+        wait_vmcnt<DQ_LOADS>();
+        __builtin_amdgcn_s_barrier();
+        compute(k0, t0s);
+        __builtin_amdgcn_s_barrier();
+        issue(min(k0 + 2 * BN, klast), t0s);
+        wait_vmcnt<DQ_LOADS>();
+        __builtin_amdgcn_s_barrier();
+        if (it + 1 < nkt) compute(k0 + BN, t1s);
+        __builtin_amdgcn_s_barrier();
     }
+    wait_vmcnt<0>();
 
     if (qvalid) {
         rope_back(dq[0], dq[1], qcs, hh);
@@ -515,17 +550,31 @@ template <int GP>
 hipError_t launch_dq(const BwdArgs &A, hipStream_t stream)
 {
     const LayerArgs &a = A.L;
-    constexpr int TT = BM / GP;
     const int G = a.hq / a.hkv;
+    const bool win = a.window >= 0;
+    // 4 waves (one per SIMD): the dq accumulators, q'/dO operands and scores need more than the 256
+    // registers a wave may hold at two waves per SIMD
+    constexpr int NW = 4;
+    const int TT = 32 * NW / GP;
     const long tiles = (long)(a.T + TT - 1) / TT + a.batch;
     const long grid = tiles * (G / GP) * a.hkv;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    trace_begin(a.window >= 0 ? "bwd_dq_swa" : "bwd_dq_global", stream);
-    if (a.window >= 0) bwd_dq_kernel<GP, true><<<(unsigned)grid, 256, 0, stream>>>(A);
-    else bwd_dq_kernel<GP, false><<<(unsigned)grid, 256, 0, stream>>>(A);
+    trace_begin(win ? "bwd_dq_swa" : "bwd_dq_global", stream);
+    if (win) bwd_dq_kernel<NW, GP, true><<<(unsigned)grid, 64 * NW, 0, stream>>>(A);
+    else bwd_dq_kernel<NW, GP, false><<<(unsigned)grid, 64 * NW, 0, stream>>>(A);
     trace_end(stream);
     return hipGetLastError();
 }
+
+template <int D, bool ROPE>
+hipError_t launch_row_prep(const u16 *x, int H, u16 *rm, u16 *tr, const LayerArgs &a, int T_pad, hipStream_t stream)
+{
+    dim3 grid((T_pad + 63) / 64, H);
+    row_prep_kernel<D, ROPE><<<grid, 256, 0, stream>>>(x, H, rm, tr, a, T_pad);
+    return hipGetLastError();
+}
+
+size_t al(size_t n) { return (n + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -538,18 +587,40 @@ hipError_t launch_zero_f32(float *p, int n, hipStream_t stream)
     return hipGetLastError();
 }
 
+// workspace: lse2 and D [hq, T_pad] fp32, q' [T_pad, hq, 192], q'^T [hq, 192, T_pad], dO^T [hq, 128, T_pad],
+// k' [T_pad, hkv, 192], k'^T [hkv, 192, T_pad] (bf16), each 256-byte aligned
 size_t bwd_workspace_bytes(int T, int hq, int hkv, int window)
 {
-    (void)hkv;
     (void)window;
-    const size_t delta = ((size_t)hq * T * sizeof(float) + 255) & ~(size_t)255;
-    return delta + 256;
+    const size_t tp = (size_t)prep_tpad(T);
+    return 2 * al(tp * hq * 4) + al(tp * hq * DQK * 2) + al(tp * hq * DQK * 2) + al(tp * hq * DVV * 2) +
+           al(tp * hkv * DQK * 2) + al(tp * hkv * DQK * 2);
+}
+
+void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A)
+{
+    const size_t tp = (size_t)prep_tpad(T);
+    char *p = (char *)ws;
+    A->T_pad = (int)tp;
+    A->lse2 = (float *)p;
+    p += al(tp * hq * 4);
+    A->delta = (float *)p;
+    p += al(tp * hq * 4);
+    A->W.qr = (u16 *)p;
+    p += al(tp * hq * DQK * 2);
+    A->W.qrt = (u16 *)p;
+    p += al(tp * hq * DQK * 2);
+    A->W.dot = (u16 *)p;
+    p += al(tp * hq * DVV * 2);
+    A->W.kr = (u16 *)p;
+    p += al(tp * hkv * DQK * 2);
+    A->W.krt = (u16 *)p;
 }
 
 hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
 {
     const LayerArgs &a = A.L;
-    const long rows = (long)a.T * a.hq;
+    const long rows = (long)A.T_pad * a.hq;
     const long pre_blocks = (rows + 63) / 64;
     if (pre_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     trace_begin("bwd_pre", stream);
@@ -559,12 +630,18 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     if (e != hipSuccess) return e;
     if (A.dsink) {
         trace_begin("bwd_dsink", stream);
-        if (a.T > 0) bwd_dsink_kernel<<<a.hq, 256, 0, stream>>>(A);
-        else zero_kernel<<<(a.hq + 255) / 256, 256, 0, stream>>>(A.dsink, a.hq);
+        bwd_dsink_kernel<<<a.hq, 256, 0, stream>>>(A);
         trace_end(stream);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    trace_begin("bwd_prep", stream);
+    e = launch_row_prep<DQK, true>(a.q, a.hq, A.W.qr, A.W.qrt, a, A.T_pad, stream);
+    if (e == hipSuccess) e = launch_row_prep<DVV, false>(A.dout, a.hq, nullptr, A.W.dot, a, A.T_pad, stream);
+    if (e == hipSuccess) e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.W.krt, a, A.T_pad, stream);
+    trace_end(stream);
+    if (e != hipSuccess) return e;
+
     const long kv_tiles = (long)(a.T + NKB - 1) / NKB + a.batch;
     const long kv_grid = kv_tiles * a.hkv;
     if (kv_grid > 0x7fffffffL) return hipErrorInvalidConfiguration;

@@ -8,34 +8,34 @@
 // "feat(models): add MiMo-V2.6-Flash-RL support" (asymmetric Q/K vs V channels, sink on SWA layers).
 //
 // Design (gfx950, wave64):
-//   * A workgroup of 4 waves owns 256 query rows: TT = 256 / GP consecutive tokens x GP query heads that
-//     share one KV head; each wave owns 64 rows as two 32-row MFMA column blocks, so every K/V operand
-//     read from LDS feeds two MFMAs (32 rows per wave would make LDS bandwidth, not MFMA, the limit).
-//     Packing heads keeps a sliding-window tile's key span short and lets all GP heads reuse each K/V
-//     tile staged in LDS; 32-key blocks that no row of a wave can see are skipped.
+//   * A prep kernel (attn_prep.hip) first writes RoPE-rotated K and per-head transposed V into the
+//     workspace.  The hot loop then moves K and V^T tiles from HBM straight into LDS with
+//     global_load_lds_dwordx4 (no register staging, no per-tile arithmetic), double-buffered: the next tile
+//     is in flight while the current one is computed, ordered by one explicit vmcnt wait and plain
+//     s_barriers.  The 16-byte chunks of each LDS row are XOR-swizzled by row (the per-lane source
+//     addresses are permuted), so every MFMA operand read is free of bank conflicts.
+//   * Each wave owns 32 query rows; a workgroup of NW waves owns 32 NW rows: TT = 32 NW / GP consecutive
+//     tokens x GP query heads of one KV group, so all GP heads reuse every K/V tile.  Causal layers use 8
+//     waves (two per SIMD, one K/V stream for 256 rows), sliding-window layers 4 waves (a short key span:
+//     the tile's tokens plus 128 keys back).  32-key blocks that no row of a wave can see are skipped.
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: the query is the MFMA column, so each lane owns a query
 //     (lanes l and l ^ 32 split its keys); row max and row sum need one permlane32 swap, and the rescale of
-//     the output accumulator is per lane.  O^T = V^T . P^T reuses the score registers as the B operand.
-//   * K tiles are rotated while being staged into LDS (cos/sin from a table built in fp64); Q is rotated
-//     once in registers.  V is staged transposed, with its 4-key chunks permuted so that the keys a lane
-//     needs for P^T come out of LDS as one 16-byte read.  LDS is double-buffered: one barrier per tile,
-//     and the next tile's HBM loads are in flight while the current tile is computed.
+//     the output accumulator is per lane.  O^T = V^T . P^T takes the score registers as its B operand, with
+//     V^T's 4-key chunks stored in the order the score registers hold the keys.  Q is rotated once in
+//     registers (cos/sin from a table built in fp64).
 //   * Online softmax in base 2 (scale folded into one multiply); the sink starts the running max and sum.
 //     The reference max moves only when a block's max exceeds it by 2^8, so most blocks skip the rescale
-//     of the accumulator (the result is exact either way: numerator and denominator share the reference).
-//     Only blocks that cross the causal or window boundary evaluate the mask.
+//     of the accumulator (exact either way: numerator and denominator share the reference); the branch is
+//     wave-uniform.  Only blocks that cross a causal, window or sequence boundary evaluate the mask.
 #include "device_common.hpp"
 #include "internal.hpp"
 
 namespace mimo {
 namespace {
 
-constexpr int BM = 128;        // query rows per workgroup (32 per wave: one MFMA column block)
 constexpr int BN = 64;         // keys per tile
 constexpr int KCH = DQK / 8;   // 16-byte chunks per K row (24)
 constexpr int VCH = BN / 8;    // 16-byte chunks per V^T row (8)
-constexpr int KLOADS = BN * KCH / 256;    // global_load_lds per thread per K tile (6)
-constexpr int VLOADS = DVV * VCH / 256;   // ... per V^T tile (4)
 constexpr float RESCALE_TH = 8.f;         // keep a stale running max until the true one exceeds it by 2^8
 
 // K tile in LDS: row r (key), 24 chunks of 16 B; logical chunk q sits at position q ^ (r & 7) inside its
@@ -44,9 +44,15 @@ constexpr float RESCALE_TH = 8.f;         // keep a stale running max until the 
 __device__ __forceinline__ int kpos(int r, int q) { return (q & ~7) | ((q & 7) ^ (r & 7)); }
 __device__ __forceinline__ int vpos(int d, int q) { return q ^ (d & 7); }
 
-template <int GP, bool SINK, bool WIN>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdArgs A)
+// NW waves per workgroup (32 query rows each) share one stream of K/V tiles: 8 for causal layers (half
+// the L2 -> LDS tile traffic), 4 for sliding-window layers (shorter key span per workgroup).
+template <int NW, int GP, bool SINK, bool WIN>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs A)
 {
+    constexpr int NT = 64 * NW;                // threads per workgroup
+    constexpr int BM = 32 * NW;                // query rows per workgroup
+    constexpr int KLOADS = BN * KCH / NT;      // global_load_lds per thread per K tile
+    constexpr int VLOADS = DVV * VCH / NT;     // ... per V^T tile
     const LayerArgs &a = A.L;
     __shared__ __attribute__((aligned(16))) uint4 sK0[BN * KCH];
     __shared__ __attribute__((aligned(16))) uint4 sV0[DVV * VCH];
@@ -90,24 +96,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdArgs A)
     const int khi = t_last;
     const int nkt = (khi - kstart + BN) / BN;
 
-    // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = 256 j + tid of each array)
+    // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = NT j + tid of each array)
     const u16 *kr_base = A.P.kr + (size_t)kvh * DQK;
     const size_t kr_row = (size_t)a.hkv * DQK;
     const u16 *vt_base = A.P.vt + (size_t)kvh * DVV * A.P.T_pad;
     auto issue_tile = [&](int k0, uint4 *sk, uint4 *sv) {
 #pragma unroll
         for (int j = 0; j < KLOADS; ++j) {
-            const int slot = 256 * j + tid;
+            const int slot = NT * j + tid;
             const int r = slot / KCH, p = slot % KCH;
             const u16 *src = kr_base + (size_t)(k0 + r) * kr_row + 8 * kpos(r, p);   // kpos is an involution
-            lds_dma16(src, sk + 256 * j + 64 * wave);
+            lds_dma16(src, sk + NT * j + 64 * wave);
         }
 #pragma unroll
         for (int j = 0; j < VLOADS; ++j) {
-            const int slot = 256 * j + tid;
+            const int slot = NT * j + tid;
             const int d = slot / VCH, p = slot % VCH;
             const u16 *src = vt_base + (size_t)d * A.P.T_pad + k0 + 8 * vpos(d, p);
-            lds_dma16(src, sv + 256 * j + 64 * wave);
+            lds_dma16(src, sv + NT * j + 64 * wave);
         }
     };
     issue_tile(kstart, sK0, sV0);
@@ -254,19 +260,20 @@ template <int GP>
 hipError_t launch_gp(const FwdArgs &A, hipStream_t stream)
 {
     const LayerArgs &a = A.L;
-    constexpr int TT = BM / GP;
     const int G = a.hq / a.hkv;
+    const bool sink = a.sink != nullptr, win = a.window >= 0;
+    const int NW = win ? 4 : 8;
+    const int TT = 32 * NW / GP;
     // upper bound on the number of token tiles: sum ceil(len/TT) <= ceil(T/TT) + batch
     const long tiles = (long)(a.T + TT - 1) / TT + a.batch;
     const long grid = tiles * (G / GP) * a.hkv;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    const bool sink = a.sink != nullptr, win = a.window >= 0;
     trace_begin(win ? "attn_fwd_swa" : "attn_fwd_global", stream);
-    if (sink && win) attn_fwd_kernel<GP, true, true><<<(unsigned)grid, 256, 0, stream>>>(A);
-    else if (sink) attn_fwd_kernel<GP, true, false><<<(unsigned)grid, 256, 0, stream>>>(A);
-    else if (win) attn_fwd_kernel<GP, false, true><<<(unsigned)grid, 256, 0, stream>>>(A);
-    else attn_fwd_kernel<GP, false, false><<<(unsigned)grid, 256, 0, stream>>>(A);
+    if (sink && win) attn_fwd_kernel<4, GP, true, true><<<(unsigned)grid, 256, 0, stream>>>(A);
+    else if (win) attn_fwd_kernel<4, GP, false, true><<<(unsigned)grid, 256, 0, stream>>>(A);
+    else if (sink) attn_fwd_kernel<8, GP, true, false><<<(unsigned)grid, 512, 0, stream>>>(A);
+    else attn_fwd_kernel<8, GP, false, false><<<(unsigned)grid, 512, 0, stream>>>(A);
     trace_end(stream);
     return hipGetLastError();
 }

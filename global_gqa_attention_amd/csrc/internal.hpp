@@ -32,16 +32,27 @@ struct FwdArgs {
     float *lse;                    // fp32 [hq,T] or nullptr
 };
 
+// DMA-ready copies the backward prepares in its workspace (see attn_bwd.hip).
+struct BwdPrep {
+    uint16_t *qr;                  // bf16 [T_pad, hq, 192]   q with RoPE applied
+    uint16_t *qrt;                 // bf16 [hq, 192, T_pad]   the same, transposed (token chunks permuted)
+    uint16_t *dot;                 // bf16 [hq, 128, T_pad]   dO transposed (token chunks permuted)
+    uint16_t *kr;                  // bf16 [T_pad, hkv, 192]  k with RoPE applied
+    uint16_t *krt;                 // bf16 [hkv, 192, T_pad]  the same, transposed
+};
+
 struct BwdArgs {
     LayerArgs L;
+    BwdPrep W;
     const uint16_t *out, *dout;    // bf16 [T,hq,128]
     const float *lse;              // [hq,T]
     uint16_t *dq, *dk, *dv;        // bf16 outputs
     float *dsink;                  // [hq] or nullptr
-    float *delta;                  // workspace: D = rowsum(dO * O) [hq,T]
-    float *dsink_part;             // workspace: per-block partial dsink sums
-    int dsink_blocks;              // number of partial blocks per head
+    float *delta;                  // workspace: D = rowsum(dO * O) [hq,T_pad]
+    float *lse2;                   // workspace: LSE * log2(e) [hq,T_pad]
+    int T_pad;
 };
+void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A);
 
 struct DecodeArgs {
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
