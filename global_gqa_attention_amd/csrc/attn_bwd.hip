@@ -63,14 +63,6 @@ __device__ __forceinline__ void rope_back(f32x16 &x0, f32x16 &x1, const float2 *
     }
 }
 
-// LDS swizzles (position of logical 16-byte chunk q in row r):
-//   rows of 8k chunks (row-major q', k', dO, v tiles; 64-token transposed tiles): q ^ (r & 7) in each 8-group
-//   rows of 4 chunks (32-token transposed tiles):                                 q ^ ((r >> 1) & 3)
-// Each makes the 8 lanes of an MFMA operand read (8 consecutive rows, one logical chunk) hit 8 different
-// bank groups.  Both are involutions, so the same function maps positions back to logical chunks.
-__device__ __forceinline__ int swz8(int r, int q) { return (q & ~7) | ((q & 7) ^ (r & 7)); }
-__device__ __forceinline__ int swz4(int r, int q) { return q ^ ((r >> 1) & 3); }
-
 // ------------------------------------------------------------------------------------------------------
 // 1. D = rowsum(dO * O) and LSE * log2(e), both [hq, T_pad] with zero padding
 // ------------------------------------------------------------------------------------------------------
@@ -197,17 +189,19 @@ template <bool WIN>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
-    __shared__ __attribute__((aligned(16))) DkdvTile t0s, t1s;
+    __shared__ __attribute__((aligned(16))) DkdvTile t0s, t1s, t2s;   // three-stage ring (121 KB)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c = lane & 31;
     const int G = a.hq / a.hkv;
 
-    // ---- work item: KV head fastest; key tiles of the sequences from last to first
+    // ---- work item: KV head fastest, then head split, then key tiles of the sequences from last to first
     const int x = blockIdx.x;
     const int kvh = x % a.hkv;
-    int tile = x / a.hkv;
+    const int split = (x / a.hkv) % A.splits;
+    int tile = x / a.hkv / A.splits;
+    const int GS = G / A.splits;      // query heads handled by this workgroup
     int seq_start = 0, seq_end = 0;
     bool found = false;
     for (int b = a.batch - 1; b >= 0; --b) {
@@ -228,39 +222,63 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int q_lo = kb0 & ~15;
     const int q_hi = WIN ? min(seq_end - 1, kb_last + a.window) : seq_end - 1;
     const int nq = (q_hi - q_lo + MQ) / MQ;
-    const int nsteps = nq * G;
+    const int nsteps = nq * GS;
 
+    // ---- direct HBM -> LDS loads of one step's tiles: fixed per-lane byte offsets + wave-uniform bases
     const size_t qr_row = (size_t)a.hq * DQK, o_row = (size_t)a.hq * DVV;
+    uint32_t o_qr[DK_QR], o_qt[DK_QT], o_or[DK_OR], o_ot[DK_OT];
+#pragma unroll
+    for (int j = 0; j < DK_QR; ++j) {
+        const int slot = 256 * j + tid, r = slot / QCH, p = slot % QCH;
+        o_qr[j] = (uint32_t)((r * qr_row + 8 * swz384(r, p)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < DK_QT; ++j) {
+        const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
+        o_qt[j] = (uint32_t)(((size_t)d * A.T_pad + 8 * swz64(d, p)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < DK_OR; ++j) {
+        const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
+        o_or[j] = (uint32_t)((r * o_row + 8 * swz256(r, p)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < DK_OT; ++j) {
+        const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
+        o_ot[j] = (uint32_t)(((size_t)d * A.T_pad + 8 * swz64(d, p)) * 2);
+    }
+    // step -> (head, query tile): heads outer, query tiles from the sequence end down.  Every key tile of a
+    // sequence walks the same absolute query tiles in the same order, so the workgroups running together
+    // on an XCD read the same q'/dO tiles and mostly hit in L2.
+    auto step_q0 = [&](int step) { return q_lo + (nq - 1 - step % nq) * MQ; };
     auto issue = [&](int step, DkdvTile &T) {
-        const int h = kvh * G + step / nq;
-        const int q0 = q_lo + (step % nq) * MQ;
+        const int h = kvh * G + split * GS + step / nq;
+        const int q0 = step_q0(step);
+        const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
+        const u16 *bqt = A.W.qrt + (size_t)h * DQK * A.T_pad + q0;
+        const u16 *bo = A.dout + ((size_t)q0 * a.hq + h) * DVV;
+        const u16 *bot = A.W.dot + (size_t)h * DVV * A.T_pad + q0;
 #pragma unroll
-        for (int j = 0; j < DK_QR; ++j) {
-            const int slot = 256 * j + tid, r = slot / QCH, p = slot % QCH;
-            lds_dma16(A.W.qr + (size_t)(q0 + r) * qr_row + (size_t)h * DQK + 8 * swz8(r, p), T.qr + 256 * j + 64 * wave);
+        for (int j = 0; j < DK_QR; ++j) lds_dma16(bq, o_qr[j], T.qr + 256 * j + 64 * wave);
+#pragma unroll
+        for (int j = 0; j < DK_QT; ++j) lds_dma16(bqt, o_qt[j], T.qt + 256 * j + 64 * wave);
+        if (q0 + MQ <= a.T) {
+#pragma unroll
+            for (int j = 0; j < DK_OR; ++j) lds_dma16(bo, o_or[j], T.orow + 256 * j + 64 * wave);
+        } else {
+            // dO is not padded: rows past its end are clamped to the last row (and masked)
+#pragma unroll
+            for (int j = 0; j < DK_OR; ++j) {
+                const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
+                const int row = min(q0 + r, a.T - 1);
+                lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256(r, p), T.orow + 256 * j + 64 * wave);
+            }
         }
 #pragma unroll
-        for (int j = 0; j < DK_QT; ++j) {
-            const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
-            lds_dma16(A.W.qrt + ((size_t)h * DQK + d) * A.T_pad + q0 + 8 * swz4(d, p), T.qt + 256 * j + 64 * wave);
-        }
-#pragma unroll
-        for (int j = 0; j < DK_OR; ++j) {
-            const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
-            const int row = min(q0 + r, a.T - 1);     // dO is not padded: rows past the end are masked
-            lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz8(r, p), T.orow + 256 * j + 64 * wave);
-        }
-#pragma unroll
-        for (int j = 0; j < DK_OT; ++j) {
-            const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
-            lds_dma16(A.W.dot + ((size_t)h * DVV + d) * A.T_pad + q0 + 8 * swz4(d, p), T.ot + 256 * j + 64 * wave);
-        }
-        {   // LSE*log2e and D: 2 x 128 bytes = 16 chunks, 4 per wave (lanes 0..3 active)
-            const int ch = 4 * wave + (lane & 3);
-            const float *src = (ch < 8 ? A.lse2 + (size_t)h * A.T_pad + q0 + 4 * ch
-                                       : A.delta + (size_t)h * A.T_pad + q0 + 4 * (ch - 8));
-            if (lane < 4) lds_dma16(src, (uint4 *)T.ld + 4 * wave);
-        }
+        for (int j = 0; j < DK_OT; ++j) lds_dma16(bot, o_ot[j], T.ot + 256 * j + 64 * wave);
+        // LSE*log2e (waves 0, 1) and D (waves 2, 3): 2 x 128 bytes, four lanes of each wave load 16 bytes
+        const float *bld = (wave < 2 ? A.lse2 : A.delta) + (size_t)h * A.T_pad + q0 + 16 * (wave & 1);
+        if (lane < 4) lds_dma16(bld, (uint32_t)(16 * lane), (uint4 *)T.ld + 4 * wave);
     };
 
     // ---- this lane's key: rotated k and v as B operands
@@ -285,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
 
     auto compute = [&](int step, const DkdvTile &T) {
-        const int q0 = q_lo + (step % nq) * MQ;
+        const int q0 = step_q0(step);
         // does any query of this step see any key of this wave?
         if (q0 + MQ - 1 < kw0 || kw0 > kb_last || (WIN && q0 > kw0 + 31 + a.window)) return;
         const bool need_mask = (q0 < kw0 + 31) || (q0 + MQ - 1 > q_hi) || (WIN && q0 + MQ - 1 > kw0 + a.window) ||
@@ -293,9 +311,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
         const u16 *qr = (const u16 *)T.qr, *orr = (const u16 *)T.orow;
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(qr + (c * QCH + swz8(c, 2 * s + hh)) * 8), kf[s], sacc);
+        for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(qr + (c * QCH + swz384(c, 2 * s + hh)) * 8), kf[s], sacc);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(orr + (c * OCH + swz8(c, 2 * s + hh)) * 8), vf[s], dpacc);
+        for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(orr + (c * OCH + swz256(c, 2 * s + hh)) * 8), vf[s], dpacc);
         bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -323,34 +341,54 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
         for (int i = 0; i < 4; ++i) {
             const int d = 32 * i + c;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) dv[i] = mfma32(ld16(ot + (d * TCH + swz4(d, 2 * s + hh)) * 8), pb[s], dv[i]);
+            for (int s = 0; s < 2; ++s) dv[i] = mfma32(ld16(ot + (d * TCH + swz64(d, 2 * s + hh)) * 8), pb[s], dv[i]);
         }
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
             const int d = 32 * i + c;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) dk[i] = mfma32(ld16(qt + (d * TCH + swz4(d, 2 * s + hh)) * 8), sb[s], dk[i]);
+            for (int s = 0; s < 2; ++s) dk[i] = mfma32(ld16(qt + (d * TCH + swz64(d, 2 * s + hh)) * 8), sb[s], dk[i]);
         }
     };
 
-    // ---- double-buffered step loop (same load/wait/barrier pattern as the forward)
+    // ---- three-stage step loop: steps st+1 and st+2 are in flight while step st is computed.  Every step
+    // issues exactly one tile set (the last one again once the steps run out), so waiting for all but the
+    // newest set makes the current one land; the barrier after that wait also means every wave finished
+    // the previous step, whose buffer the new loads refill.
     issue(0, t0s);
-    for (int st = 0; st < nsteps; st += 2) {
-        issue(min(st + 1, nsteps - 1), t1s);
+    issue(min(1, nsteps - 1), t1s);
+    auto stage = [&](int st, const DkdvTile &cur, DkdvTile &nxt) {
         wait_vmcnt<DK_LOADS>();
         __builtin_amdgcn_s_barrier();
-        compute(st, t0s);
-        __builtin_amdgcn_s_barrier();
-        issue(min(st + 2, nsteps - 1), t0s);
-        wait_vmcnt<DK_LOADS>();
-        __builtin_amdgcn_s_barrier();
-        if (st + 1 < nsteps) compute(st + 1, t1s);
-        __builtin_amdgcn_s_barrier();
+        issue(min(st + 2, nsteps - 1), nxt);
+        if (st < nsteps) compute(st, cur);
+    };
+    for (int st = 0; st < nsteps; st += 3) {
+        stage(st, t0s, t2s);
+        stage(st + 1, t1s, t0s);
+        stage(st + 2, t2s, t1s);
     }
     wait_vmcnt<0>();
 
-    // ---- epilogue: dv = 0.707 * dV^T, dk = R^T dK^T / sqrt(192)
-    if (kvalid) {
+    // ---- epilogue: dv = 0.707 * dV^T, dk = R^T dK^T / sqrt(192); with several head splits, fp32 partials
+    // that bwd_dkv_reduce sums in split order
+    if (kvalid && A.splits > 1) {
+        const float2 *cs = a.rope + (size_t)min(kj - seq_start, a.rope_len - 1) * NHALF;
+        rope_back(dk[0], dk[1], cs, hh);
+        float *pp = A.dkv_part + (((size_t)split * A.T_pad + kj) * a.hkv + kvh) * (DQK + DVV) + 4 * hh;
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *(float4 *)(pp + 32 * i + 8 * jj) = make_float4(dk[i][4 * jj] * RSQRT_DQK, dk[i][4 * jj + 1] * RSQRT_DQK,
+                                                                dk[i][4 * jj + 2] * RSQRT_DQK, dk[i][4 * jj + 3] * RSQRT_DQK);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *(float4 *)(pp + DQK + 32 * i + 8 * jj) = make_float4(dv[i][4 * jj] * VSCALE, dv[i][4 * jj + 1] * VSCALE,
+                                                                      dv[i][4 * jj + 2] * VSCALE, dv[i][4 * jj + 3] * VSCALE);
+    } else if (kvalid) {
         u16 *dvp = A.dv + ((size_t)kj * a.hkv + kvh) * DVV + 4 * hh;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -376,6 +414,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
             }
         }
     }
+}
+
+// sum of the head-split partials, in split order (deterministic): one thread per 8 of the 320 values
+__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(const BwdArgs A)
+{
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const long rows = (long)A.L.T * A.L.hkv;
+    if (idx >= rows * 40) return;
+    const long row = idx / 40;
+    const int c8 = (int)(idx % 40);
+    const int t = (int)(row / A.L.hkv), kvh = (int)(row % A.L.hkv);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int sp = 0; sp < A.splits; ++sp) {
+        const float *pp = A.dkv_part + (((size_t)sp * A.T_pad + t) * A.L.hkv + kvh) * (DQK + DVV) + 8 * c8;
+        const float4 x0 = *(const float4 *)pp, x1 = *(const float4 *)(pp + 4);
+        acc[0] += x0.x; acc[1] += x0.y; acc[2] += x0.z; acc[3] += x0.w;
+        acc[4] += x1.x; acc[5] += x1.y; acc[6] += x1.z; acc[7] += x1.w;
+    }
+    bf16x8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = f2bf(acc[e]);
+    if (c8 < DQK / 8) st16(A.dk + ((size_t)t * A.L.hkv + kvh) * DQK + 8 * c8, w);
+    else st16(A.dv + ((size_t)t * A.L.hkv + kvh) * DVV + 8 * (c8 - DQK / 8), w);
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -433,22 +494,41 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
 
     const u16 *kr_g = A.W.kr + (size_t)kvh * DQK, *kt_g = A.W.krt + (size_t)kvh * DQK * A.T_pad;
     const size_t kr_row = (size_t)a.hkv * DQK, v_row = (size_t)a.hkv * DVV;
+    uint32_t o_kr[L_KR], o_kt[L_KT], o_vr[L_VR];
+#pragma unroll
+    for (int j = 0; j < L_KR; ++j) {
+        const int slot = NT * j + tid, r = slot / KCH, p = slot % KCH;
+        o_kr[j] = (uint32_t)((r * kr_row + 8 * swz384(r, p)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < L_KT; ++j) {
+        const int slot = NT * j + tid, d = slot / KTCH, p = slot % KTCH;
+        o_kt[j] = (uint32_t)(((size_t)d * A.T_pad + 8 * swz128(d, p)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < L_VR; ++j) {
+        const int slot = NT * j + tid, r = slot / VCH, p = slot % VCH;
+        o_vr[j] = (uint32_t)((r * v_row + 8 * swz256(r, p)) * 2);
+    }
     auto issue = [&](int k0, DqTile &T) {
+        const u16 *bk = kr_g + (size_t)k0 * kr_row;
+        const u16 *bkt = kt_g + k0;
+        const u16 *bv = a.v + ((size_t)k0 * a.hkv + kvh) * DVV;
 #pragma unroll
-        for (int j = 0; j < L_KR; ++j) {
-            const int slot = NT * j + tid, r = slot / KCH, p = slot % KCH;
-            lds_dma16(kr_g + (size_t)(k0 + r) * kr_row + 8 * swz8(r, p), T.kr + NT * j + 64 * wave);
-        }
+        for (int j = 0; j < L_KR; ++j) lds_dma16(bk, o_kr[j], T.kr + NT * j + 64 * wave);
 #pragma unroll
-        for (int j = 0; j < L_KT; ++j) {
-            const int slot = NT * j + tid, d = slot / KTCH, p = slot % KTCH;
-            lds_dma16(kt_g + (size_t)d * A.T_pad + k0 + 8 * swz8(d, p), T.kt + NT * j + 64 * wave);
-        }
+        for (int j = 0; j < L_KT; ++j) lds_dma16(bkt, o_kt[j], T.kt + NT * j + 64 * wave);
+        if (k0 + BN <= a.T) {
 #pragma unroll
-        for (int j = 0; j < L_VR; ++j) {
-            const int slot = NT * j + tid, r = slot / VCH, p = slot % VCH;
-            const int row = min(k0 + r, a.T - 1);     // v is not padded: rows past the end are masked
-            lds_dma16(a.v + (size_t)row * v_row + (size_t)kvh * DVV + 8 * swz8(r, p), T.vr + NT * j + 64 * wave);
+            for (int j = 0; j < L_VR; ++j) lds_dma16(bv, o_vr[j], T.vr + NT * j + 64 * wave);
+        } else {
+            // v is not padded: rows past its end are clamped to the last row (and masked)
+#pragma unroll
+            for (int j = 0; j < L_VR; ++j) {
+                const int slot = NT * j + tid, r = slot / VCH, p = slot % VCH;
+                const int row = min(k0 + r, a.T - 1);
+                lds_dma16(a.v + (size_t)row * v_row + (size_t)kvh * DVV + 8 * swz256(r, p), T.vr + NT * j + 64 * wave);
+            }
         }
     };
     issue(kstart, t0s);
@@ -489,9 +569,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
             const int rr = 32 * kb + c;
             f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-            for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(kr + (rr * KCH + swz8(rr, 2 * s + hh)) * 8), qf[s], sacc);
+            for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(kr + (rr * KCH + swz384(rr, 2 * s + hh)) * 8), qf[s], sacc);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(vr + (rr * VCH + swz8(rr, 2 * s + hh)) * 8), of[s], dpacc);
+            for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(vr + (rr * VCH + swz256(rr, 2 * s + hh)) * 8), of[s], dpacc);
             const bool need_mask = (kbase + 31 > wt0) || (kbase < seq_start) || (WIN && kbase < wt1 - a.window);
             bf16x8 sb[2];
 #pragma unroll
@@ -509,7 +589,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
                 const int d = 32 * i + c;
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    dq[i] = mfma32(ld16(kt + (d * KTCH + swz8(d, 4 * kb + 2 * s + hh)) * 8), sb[s], dq[i]);
+                    dq[i] = mfma32(ld16(kt + (d * KTCH + swz128(d, 4 * kb + 2 * s + hh)) * 8), sb[s], dq[i]);
             }
         }
     };
@@ -589,12 +669,23 @@ hipError_t launch_zero_f32(float *p, int n, hipStream_t stream)
 
 // workspace: lse2 and D [hq, T_pad] fp32, q' [T_pad, hq, 192], q'^T [hq, 192, T_pad], dO^T [hq, 128, T_pad],
 // k' [T_pad, hkv, 192], k'^T [hkv, 192, T_pad] (bf16), each 256-byte aligned
+// Causal layers with large groups split each key tile's query heads over several workgroups, so that the
+// first key tiles of a long sequence (which every later query sees) do not set the kernel's length alone.
+static int dkv_splits(int hq, int hkv, int window)
+{
+    const int G = hq / hkv;
+    if (window >= 0) return 1;
+    if (G % 4 == 0 && G >= 8) return 4;
+    if (G % 2 == 0 && G >= 4) return 2;
+    return 1;
+}
+
 size_t bwd_workspace_bytes(int T, int hq, int hkv, int window)
 {
-    (void)window;
     const size_t tp = (size_t)prep_tpad(T);
+    const int sp = dkv_splits(hq, hkv, window);
     return 2 * al(tp * hq * 4) + al(tp * hq * DQK * 2) + al(tp * hq * DQK * 2) + al(tp * hq * DVV * 2) +
-           al(tp * hkv * DQK * 2) + al(tp * hkv * DQK * 2);
+           al(tp * hkv * DQK * 2) + al(tp * hkv * DQK * 2) + (sp > 1 ? al((size_t)sp * tp * hkv * (DQK + DVV) * 4) : 0);
 }
 
 void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A)
@@ -615,6 +706,9 @@ void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A)
     A->W.kr = (u16 *)p;
     p += al(tp * hkv * DQK * 2);
     A->W.krt = (u16 *)p;
+    p += al(tp * hkv * DQK * 2);
+    A->splits = dkv_splits(hq, hkv, A->L.window);
+    A->dkv_part = A->splits > 1 ? (float *)p : nullptr;
 }
 
 hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
@@ -643,7 +737,7 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     if (e != hipSuccess) return e;
 
     const long kv_tiles = (long)(a.T + NKB - 1) / NKB + a.batch;
-    const long kv_grid = kv_tiles * a.hkv;
+    const long kv_grid = kv_tiles * a.hkv * A.splits;
     if (kv_grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     trace_begin(a.window >= 0 ? "bwd_dkdv_swa" : "bwd_dkdv_global", stream);
     if (a.window >= 0) bwd_dkdv_kernel<true><<<(unsigned)kv_grid, 256, 0, stream>>>(A);
@@ -651,6 +745,14 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     trace_end(stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (A.splits > 1) {
+        const long items = (long)a.T * a.hkv * 40;
+        trace_begin("bwd_dkv_reduce", stream);
+        bwd_dkv_reduce_kernel<<<(unsigned)((items + 255) / 256), 256, 0, stream>>>(A);
+        trace_end(stream);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int G = a.hq / a.hkv;
     if (G % 8 == 0) return launch_dq<8>(A, stream);
     if (G % 4 == 0) return launch_dq<4>(A, stream);

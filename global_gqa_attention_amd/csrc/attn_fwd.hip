@@ -38,11 +38,9 @@ constexpr int KCH = DQK / 8;   // 16-byte chunks per K row (24)
 constexpr int VCH = BN / 8;    // 16-byte chunks per V^T row (8)
 constexpr float RESCALE_TH = 8.f;         // keep a stale running max until the true one exceeds it by 2^8
 
-// K tile in LDS: row r (key), 24 chunks of 16 B; logical chunk q sits at position q ^ (r & 7) inside its
-// group of 8, so the 8 lanes of an MFMA operand read (8 consecutive rows, same logical chunk) hit 8
-// different bank groups.  V^T tile: row d (dim), 8 chunks, position q ^ (d & 7).
-__device__ __forceinline__ int kpos(int r, int q) { return (q & ~7) | ((q & 7) ^ (r & 7)); }
-__device__ __forceinline__ int vpos(int d, int q) { return q ^ (d & 7); }
+// K tile in LDS: row r (key), 24 chunks of 16 B (384-byte rows); V^T tile: row d (dim), 8 chunks.
+__device__ __forceinline__ int kpos(int r, int q) { return swz384(r, q); }
+__device__ __forceinline__ int vpos(int d, int q) { return swz128(d, q); }
 
 // NW waves per workgroup (32 query rows each) share one stream of K/V tiles: 8 for causal layers (half
 // the L2 -> LDS tile traffic), 4 for sliding-window layers (shorter key span per workgroup).
@@ -54,10 +52,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
     constexpr int KLOADS = BN * KCH / NT;      // global_load_lds per thread per K tile
     constexpr int VLOADS = DVV * VCH / NT;     // ... per V^T tile
     const LayerArgs &a = A.L;
+    constexpr int NBUF = NW == 8 ? 3 : 2;      // LDS stages (3 x 40 KB for one 8-wave workgroup per CU)
     __shared__ __attribute__((aligned(16))) uint4 sK0[BN * KCH];
     __shared__ __attribute__((aligned(16))) uint4 sV0[DVV * VCH];
     __shared__ __attribute__((aligned(16))) uint4 sK1[BN * KCH];
     __shared__ __attribute__((aligned(16))) uint4 sV1[DVV * VCH];
+    __shared__ __attribute__((aligned(16))) uint4 sK2[NBUF == 3 ? BN * KCH : 1];
+    __shared__ __attribute__((aligned(16))) uint4 sV2[NBUF == 3 ? DVV * VCH : 1];
 
     constexpr int TT = BM / GP;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -96,25 +97,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
     const int khi = t_last;
     const int nkt = (khi - kstart + BN) / BN;
 
-    // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = NT j + tid of each array)
+    // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = NT j + tid of each array): the
+    // per-lane byte offsets are fixed, the tile start is a wave-uniform base
     const u16 *kr_base = A.P.kr + (size_t)kvh * DQK;
     const size_t kr_row = (size_t)a.hkv * DQK;
     const u16 *vt_base = A.P.vt + (size_t)kvh * DVV * A.P.T_pad;
+    uint32_t koff[KLOADS], voff[VLOADS];
+#pragma unroll
+    for (int j = 0; j < KLOADS; ++j) {
+        const int slot = NT * j + tid, r = slot / KCH, p = slot % KCH;
+        koff[j] = (uint32_t)((r * kr_row + 8 * kpos(r, p)) * 2);    // kpos is an involution
+    }
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j) {
+        const int slot = NT * j + tid, d = slot / VCH, p = slot % VCH;
+        voff[j] = (uint32_t)(((size_t)d * A.P.T_pad + 8 * vpos(d, p)) * 2);
+    }
     auto issue_tile = [&](int k0, uint4 *sk, uint4 *sv) {
+        const u16 *kb = kr_base + (size_t)k0 * kr_row;
+        const u16 *vb = vt_base + k0;
 #pragma unroll
-        for (int j = 0; j < KLOADS; ++j) {
-            const int slot = NT * j + tid;
-            const int r = slot / KCH, p = slot % KCH;
-            const u16 *src = kr_base + (size_t)(k0 + r) * kr_row + 8 * kpos(r, p);   // kpos is an involution
-            lds_dma16(src, sk + NT * j + 64 * wave);
-        }
+        for (int j = 0; j < KLOADS; ++j) lds_dma16(kb, koff[j], sk + NT * j + 64 * wave);
 #pragma unroll
-        for (int j = 0; j < VLOADS; ++j) {
-            const int slot = NT * j + tid;
-            const int d = slot / VCH, p = slot % VCH;
-            const u16 *src = vt_base + (size_t)d * A.P.T_pad + k0 + 8 * vpos(d, p);
-            lds_dma16(src, sv + NT * j + 64 * wave);
-        }
+        for (int j = 0; j < VLOADS; ++j) lds_dma16(vb, voff[j], sv + NT * j + 64 * wave);
     };
     issue_tile(kstart, sK0, sV0);
 
@@ -215,25 +220,46 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
         }
     };
 
-    // ---- double-buffered loop, unrolled by two so each half names its own buffers.  Every half issues
-    // exactly one tile (the last valid tile again once the range is exhausted), so the number of loads in
-    // flight is the same on every path: the wait for a buffer is always "all but the 10 newest loads".  The
-    // LDS tiles are written only by these direct loads, so a plain s_barrier suffices: each wave waits
-    // (vmcnt) for its own loads of the tile it reads next, and reaches the following barrier only after
-    // its MFMAs consumed every LDS read of the buffer that is refilled next.
     const int klast = kstart + (nkt - 1) * BN;
-    for (int it = 0; it < nkt; it += 2) {
-        const int k0 = kstart + it * BN;
-        issue_tile(min(k0 + BN, klast), sK1, sV1);
-        wait_vmcnt<KLOADS + VLOADS>();
-        __builtin_amdgcn_s_barrier();       // tile it is in buffer 0 for every wave
-        compute_tile(k0, sK0, sV0);
-        __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 0
-        issue_tile(min(k0 + 2 * BN, klast), sK0, sV0);
-        wait_vmcnt<KLOADS + VLOADS>();
-        __builtin_amdgcn_s_barrier();       // tile it+1 is in buffer 1 for every wave
-        if (it + 1 < nkt) compute_tile(k0 + BN, sK1, sV1);
-        __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 1
+    if constexpr (NBUF == 3) {
+        // ---- three-stage ring, unrolled by three so each step names its buffers.  Every step issues
+        // exactly one tile (the last valid tile again once the range is exhausted), so the loads in flight
+        // are always the current tile and the next one: waiting for all but the newest tile's loads makes
+        // the current tile land.  The barrier after that wait also tells this wave that every wave has
+        // finished the previous step, whose buffer the new loads then refill.  The LDS tiles are written
+        // only by these direct loads, so a plain s_barrier suffices.
+        issue_tile(min(kstart + BN, klast), sK1, sV1);
+        auto step = [&](int it, const uint4 *ck, const uint4 *cv, uint4 *nk, uint4 *nv) {
+            wait_vmcnt<KLOADS + VLOADS>();
+            __builtin_amdgcn_s_barrier();
+            issue_tile(min(kstart + (it + 2) * BN, klast), nk, nv);
+            if (it < nkt) compute_tile(kstart + it * BN, ck, cv);
+        };
+        for (int it = 0; it < nkt; it += 3) {
+            step(it, sK0, sV0, sK2, sV2);
+            step(it + 1, sK1, sV1, sK0, sV0);
+            step(it + 2, sK2, sV2, sK1, sV1);
+        }
+    } else {
+        // ---- double-buffered loop, unrolled by two so each half names its own buffers.  Every half
+        // issues exactly one tile (the last valid tile again once the range is exhausted), so the number
+        // of loads in flight is the same on every path: the wait for a buffer is always "all but the
+        // newest tile's loads".  Each wave waits (vmcnt) for its own loads of the tile it reads next, and
+        // reaches the following barrier only after its MFMAs consumed every LDS read of the buffer that
+        // is refilled next.
+        for (int it = 0; it < nkt; it += 2) {
+            const int k0 = kstart + it * BN;
+            issue_tile(min(k0 + BN, klast), sK1, sV1);
+            wait_vmcnt<KLOADS + VLOADS>();
+            __builtin_amdgcn_s_barrier();       // tile it is in buffer 0 for every wave
+            compute_tile(k0, sK0, sV0);
+            __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 0
+            issue_tile(min(k0 + 2 * BN, klast), sK0, sV0);
+            wait_vmcnt<KLOADS + VLOADS>();
+            __builtin_amdgcn_s_barrier();       // tile it+1 is in buffer 1 for every wave
+            if (it + 1 < nkt) compute_tile(k0 + BN, sK1, sV1);
+            __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 1
+        }
     }
     wait_vmcnt<0>();                        // no load may still target this workgroup's LDS at exit
 

@@ -66,12 +66,33 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, void *lds_wave_base)
                  : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base address plus a per-lane byte offset (saddr form: the per-lane
+// part needs no 64-bit address arithmetic).
+__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, void *lds_wave_base)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector-memory loads are still in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// LDS swizzles for tiles filled by lds_dma16: the position of logical 16-byte chunk q in row r of a tile
+// whose rows are 384, 256, 128 or 64 bytes long.  gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a
+// time from 64 banks; an MFMA operand read has 16 consecutive lanes on 16 consecutive rows at one logical
+// chunk, and each mapping sends those 16 reads to 16 different 16-byte bank groups.  Each is an
+// involution, so it also maps a position back to its logical chunk.
+__device__ __forceinline__ int swz384(int r, int q) { return (q & ~7) | ((q & 7) ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ int swz256(int r, int q) { return q ^ (r & 15); }
+__device__ __forceinline__ int swz128(int r, int q) { return q ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz64(int r, int q) { return q ^ ((r >> 2) & 3); }
 
 // Rotate-half RoPE of one 8-wide chunk pair: x0 holds dims d..d+7 (d < 32), x1 dims d+32..d+39, cs the
 // (cos, sin) of the 8 matching frequencies.  Rounded back to bf16 (the MFMA operand precision).

@@ -50,7 +50,9 @@ struct BwdArgs {
     float *dsink;                  // [hq] or nullptr
     float *delta;                  // workspace: D = rowsum(dO * O) [hq,T_pad]
     float *lse2;                   // workspace: LSE * log2(e) [hq,T_pad]
+    float *dkv_part;               // workspace: fp32 dk|dv partials [splits, T_pad, hkv, 320] (splits > 1)
     int T_pad;
+    int splits;                    // query heads of a group are split over this many key-tile workgroups
 };
 void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A);
 
