@@ -9,6 +9,13 @@ The decode step (batch 64, SWA ring of 128 + sink; global cache lengths in [8192
 same run and reported as GB/s of cache traffic under "decode"; it is not part of the step's value.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+HBM traffic of the kernels (the roofline's "traffic") is taken with two rocprofv3 counter passes over
+`--traffic-probe` (one warm step plus a plain 1 GiB copy that calibrates the counters), then summarised:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o p -- python3 bench.py --traffic-probe D1
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o p -- python3 bench.py --traffic-probe D2
+    python bench.py --traffic-summary D1 D2      # writes profiles/traffic.json
 """
 from __future__ import annotations
 
@@ -67,9 +74,8 @@ def measured_traffic(kernel):
 
 
 def cpu_baseline(thd, dout, nthreads):
-    """The fp64 oracle on a bounded sample of the same workload: the first two sequences of the batch for the
-    sliding-window layer and the first 1024 tokens of the first sequence for the global layer, forward and
-    backward, all 64 heads."""
+    """The fp64 oracle on a bounded sample of the same workload (about 25 s on 16 host threads): the first two
+    sequences of the batch for both layers, forward and backward, all 64 heads."""
     import torch
 
     import mimo_inputs as mi
@@ -78,7 +84,7 @@ def cpu_baseline(thd, dout, nthreads):
     flops, secs, parts = 0.0, 0.0, []
     for name, d, n_tok, lens in (
         ("swa", thd["swa"], sum(thd["swa"]["lengths"][:2]), thd["swa"]["lengths"][:2]),
-        ("glb", thd["glb"], 1024, [1024]),
+        ("glb", thd["glb"], sum(thd["glb"]["lengths"][:2]), thd["glb"]["lengths"][:2]),
     ):
         q, k, v = d["q"][:n_tok], d["k"][:n_tok], d["v"][:n_tok]
         cu = mi.cu_from_lengths(lens)
@@ -134,31 +140,9 @@ def run_decode(ga, torch, mi, reps=20):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs the attention layer on a single MI355X and "
-              f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import global_gqa_attention_amd as ga
-    import mimo_inputs as mi
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
+def setup_layers(ga, torch, mi, dev):
+    """The 32768-token THD batch of both layers, resident on `dev`, with outputs, gradients and workspaces
+    allocated; returns (thd on the host, dO on the host, layers, step)."""
     thd = mi.thd_32k()
     dout_cpu = mi.dout_like(32768, 4)
     layers = {}
@@ -182,6 +166,166 @@ def main():
                    out=g["out"], lse=g["lse"])
             ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], dout, g["cu_seqlens"], g["max_seqlen"],
                    g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"])
+
+    return thd, dout_cpu, layers, step
+
+
+# trace name prefix -> kernel function name (checks that traced launches and counted dispatches line up)
+TRACE_TO_KERNEL = (("kv_prep", "kv_prep_kernel"), ("attn_fwd", "attn_fwd_kernel"), ("bwd_prep", "row_prep_kernel"),
+                   ("bwd_pre", "bwd_pre_kernel"), ("bwd_dsink", "bwd_dsink_kernel"),
+                   ("bwd_dkdv", "bwd_dkdv_kernel"), ("bwd_dkv_reduce", "bwd_dkv_reduce_kernel"),
+                   ("bwd_dq", "bwd_dq_kernel"), ("decode_split", "decode_split_kernel"),
+                   ("decode_combine", "decode_combine_kernel"))
+COPY_BYTES = 1 << 30    # the calibration copy: 1 GiB read, 1 GiB written
+
+
+def traffic_probe(outdir):
+    """One warm step of the hot path and a plain device copy of COPY_BYTES, for rocprofv3 counter passes; the
+    library kernels' launch order of the step is written to <outdir>/traffic_order.json."""
+    import torch
+
+    import global_gqa_attention_amd as ga
+    import mimo_inputs as mi
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    _, _, layers, step = setup_layers(ga, torch, mi, dev)
+    step()
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    ga.trace_read(clear=True)
+    ga.trace_enable(True)
+    step()
+    torch.cuda.synchronize()
+    ga.trace_enable(False)
+    names = [n for n, _ in ga.trace_read(clear=True)]
+    os.makedirs(outdir, exist_ok=True)
+    with open(os.path.join(outdir, "traffic_order.json"), "w") as f:
+        json.dump({"launches": names}, f)
+    print(f"traffic probe: {len(names)} library launches in the step", flush=True)
+
+
+def _counter_rows(d, counter):
+    """(kernel name, value) per dispatch, in dispatch order, from a rocprofv3 counter_collection.csv."""
+    import csv
+
+    path = None
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                path = os.path.join(root, f)
+    if path is None:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        name, val = rows.get(key, (r["Kernel_Name"], 0.0))
+        rows[key] = (name, val + float(r["Counter_Value"]))
+    return [rows[k] for k in sorted(rows)]
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """Writes profiles/traffic.json: per library kernel of the step, HBM bytes per launch read and written,
+    each counter (KiB per dispatch) scaled by what it reads for the COPY_BYTES copy."""
+    order = json.load(open(os.path.join(fetch_dir, "traffic_order.json")))["launches"]
+    out = {"source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+           "commands": [f"cd /tmp && rocprofv3 --pmc {c} --output-format csv -d $REPO/{d} -o p -- python3 "
+                        f"$REPO/bench.py --traffic-probe $REPO/{d}"
+                        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))]
+           + [f"python bench.py --traffic-summary {fetch_dir} {write_dir}"],
+           "note": "bytes = counter (KiB per dispatch) x 1024 x scale; scale = copy_bytes / the counter's reading "
+                   "for a plain device copy of copy_bytes in the same run", "kernels": {}}
+    per = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        copies = [v for n, v in rows if "copy" in n.lower()]
+        if not copies:
+            raise SystemExit(f"{counter}: no copy dispatch found")
+        scale = COPY_BYTES / (max(copies) * 1024.0)
+        out[f"{counter.lower()}_scale"] = round(scale, 5)
+        if not 0.25 < scale < 4.0:
+            raise SystemExit(f"{counter}: implausible copy calibration {scale}")
+        lib = [(n, v) for n, v in rows if "mimo::" in n]
+        if len(lib) < len(order):
+            raise SystemExit(f"{counter}: {len(lib)} library dispatches, expected at least {len(order)}")
+        for name, (kname, v) in zip(order, lib[-len(order):]):
+            want = next(k for p, k in TRACE_TO_KERNEL if name.startswith(p))
+            if want not in kname:
+                raise SystemExit(f"{counter}: launch {name} lines up with dispatch {kname}")
+            per.setdefault(name, {}).setdefault(counter, []).append(v * 1024.0 * scale)
+    for name, rec in per.items():
+        fb = sum(rec["FETCH_SIZE"]) / len(rec["FETCH_SIZE"])
+        wb = sum(rec["WRITE_SIZE"]) / len(rec["WRITE_SIZE"])
+        out["kernels"][name] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {path}")
+
+
+def stats_summary(csv_path, title, command):
+    """Prints a rocprofv3 kernel_stats.csv as a short text table (kernel, calls, average/min/max us, share)."""
+    import csv
+    import re
+
+    def short(n):
+        m = re.search(r"mimo::\(anonymous namespace\)::(\w+)(<[^>(]*>)?", n)
+        return m.group(1) + (m.group(2) or "") if m else n.split("(")[0][-70:]
+
+    print(f"# {title}\n# command: {command}\n# source: rocprofv3 --kernel-trace --stats (kernel_stats.csv)\n")
+    print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in csv.DictReader(open(csv_path)):
+        print(f"{short(r['Name'])[:64]:64s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.1f} "
+              f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--traffic-probe", metavar="DIR", help="run the counter-pass workload (see the module doc)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two counter passes")
+    ap.add_argument("--stats-summary", nargs=3, metavar=("CSV", "TITLE", "COMMAND"),
+                    help="print a rocprofv3 kernel_stats.csv as a text table")
+    args = ap.parse_args()
+    if args.stats_summary:
+        stats_summary(*args.stats_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.traffic_probe:
+        traffic_probe(args.traffic_probe)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs the attention layer on a single MI355X and "
+              f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import global_gqa_attention_amd as ga
+    import mimo_inputs as mi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    thd, dout_cpu, layers, step = setup_layers(ga, torch, mi, dev)
 
     for _ in range(args.warmup):
         step()
@@ -226,15 +370,13 @@ def main():
 
     layer_tflops = {}
     for lname, g in layers.items():
-        suf = "swa" if lname == "swa" else "global"
-        fwd_ms = kernels.get(f"attn_fwd_{suf}", {}).get("avg_ms")
-        bwd_ms = sum(kernels.get(f"{k}_{suf}", {}).get("avg_ms", 0.0) for k in ("bwd_dkdv", "bwd_dq"))
-        bwd_ms += (kernels.get("bwd_pre", {}).get("avg_ms", 0.0) + kernels.get("bwd_dsink", {}).get("avg_ms", 0.0)
-                   * (1 if lname == "swa" else 0))
+        suf = "_swa" if lname == "swa" else "_global"
+        mine = {k[: -len(suf)]: v for k, v in kernels.items() if k.endswith(suf)}
+        fwd_ms = sum(v["avg_ms"] for k, v in mine.items() if k in ("kv_prep", "attn_fwd"))
+        bwd_ms = sum(v["avg_ms"] for k, v in mine.items() if k.startswith("bwd_"))
         layer_tflops[lname] = {
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_TFLOP/s": round(g["pairs"] * FWD_FLOP_PER_PAIR / (fwd_ms * 1e-3) / 1e12, 1) if fwd_ms else None,
-            "fwd_frac": round(g["pairs"] * FWD_FLOP_PER_PAIR / (fwd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-            if fwd_ms else None,
             "bwd_TFLOP/s": round(g["pairs"] * BWD_FLOP_PER_PAIR / (bwd_ms * 1e-3) / 1e12, 1) if bwd_ms else None,
             "pairs": g["pairs"]}
 

@@ -717,22 +717,28 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     const long rows = (long)A.T_pad * a.hq;
     const long pre_blocks = (rows + 63) / 64;
     if (pre_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    trace_begin("bwd_pre", stream);
+    trace_begin(a.window >= 0 ? "bwd_pre_swa" : "bwd_pre_global", stream);
     bwd_pre_kernel<<<(unsigned)pre_blocks, 256, 0, stream>>>(A);
     trace_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (A.dsink) {
-        trace_begin("bwd_dsink", stream);
+        trace_begin(a.window >= 0 ? "bwd_dsink_swa" : "bwd_dsink_global", stream);
         bwd_dsink_kernel<<<a.hq, 256, 0, stream>>>(A);
         trace_end(stream);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    trace_begin("bwd_prep", stream);
+    trace_begin(a.window >= 0 ? "bwd_prep_q_swa" : "bwd_prep_q_global", stream);
     e = launch_row_prep<DQK, true>(a.q, a.hq, A.W.qr, A.W.qrt, a, A.T_pad, stream);
-    if (e == hipSuccess) e = launch_row_prep<DVV, false>(A.dout, a.hq, nullptr, A.W.dot, a, A.T_pad, stream);
-    if (e == hipSuccess) e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.W.krt, a, A.T_pad, stream);
+    trace_end(stream);
+    if (e != hipSuccess) return e;
+    trace_begin(a.window >= 0 ? "bwd_prep_dout_swa" : "bwd_prep_dout_global", stream);
+    e = launch_row_prep<DVV, false>(A.dout, a.hq, nullptr, A.W.dot, a, A.T_pad, stream);
+    trace_end(stream);
+    if (e != hipSuccess) return e;
+    trace_begin(a.window >= 0 ? "bwd_prep_k_swa" : "bwd_prep_k_global", stream);
+    e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.W.krt, a, A.T_pad, stream);
     trace_end(stream);
     if (e != hipSuccess) return e;
 
@@ -747,7 +753,7 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     if (e != hipSuccess) return e;
     if (A.splits > 1) {
         const long items = (long)a.T * a.hkv * 40;
-        trace_begin("bwd_dkv_reduce", stream);
+        trace_begin(a.window >= 0 ? "bwd_dkv_reduce_swa" : "bwd_dkv_reduce_global", stream);
         bwd_dkv_reduce_kernel<<<(unsigned)((items + 255) / 256), 256, 0, stream>>>(A);
         trace_end(stream);
         e = hipGetLastError();

@@ -116,7 +116,7 @@ void prep_carve(void *ws, int T, int hkv, KVPrep *p)
 hipError_t launch_kv_prep(const LayerArgs &a, const KVPrep &p, hipStream_t stream)
 {
     dim3 grid((p.T_pad + PT - 1) / PT, a.hkv);
-    trace_begin("kv_prep", stream);
+    trace_begin(a.window >= 0 ? "kv_prep_swa" : "kv_prep_global", stream);
     kv_prep_kernel<<<grid, 256, 0, stream>>>(a, p);
     trace_end(stream);
     return hipGetLastError();

@@ -1,0 +1,71 @@
+"""Host-side logic of bench.py (no GPU): the attended-pair count behind every FLOP figure, and the counter
+summary that turns rocprofv3 FETCH_SIZE / WRITE_SIZE readings into bytes per launch."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+
+
+def brute_pairs(L, window):
+    return sum(1 for i in range(L) for j in range(i + 1) if window < 0 or i - j <= window)
+
+
+@pytest.mark.parametrize("L", [0, 1, 5, 128, 129, 130, 300])
+@pytest.mark.parametrize("window", [-1, 0, 3, 128])
+def test_pairs_per_head_matches_enumeration(L, window):
+    assert bench.pairs_per_head([L], window) == brute_pairs(L, window)
+
+
+def test_pairs_per_head_sums_sequences():
+    assert bench.pairs_per_head([7, 0, 300], 128) == brute_pairs(7, 128) + brute_pairs(300, 128)
+
+
+def _write_counters(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "p_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, val) in enumerate(rows):
+            # two rows per dispatch (as for a counter summed over several instances)
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val / 2})
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val / 2})
+
+
+def test_traffic_summary_scales_by_copy(tmp_path, monkeypatch):
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    k = "void mimo::(anonymous namespace)::"
+    gib_kib = bench.COPY_BYTES / 1024
+    step = [(k + "kv_prep_kernel(...)", 100.0), (k + "attn_fwd_kernel<4, 8, true, true>(...)", 400.0)]
+    # warm step, fill + copy, traced step
+    _write_counters(fetch, "FETCH_SIZE", step + [("fill", 0.0), ("__amd_rocclr_copyBuffer", gib_kib / 2)] + step)
+    _write_counters(write, "WRITE_SIZE", step + [("fill", gib_kib), ("__amd_rocclr_copyBuffer", gib_kib)] + step)
+    with open(os.path.join(fetch, "traffic_order.json"), "w") as f:
+        json.dump({"launches": ["kv_prep_swa", "attn_fwd_swa"]}, f)
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h")
+    bench.traffic_summary(fetch, write)
+    out = json.load(open(tmp_path / "profiles" / "traffic.json"))
+    assert out["fetch_size_scale"] == 2.0 and out["write_size_scale"] == 1.0
+    assert out["kernels"]["attn_fwd_swa"] == {"fetch_bytes": 400 * 1024 * 2, "write_bytes": 400 * 1024,
+                                              "bytes_per_launch": 400 * 1024 * 3}
+    assert bench.measured_traffic("attn_fwd_swa") == 400 * 1024 * 3
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
+    assert bench.measured_traffic("attn_fwd_swa") is None
+
+
+def test_traffic_summary_rejects_misaligned_launches(tmp_path, monkeypatch):
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    k = "void mimo::(anonymous namespace)::"
+    rows = [("__amd_rocclr_copyBuffer", bench.COPY_BYTES / 1024), (k + "bwd_dq_kernel<4, 8, false>(...)", 1.0)]
+    _write_counters(fetch, "FETCH_SIZE", rows)
+    _write_counters(write, "WRITE_SIZE", rows)
+    with open(os.path.join(fetch, "traffic_order.json"), "w") as f:
+        json.dump({"launches": ["bwd_dkdv_global"]}, f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h")
+    with pytest.raises(SystemExit):
+        bench.traffic_summary(fetch, write)
