@@ -26,6 +26,8 @@
 //   5. bwd_dq:    query-major, shaped like the forward: S^T = K'Q'^T, P^T, dP^T = V dO^T, dS^T, then
 //                 dQ^T += K'^T dS^T with k' (both layouts) and v streamed HBM -> LDS.
 // dq and dk leave through the transposed rotation in their epilogues.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -179,6 +181,7 @@ constexpr int DK_QT = DQK * TCH / 256;   // q'^T (3)
 constexpr int DK_OR = MQ * OCH / 256;    // dO rows (2)
 constexpr int DK_OT = DVV * TCH / 256;   // dO^T (2)
 constexpr int DK_LOADS = DK_QR + DK_QT + DK_OR + DK_OT + 1;   // + LSE/D (one per wave)
+constexpr int DK_AHEAD = 4;              // LDS operand reads in flight ahead of the MFMAs
 
 struct DkdvTile {
     uint4 qr[MQ * QCH], qt[DQK * TCH], orow[MQ * OCH], ot[DVV * TCH];
@@ -302,19 +305,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
 
-    auto compute = [&](int step, const DkdvTile &T) {
+    // ---- one step = S, dP (MFMA) -> P, dS (VALU) -> dV, dK (MFMA).  Steps are software-pipelined: the S/dP
+    // products of step st+1 are issued between the softmax instructions of step st, so the MFMA pipe works
+    // while the VALU does; then the dV/dK products of step st follow.
+    //
+    // Which queries of a step does this wave need?  None (skip), all (no mask), or some (mask).
+    auto visible = [&](int step) {
         const int q0 = step_q0(step);
-        // does any query of this step see any key of this wave?
-        if (q0 + MQ - 1 < kw0 || kw0 > kb_last || (WIN && q0 > kw0 + 31 + a.window)) return;
-        const bool need_mask = (q0 < kw0 + 31) || (q0 + MQ - 1 > q_hi) || (WIN && q0 + MQ - 1 > kw0 + a.window) ||
-                               (kw0 + 31 > kb_last);
+        return step < nsteps && !(q0 + MQ - 1 < kw0 || kw0 > kb_last || (WIN && q0 > kw0 + 31 + a.window));
+    };
+    auto masked = [&](int step) {
+        const int q0 = step_q0(step);
+        return q0 < kw0 + 31 || q0 + MQ - 1 > q_hi || (WIN && q0 + MQ - 1 - kw0 > a.window);
+    };
+    // mask bound: query qi sees this lane's key iff 0 <= qi - kj <= ub.  Lanes past the tile's last key are
+    // never written back, so their values do not matter.  An invisible step is masked, so computing it
+    // anyway adds exact zeros.
+    const int ub = WIN ? min(a.window, q_hi - kj) : q_hi - kj;
+
+    auto sdp = [&](const DkdvTile &T, f32x16 &sacc, f32x16 &dpacc) {
         const u16 *qr = (const u16 *)T.qr, *orr = (const u16 *)T.orow;
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        sacc = f32x16{};
+        dpacc = f32x16{};
 #pragma unroll
         for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(qr + (c * QCH + swz384(c, 2 * s + hh)) * 8), kf[s], sacc);
 #pragma unroll
         for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(orr + (c * OCH + swz256(c, 2 * s + hh)) * 8), vf[s], dpacc);
-        bf16x8 pb[2], sb[2];
+    };
+    // P and dS of one step (uba = the mask bound, or all-ones for a step that needs no mask)
+    auto softmax = [&](int step, const DkdvTile &T, const f32x16 &sacc, const f32x16 &dpacc, uint32_t uba,
+                       bf16x8 *pb, bf16x8 *sb) {
+        const int base = step_q0(step) - kj;   // qi - kj of this lane's first row
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int ql = 8 * jj + 4 * hh;
@@ -326,16 +347,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
             for (int t = 0; t < 4; ++t) {
                 const int j = 4 * jj + t;
                 float p = fast_exp2(sacc[j] * a.scale_log2 - Lv[t]);
-                if (need_mask) {
-                    const int qi = q0 + ql + t;
-                    const bool ok = kvalid && qi >= kj && qi <= q_hi && (!WIN || qi - kj <= a.window);
-                    p = ok ? p : 0.f;
-                }
+                p = (uint32_t)(base + ql + t) <= uba ? p : 0.f;
                 pb[j >> 3][j & 7] = f2bf(p);
                 sb[j >> 3][j & 7] = f2bf(p * (VSCALE * dpacc[j] - Dv[t]));
             }
         }
-        // dV^T += dO^T P,  dK^T += Q'^T dS  (two 16-query k-steps)
+    };
+    // dV^T += dO^T P,  dK^T += Q'^T dS  (two 16-query k-steps)
+    auto dkdv_mm = [&](const DkdvTile &T, const bf16x8 *pb, const bf16x8 *sb) {
         const u16 *ot = (const u16 *)T.ot, *qt = (const u16 *)T.qt;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -351,22 +370,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
         }
     };
 
-    // ---- three-stage step loop: steps st+1 and st+2 are in flight while step st is computed.  Every step
-    // issues exactly one tile set (the last one again once the steps run out), so waiting for all but the
-    // newest set makes the current one land; the barrier after that wait also means every wave finished
-    // the previous step, whose buffer the new loads refill.
+    // ---- three-stage tile ring.  At stage st the tiles of steps st and st+1 are read and step st+2 is
+    // loaded: wait for all of this wave's loads (step st+1's tiles, issued one stage earlier), barrier (every
+    // wave has landed its part and has finished stage st-1, whose buffer the new loads refill), issue.  Every
+    // stage issues one tile set (the last step's again once the steps run out), so the waits stay uniform.
+    // The compute of a stage is the softmax of step st (its S/dP in s0/d0) with the S/dP of step st+1 (into
+    // s1/d1) interleaved, then dV/dK of step st: one basic block, so the scheduler can mix the two chains
+    // and keep the MFMA pipe busy while the VALU works; the group barriers ask for one MFMA, one LDS read and
+    // a run of VALU work in turn.
+    f32x16 sA = f32x16{}, dA = f32x16{}, sB = f32x16{}, dB = f32x16{};
     issue(0, t0s);
     issue(min(1, nsteps - 1), t1s);
-    auto stage = [&](int st, const DkdvTile &cur, DkdvTile &nxt) {
-        wait_vmcnt<DK_LOADS>();
+    wait_vmcnt<DK_LOADS>();
+    __builtin_amdgcn_s_barrier();
+    sdp(t0s, sA, dA);
+    auto stage = [&](int st, const DkdvTile &cur, const DkdvTile &nxt, DkdvTile &fill, const f32x16 &s0,
+                     const f32x16 &d0, f32x16 &s1, f32x16 &d1) {
+        wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(min(st + 2, nsteps - 1), nxt);
-        if (st < nsteps) compute(st, cur);
+        issue(min(st + 2, nsteps - 1), fill);
+        if (visible(st) || visible(st + 1)) {
+            const uint32_t uba = masked(st) ? (uint32_t)ub : 0xffffffffu;
+            bf16x8 pb[2], sb[2];
+            softmax(st, cur, s0, d0, uba, pb, sb);
+            sdp(nxt, s1, d1);
+            dkdv_mm(cur, pb, sb);
+            // LDS operand reads run DK_AHEAD reads ahead of the MFMAs that consume them
+            __builtin_amdgcn_sched_group_barrier(0x100, 8 + DK_AHEAD, 0);   // LSE/D rows + first operands
+#pragma unroll
+            for (int i = 0; i < 20; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA (S, dP of step st+1)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);          // VALU (softmax of step st)
+            }
+#pragma unroll
+            for (int i = 0; i < 20; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA (dV, dK of step st)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);          // VALU
+            }
+        }
     };
-    for (int st = 0; st < nsteps; st += 3) {
-        stage(st, t0s, t2s);
-        stage(st + 1, t1s, t0s);
-        stage(st + 2, t2s, t1s);
+    // unrolled by six: the tile ring has period three and the S/dP register pair period two
+    for (int st = 0; st < nsteps; st += 6) {
+        stage(st, t0s, t1s, t2s, sA, dA, sB, dB);
+        if (st + 1 >= nsteps) break;
+        stage(st + 1, t1s, t2s, t0s, sB, dB, sA, dA);
+        if (st + 2 >= nsteps) break;
+        stage(st + 2, t2s, t0s, t1s, sA, dA, sB, dB);
+        if (st + 3 >= nsteps) break;
+        stage(st + 3, t0s, t1s, t2s, sB, dB, sA, dA);
+        if (st + 4 >= nsteps) break;
+        stage(st + 4, t1s, t2s, t0s, sA, dA, sB, dB);
+        if (st + 5 >= nsteps) break;
+        stage(st + 5, t2s, t0s, t1s, sB, dB, sA, dA);
     }
     wait_vmcnt<0>();
 
