@@ -499,10 +499,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(const BwdArgs A)
 // ------------------------------------------------------------------------------------------------------
 // 5. dQ (query-major)
 // ------------------------------------------------------------------------------------------------------
-constexpr int BN = 64;                   // keys per tile
+constexpr int BN = 32;                   // keys per tile (one step)
 constexpr int KCH = DQK / 8;             // 24 chunks per k' row
 constexpr int VCH = DVV / 8;             // 16 chunks per v row
-constexpr int KTCH = BN / 8;             // 8 chunks per k'^T row
+constexpr int KTCH = BN / 8;             // 4 chunks per k'^T row
+constexpr int DQ_AHEAD = 4;              // LDS operand reads in flight ahead of the MFMAs
 
 struct DqTile {
     uint4 kr[BN * KCH], kt[DQK * KTCH], vr[BN * VCH];
@@ -514,8 +515,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
     const LayerArgs &a = A.L;
     constexpr int NT = 64 * NW, BM = 32 * NW, TT = BM / GP;
     constexpr int L_KR = BN * KCH / NT, L_KT = DQK * KTCH / NT, L_VR = BN * VCH / NT;
-    constexpr int DQ_LOADS = L_KR + L_KT + L_VR;
-    __shared__ __attribute__((aligned(16))) DqTile t0s, t1s;
+    static_assert(L_KR * NT == BN * KCH && L_KT * NT == DQK * KTCH && L_VR * NT == BN * VCH, "tile split");
+    __shared__ __attribute__((aligned(16))) DqTile t0s, t1s, t2s;   // three-stage ring (96 KB)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -547,7 +548,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
     const int klo = WIN ? max(seq_start, t0 - a.window) : seq_start;
     const int kstart = klo & ~15;
     const int khi = t_last;
-    const int nkt = (khi - kstart + BN) / BN;
+    const int nsteps = (khi - kstart + BN) / BN;
 
     const u16 *kr_g = A.W.kr + (size_t)kvh * DQK, *kt_g = A.W.krt + (size_t)kvh * DQK * A.T_pad;
     const size_t kr_row = (size_t)a.hkv * DQK, v_row = (size_t)a.hkv * DVV;
@@ -560,14 +561,15 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
 #pragma unroll
     for (int j = 0; j < L_KT; ++j) {
         const int slot = NT * j + tid, d = slot / KTCH, p = slot % KTCH;
-        o_kt[j] = (uint32_t)(((size_t)d * A.T_pad + 8 * swz128(d, p)) * 2);
+        o_kt[j] = (uint32_t)(((size_t)d * A.T_pad + 8 * swz64(d, p)) * 2);
     }
 #pragma unroll
     for (int j = 0; j < L_VR; ++j) {
         const int slot = NT * j + tid, r = slot / VCH, p = slot % VCH;
         o_vr[j] = (uint32_t)((r * v_row + 8 * swz256(r, p)) * 2);
     }
-    auto issue = [&](int k0, DqTile &T) {
+    auto issue = [&](int step, DqTile &T) {
+        const int k0 = kstart + step * BN;
         const u16 *bk = kr_g + (size_t)k0 * kr_row;
         const u16 *bkt = kt_g + k0;
         const u16 *bv = a.v + ((size_t)k0 * a.hkv + kvh) * DVV;
@@ -588,8 +590,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
             }
         }
     };
-    issue(kstart, t0s);
+    issue(0, t0s);
+    issue(min(1, nsteps - 1), t1s);
 
+    // ---- this lane's query row: rotated q and dO as B operands, its LSE and D
     const int r = wave * 32 + c;
     const int qt = t0 + r / GP;
     const int qh = h0 + r % GP;
@@ -608,62 +612,103 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
     const float Lq = A.lse2[(size_t)qh * A.T_pad + qtl];
     const float Dq = A.delta[(size_t)qh * A.T_pad + qtl];
 
+    // this wave's token span and the keys it sees
     const int wt0 = t0 + (wave * 32) / GP;
     const int wt1 = min(t0 + (wave * 32 + 31) / GP, seq_end - 1);
     const int wklo = WIN ? max(seq_start, wt0 - a.window) : seq_start;
     const int wkhi = wt1;
+    auto visible = [&](int step) {
+        const int k0 = kstart + step * BN;
+        return step < nsteps && !(k0 > wkhi || k0 + BN - 1 < wklo);
+    };
+    auto masked = [&](int step) {
+        const int k0 = kstart + step * BN;
+        return k0 + BN - 1 > wt0 || k0 < seq_start || (WIN && k0 < wt1 - a.window);
+    };
+    // mask bound: key kj is seen by this lane's query iff 0 <= qt - kj <= ub (rows of invalid query lanes
+    // are never written back)
+    const int ub = WIN ? min(a.window, qt - seq_start) : qt - seq_start;
 
     f32x16 dq[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) dq[i] = f32x16{};
 
-    auto compute = [&](int k0, const DqTile &T) {
-        const u16 *kr = (const u16 *)T.kr, *kt = (const u16 *)T.kt, *vr = (const u16 *)T.vr;
+    // S^T = K' Q'^T and dP^T = V dO^T of one tile
+    auto sdp = [&](const DqTile &T, f32x16 &sacc, f32x16 &dpacc) {
+        const u16 *kr = (const u16 *)T.kr, *vr = (const u16 *)T.vr;
+        sacc = f32x16{};
+        dpacc = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int kbase = k0 + 32 * kb;
-            if (kbase > wkhi || kbase + 31 < wklo) continue;
-            const int rr = 32 * kb + c;
-            f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(kr + (c * KCH + swz384(c, 2 * s + hh)) * 8), qf[s], sacc);
 #pragma unroll
-            for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(kr + (rr * KCH + swz384(rr, 2 * s + hh)) * 8), qf[s], sacc);
+        for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(vr + (c * VCH + swz256(c, 2 * s + hh)) * 8), of[s], dpacc);
+    };
+    // dS^T of one tile (uba = the mask bound, or all-ones for a tile that needs no mask)
+    auto softmax = [&](int step, const f32x16 &sacc, const f32x16 &dpacc, uint32_t uba, bf16x8 *sb) {
+        const int base = qt - (kstart + step * BN) - 4 * hh;   // qt - key of this lane's first row
 #pragma unroll
-            for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(vr + (rr * VCH + swz256(rr, 2 * s + hh)) * 8), of[s], dpacc);
-            const bool need_mask = (kbase + 31 > wt0) || (kbase < seq_start) || (WIN && kbase < wt1 - a.window);
-            bf16x8 sb[2];
+        for (int j = 0; j < 16; ++j) {
+            float p = fast_exp2(sacc[j] * a.scale_log2 - Lq);
+            p = (uint32_t)(base - 8 * (j >> 2) - (j & 3)) <= uba ? p : 0.f;
+            sb[j >> 3][j & 7] = f2bf(p * (VSCALE * dpacc[j] - Dq));
+        }
+    };
+    // dQ^T += K'^T dS^T (two 16-key k-steps)
+    auto dq_mm = [&](const DqTile &T, const bf16x8 *sb) {
+        const u16 *kt = (const u16 *)T.kt;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float p = fast_exp2(sacc[j] * a.scale_log2 - Lq);
-                if (need_mask) {
-                    const int key = kbase + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    const bool ok = key <= qt && key >= seq_start && (!WIN || key >= qt - a.window);
-                    p = ok ? p : 0.f;
-                }
-                sb[j >> 3][j & 7] = f2bf(p * (VSCALE * dpacc[j] - Dq));
-            }
+        for (int i = 0; i < 6; ++i) {
+            const int d = 32 * i + c;
 #pragma unroll
-            for (int i = 0; i < 6; ++i) {
-                const int d = 32 * i + c;
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    dq[i] = mfma32(ld16(kt + (d * KTCH + swz128(d, 4 * kb + 2 * s + hh)) * 8), sb[s], dq[i]);
-            }
+            for (int s = 0; s < 2; ++s) dq[i] = mfma32(ld16(kt + (d * KTCH + swz64(d, 2 * s + hh)) * 8), sb[s], dq[i]);
         }
     };
 
-    const int klast = kstart + (nkt - 1) * BN;
-    for (int it = 0; it < nkt; it += 2) {
-        const int k0 = kstart + it * BN;
-        issue(min(k0 + BN, klast), t1s);
-        wait_vmcnt<DQ_LOADS>();
+    // ---- three-stage tile ring, software-pipelined like the dK/dV kernel: at stage st the tiles of steps st
+    // and st+1 are read and step st+2 is loaded; the softmax of step st runs between the S/dP products of
+    // step st+1, then dQ of step st.
+    f32x16 sA = f32x16{}, dA = f32x16{}, sB = f32x16{}, dB = f32x16{};
+    wait_vmcnt<L_KR + L_KT + L_VR>();
+    __builtin_amdgcn_s_barrier();
+    sdp(t0s, sA, dA);
+    auto stage = [&](int st, const DqTile &cur, const DqTile &nxt, DqTile &fill, const f32x16 &s0, const f32x16 &d0,
+                     f32x16 &s1, f32x16 &d1) {
+        wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        compute(k0, t0s);
-        __builtin_amdgcn_s_barrier();
-        issue(min(k0 + 2 * BN, klast), t0s);
-        wait_vmcnt<DQ_LOADS>();
-        __builtin_amdgcn_s_barrier();
-        if (it + 1 < nkt) compute(k0 + BN, t1s);
-        __builtin_amdgcn_s_barrier();
+        issue(min(st + 2, nsteps - 1), fill);
+        if (visible(st) || visible(st + 1)) {
+            const uint32_t uba = masked(st) ? (uint32_t)ub : 0xffffffffu;
+            bf16x8 sb[2];
+            softmax(st, s0, d0, uba, sb);
+            sdp(nxt, s1, d1);
+            dq_mm(cur, sb);
+            __builtin_amdgcn_sched_group_barrier(0x100, DQ_AHEAD, 0);       // first operand reads
+#pragma unroll
+            for (int i = 0; i < 20; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA (S, dP of step st+1)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);          // VALU (softmax of step st)
+            }
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA (dQ of step st)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);          // VALU
+            }
+        }
+    };
+    for (int st = 0; st < nsteps; st += 6) {
+        stage(st, t0s, t1s, t2s, sA, dA, sB, dB);
+        if (st + 1 >= nsteps) break;
+        stage(st + 1, t1s, t2s, t0s, sB, dB, sA, dA);
+        if (st + 2 >= nsteps) break;
+        stage(st + 2, t2s, t0s, t1s, sA, dA, sB, dB);
+        if (st + 3 >= nsteps) break;
+        stage(st + 3, t0s, t1s, t2s, sB, dB, sA, dA);
+        if (st + 4 >= nsteps) break;
+        stage(st + 4, t1s, t2s, t0s, sA, dA, sB, dB);
+        if (st + 5 >= nsteps) break;
+        stage(st + 5, t2s, t0s, t1s, sB, dB, sA, dA);
     }
     wait_vmcnt<0>();
 
