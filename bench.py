@@ -35,7 +35,8 @@ FWD_FLOP_PER_PAIR = 2 * (192 + 128)
 BWD_FLOP_PER_PAIR = 2 * (3 * 192 + 2 * 128)
 # per-kernel algorithmic work: the dK/dV kernel does S, dP, dV, dK (2*(192+128+128+192) per pair); the dQ
 # kernel's new work is dQ (2*192 per pair; its S and dP are recomputation)
-KERNEL_FLOP_PER_PAIR = {"attn_fwd": FWD_FLOP_PER_PAIR, "bwd_dkdv": 2 * (192 + 128 + 128 + 192), "bwd_dq": 2 * 192}
+KERNEL_FLOP_PER_PAIR = {"attn_fwd": FWD_FLOP_PER_PAIR, "bwd_dkdv": 2 * (192 + 128 + 128 + 192), "bwd_dq": 2 * 192,
+                        "bwd_dq_ds": 2 * 192}
 
 
 def pairs_per_head(lengths, window):
@@ -155,7 +156,9 @@ def setup_layers(ga, torch, mi, dev):
         g["lse"] = torch.empty(hq, T, dtype=torch.float32, device=dev)
         g["grads"] = (torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"]),
                       torch.empty(hq, dtype=torch.float32, device=dev) if g["sink"] is not None else None)
-        g["ws"] = torch.empty(ga.bwd_workspace_size(T, hq, hkv, g["window"]), dtype=torch.uint8, device=dev)
+        # the workspace that keeps the dS blocks (the dQ kernel reads them back instead of recomputing)
+        g["ws"] = torch.empty(ga.bwd_workspace_size(T, hq, hkv, g["window"], len(d["lengths"]), max(d["lengths"])),
+                              dtype=torch.uint8, device=dev)
         g["pairs"] = pairs_per_head(d["lengths"], d["window"]) * hq
         layers[name] = g
     dout = dout_cpu.to(dev)
@@ -173,6 +176,7 @@ def setup_layers(ga, torch, mi, dev):
 # trace name prefix -> kernel function name (checks that traced launches and counted dispatches line up)
 TRACE_TO_KERNEL = (("kv_prep", "kv_prep_kernel"), ("attn_fwd", "attn_fwd_kernel"), ("bwd_prep", "row_prep_kernel"),
                    ("bwd_pre", "bwd_pre_kernel"), ("bwd_dsink", "bwd_dsink_kernel"),
+                   ("bwd_ds_index", "bwd_ds_index_kernel"), ("bwd_dq_ds", "bwd_dq_ds_kernel"),
                    ("bwd_dkdv", "bwd_dkdv_kernel"), ("bwd_dkv_reduce", "bwd_dkv_reduce_kernel"),
                    ("bwd_dq", "bwd_dq_kernel"), ("decode_split", "decode_split_kernel"),
                    ("decode_combine", "decode_combine_kernel"))

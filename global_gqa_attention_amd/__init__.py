@@ -43,6 +43,8 @@ def lib():
         L.mimo_attn_fwd_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_fwd_workspace_size.restype = sz
         L.mimo_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mimo_attn_bwd_workspace_size_fast.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.mimo_attn_bwd_workspace_size_fast.restype = sz
         L.mimo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
         L.mimo_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_decode.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
@@ -136,12 +138,19 @@ def fwd(q, k, v, sink, cu_seqlens, max_seqlen, window, rope_base, out=None, lse=
     return out, lse
 
 
-def bwd_workspace_size(total_tokens, n_q_heads, n_kv_heads, window) -> int:
-    return int(lib().mimo_attn_bwd_workspace_size(int(total_tokens), int(n_q_heads), int(n_kv_heads), int(window)))
+def bwd_workspace_size(total_tokens, n_q_heads, n_kv_heads, window, batch=None, max_seqlen=None) -> int:
+    """Workspace bytes of the backward: the least size (dQ recomputes S and dP) when batch or max_seqlen is not
+    given, else the size that selects the stored-dS path (mimo_attn_bwd_workspace_size_fast)."""
+    if batch is None or max_seqlen is None:
+        return int(lib().mimo_attn_bwd_workspace_size(int(total_tokens), int(n_q_heads), int(n_kv_heads),
+                                                      int(window)))
+    return int(lib().mimo_attn_bwd_workspace_size_fast(int(total_tokens), int(batch), int(max_seqlen),
+                                                       int(n_q_heads), int(n_kv_heads), int(window)))
 
 
 def bwd(q, k, v, sink, out, lse, dout, cu_seqlens, max_seqlen, window, rope_base, workspace=None, grads=None):
-    """Backward of one layer.  Returns (dq, dk, dv, dsink or None)."""
+    """Backward of one layer.  Returns (dq, dk, dv, dsink or None).  Without a workspace one of the fast size
+    (stored dS) is allocated; a given workspace selects the path by its size."""
     T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
     _need(out, "out", torch.bfloat16, (T, hq, DV))
     _need(dout, "dout", torch.bfloat16, (T, hq, DV))
@@ -153,8 +162,8 @@ def bwd(q, k, v, sink, out, lse, dout, cu_seqlens, max_seqlen, window, rope_base
         dsink = torch.empty((hq,), dtype=torch.float32, device=q.device) if sink is not None else None
     else:
         dq, dk, dv, dsink = grads
-    need = bwd_workspace_size(T, hq, hkv, window)
     if workspace is None:
+        need = bwd_workspace_size(T, hq, hkv, window, batch, max_seqlen)
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
     rc = lib().mimo_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout),
                              _ptr(cu_seqlens), batch, T, int(max_seqlen), int(window), float(rope_base), hq, hkv,

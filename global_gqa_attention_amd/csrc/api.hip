@@ -268,6 +268,14 @@ size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int
     return mimo::bwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
 }
 
+size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, int32_t max_seqlen,
+                                         int32_t n_q_heads, int32_t n_kv_heads, int32_t window)
+{
+    if (total_tokens < 0 || batch < 0 || max_seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
+    const size_t ds = mimo::bwd_workspace_bytes_ds(total_tokens, n_q_heads, n_kv_heads, window, batch, max_seqlen);
+    return ds ? ds : mimo::bwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
+}
+
 mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const float *sink,
                             const void *out, const float *lse, const void *dout,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
@@ -316,7 +324,11 @@ mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const f
     a.dk = (uint16_t *)dk;
     a.dv = (uint16_t *)dv;
     a.dsink = dsink;
-    mimo::bwd_carve(workspace, total_tokens, n_q_heads, n_kv_heads, &a);
+    const size_t ds_need = mimo::bwd_workspace_bytes_ds(total_tokens, n_q_heads, n_kv_heads, window, batch,
+                                                        max_seqlen);
+    const bool stored_ds = ds_need > 0 && workspace_bytes >= ds_need;
+    mimo::bwd_carve(workspace, total_tokens, n_q_heads, n_kv_heads, &a, stored_ds, batch, max_seqlen);
+    if (stored_ds) a.ds_cap = (int64_t)((ds_need - (size_t)((char *)a.ds - (char *)workspace)) / 2048);
     hipError_t e = mimo::launch_bwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return ok();

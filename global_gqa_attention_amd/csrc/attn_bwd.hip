@@ -13,17 +13,18 @@
 // dsink is summed in a fixed order, so results are bitwise repeatable):
 //   1. bwd_pre:   D and LSE * log2(e) for every (head, token), zero-padded to T_pad.
 //   2. bwd_dsink: one workgroup per head, fixed-order tree sum (only when a sink is given).
-//   3. row_prep:  DMA-ready copies in the workspace: q' (rotated) row-major and transposed, dO transposed,
-//                 k' (rotated) row-major and transposed.  Transposed copies keep each 16-token group's
-//                 4-token chunks in the order (0, 2, 1, 3), the order in which the score registers hold
-//                 tokens, so an MFMA operand read of 8 consecutive elements is one 16-byte LDS read.
+//   3. row_prep:  DMA-ready copies in the workspace: q' (rotated) row-major, k' (rotated) row-major and
+//                 transposed (the transposed copy keeps each 16-token group's 4-token chunks in the order
+//                 (0, 2, 1, 3), the order in which the score registers hold tokens).
 //   4. bwd_dkdv:  key-major.  A workgroup owns 128 keys of one KV head (32 per wave; the key is the MFMA
 //                 column, so each lane owns one key with its rotated k and v resident in registers) and
 //                 walks every (query head of the group, 32-query tile) that sees them: S = Q'K'^T, P,
-//                 dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q'^T dS.  The four query-side tiles
-//                 (q' both layouts, dO both layouts) and LSE/D stream HBM -> LDS with global_load_lds,
-//                 double-buffered and XOR-swizzled (conflict-free operand reads).
-//   5. bwd_dq:    query-major, shaped like the forward: S^T = K'Q'^T, P^T, dP^T = V dO^T, dS^T, then
+//                 dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q'^T dS.  The q' and dO row tiles and
+//                 LSE/D stream HBM -> LDS with global_load_lds (three-stage ring, XOR-swizzled); the
+//                 transposed operands of dV and dK come from the same tiles through ds_read_b64_tr_b16.
+//                 With the stored-dS workspace it also writes every dS block it computes.
+//   5. bwd_dq:    either from the stored dS blocks (5b: dQ^T += K'^T dS^T, no recomputation), or
+//                 query-major like the forward: S^T = K'Q'^T, P^T, dP^T = V dO^T, dS^T, then
 //                 dQ^T += K'^T dS^T with k' (both layouts) and v streamed HBM -> LDS.
 // dq and dk leave through the transposed rotation in their epilogues.
 #include <type_traits>
@@ -51,6 +52,30 @@ __device__ __forceinline__ int tperm16(int t)
 {
     const int c4 = (t >> 2) & 3;
     return (t & ~15) | ((((c4 & 1) << 1) | (c4 >> 1)) << 2) | (t & 3);
+}
+
+// ------------------------------------------------------------------------------------------------------
+// Stored-dS layout.  A block is 32 queries x 32 keys of one head in bf16 (2 KB), written by the dK/dV
+// kernel in its own register order as two 1 KB planes: plane P, row (L ^ 8 (L / 32) ^ 4 P) holds the 8
+// values of lane L = key + 32 hh for queries 16 P + 4 hh + 8 (e / 4) + e % 4, e = 0..7 (the row permutation
+// spreads the dQ kernel's transposed reads over all LDS banks; each plane is one whole store).  Query tiles of sequence b
+// start at S16 = seq_start & ~15 (tile n: S16 + 32 n ..), key blocks at seq_start (block k: seq_start +
+// 32 k ..).  Row n of a sequence holds the key blocks k_lo(n) .. k_hi(n) that tile n sees: causal rows
+// have n + 1 slots, sliding-window rows ds_row_width(window) slots.
+// ------------------------------------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int ds_row_width(int window) { return (window + 62) / 32 + 1; }
+__device__ __forceinline__ int ds_nq(int seq_start, int seq_end)
+{
+    return seq_end > seq_start ? (seq_end - 1 - (seq_start & ~15)) / 32 + 1 : 0;
+}
+__device__ __forceinline__ int64_t ds_rows_before(int n, int window)
+{
+    return window >= 0 ? (int64_t)n * ds_row_width(window) : (int64_t)n * (n + 1) / 2;
+}
+// first key block that query tile n (first query q0) can see
+__device__ __forceinline__ int ds_klo(int q0, int seq_start, int window)
+{
+    return window >= 0 ? max(0, q0 - window - seq_start) / 32 : 0;
 }
 
 // Transposed RoPE of a 32-dim block pair held in C layout: x0 = dims 8(j/4)+4hh+j%4, x1 the same dims + 32.
@@ -122,6 +147,35 @@ __global__ void zero_kernel(float *p, int n)
     if (i < n) p[i] = 0.f;
 }
 
+// ds_index[b] = dS blocks of sequences 0 .. b-1 within one head (exclusive scan over the batch, one
+// workgroup), ds_index[batch] = blocks per head
+__global__ __launch_bounds__(256) void bwd_ds_index_kernel(const BwdArgs A)
+{
+    __shared__ int64_t part[256];
+    const int tid = threadIdx.x, batch = A.L.batch;
+    const int per = (batch + 255) / 256, b0 = min(batch, tid * per), b1 = min(batch, b0 + per);
+    auto region = [&](int b) { return ds_rows_before(ds_nq(A.L.cu[b], A.L.cu[b + 1]), A.L.window); };
+    int64_t sum = 0;
+    for (int b = b0; b < b1; ++b) sum += region(b);
+    part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t run = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int64_t v = part[i];
+            part[i] = run;
+            run += v;
+        }
+        A.ds_index[batch] = run;
+    }
+    __syncthreads();
+    int64_t run = part[tid];
+    for (int b = b0; b < b1; ++b) {
+        A.ds_index[b] = run;
+        run += region(b);
+    }
+}
+
 // ------------------------------------------------------------------------------------------------------
 // 3. row_prep: for 64 tokens of head h of x [T, H, D]: optional rotation of dims 0..63, then a row-major
 //    copy rm [T_pad, H, D] and/or a transposed copy tr [H, D, T_pad] (tokens in tperm16 order), zero-filled
@@ -175,16 +229,13 @@ constexpr int NKB = 128;                 // keys per workgroup (32 per wave)
 constexpr int MQ = 32;                   // queries per step
 constexpr int QCH = DQK / 8;             // 24 chunks per q' row
 constexpr int OCH = DVV / 8;             // 16 chunks per dO row
-constexpr int TCH = MQ / 8;              // 4 chunks per transposed row
 constexpr int DK_QR = MQ * QCH / 256;    // DMAs per thread per step: q' rows (3)
-constexpr int DK_QT = DQK * TCH / 256;   // q'^T (3)
 constexpr int DK_OR = MQ * OCH / 256;    // dO rows (2)
-constexpr int DK_OT = DVV * TCH / 256;   // dO^T (2)
-constexpr int DK_LOADS = DK_QR + DK_QT + DK_OR + DK_OT + 1;   // + LSE/D (one per wave)
+constexpr int DK_LOADS = DK_QR + DK_OR + 1;   // + LSE/D (one per wave)
 constexpr int DK_AHEAD = 4;              // LDS operand reads in flight ahead of the MFMAs
 
 struct DkdvTile {
-    uint4 qr[MQ * QCH], qt[DQK * TCH], orow[MQ * OCH], ot[DVV * TCH];
+    uint4 qr[MQ * QCH], orow[MQ * OCH];  // q' and dO rows (read as rows and, transposed, as columns)
     float ld[2 * MQ];                    // LSE * log2(e) [MQ], then D [MQ]
 };
 
@@ -205,19 +256,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int split = (x / a.hkv) % A.splits;
     int tile = x / a.hkv / A.splits;
     const int GS = G / A.splits;      // query heads handled by this workgroup
-    int seq_start = 0, seq_end = 0;
-    bool found = false;
+    int seq_start = 0, seq_end = 0, bseq = -1;
     for (int b = a.batch - 1; b >= 0; --b) {
         seq_start = a.cu[b];
         seq_end = a.cu[b + 1];
         const int nt = (seq_end - seq_start + NKB - 1) / NKB;
         if (tile < nt) {
-            found = true;
+            bseq = b;
             break;
         }
         tile -= nt;
     }
-    if (!found) return;
+    if (bseq < 0) return;
     const int kb0 = seq_start + tile * NKB;
     const int kb_last = min(kb0 + NKB - 1, seq_end - 1);
 
@@ -229,26 +279,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
 
     // ---- direct HBM -> LDS loads of one step's tiles: fixed per-lane byte offsets + wave-uniform bases
     const size_t qr_row = (size_t)a.hq * DQK, o_row = (size_t)a.hq * DVV;
-    uint32_t o_qr[DK_QR], o_qt[DK_QT], o_or[DK_OR], o_ot[DK_OT];
+    uint32_t o_qr[DK_QR], o_or[DK_OR];
 #pragma unroll
     for (int j = 0; j < DK_QR; ++j) {
         const int slot = 256 * j + tid, r = slot / QCH, p = slot % QCH;
-        o_qr[j] = (uint32_t)((r * qr_row + 8 * swz384(r, p)) * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < DK_QT; ++j) {
-        const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
-        o_qt[j] = (uint32_t)(((size_t)d * A.T_pad + 8 * swz64(d, p)) * 2);
+        o_qr[j] = (uint32_t)((r * qr_row + 8 * swz384t(r, p)) * 2);
     }
 #pragma unroll
     for (int j = 0; j < DK_OR; ++j) {
         const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
-        o_or[j] = (uint32_t)((r * o_row + 8 * swz256(r, p)) * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < DK_OT; ++j) {
-        const int slot = 256 * j + tid, d = slot / TCH, p = slot % TCH;
-        o_ot[j] = (uint32_t)(((size_t)d * A.T_pad + 8 * swz64(d, p)) * 2);
+        o_or[j] = (uint32_t)((r * o_row + 8 * swz256t(r, p)) * 2);
     }
     // step -> (head, query tile): heads outer, query tiles from the sequence end down.  Every key tile of a
     // sequence walks the same absolute query tiles in the same order, so the workgroups running together
@@ -258,13 +298,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
         const int h = kvh * G + split * GS + step / nq;
         const int q0 = step_q0(step);
         const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
-        const u16 *bqt = A.W.qrt + (size_t)h * DQK * A.T_pad + q0;
         const u16 *bo = A.dout + ((size_t)q0 * a.hq + h) * DVV;
-        const u16 *bot = A.W.dot + (size_t)h * DVV * A.T_pad + q0;
 #pragma unroll
         for (int j = 0; j < DK_QR; ++j) lds_dma16(bq, o_qr[j], T.qr + 256 * j + 64 * wave);
-#pragma unroll
-        for (int j = 0; j < DK_QT; ++j) lds_dma16(bqt, o_qt[j], T.qt + 256 * j + 64 * wave);
         if (q0 + MQ <= a.T) {
 #pragma unroll
             for (int j = 0; j < DK_OR; ++j) lds_dma16(bo, o_or[j], T.orow + 256 * j + 64 * wave);
@@ -274,11 +310,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
             for (int j = 0; j < DK_OR; ++j) {
                 const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
                 const int row = min(q0 + r, a.T - 1);
-                lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256(r, p), T.orow + 256 * j + 64 * wave);
+                lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256t(r, p), T.orow + 256 * j + 64 * wave);
             }
         }
-#pragma unroll
-        for (int j = 0; j < DK_OT; ++j) lds_dma16(bot, o_ot[j], T.ot + 256 * j + 64 * wave);
         // LSE*log2e (waves 0, 1) and D (waves 2, 3): 2 x 128 bytes, four lanes of each wave load 16 bytes
         const float *bld = (wave < 2 ? A.lse2 : A.delta) + (size_t)h * A.T_pad + q0 + 16 * (wave & 1);
         if (lane < 4) lds_dma16(bld, (uint32_t)(16 * lane), (uint4 *)T.ld + 4 * wave);
@@ -316,99 +350,139 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     };
     auto masked = [&](int step) {
         const int q0 = step_q0(step);
-        return q0 < kw0 + 31 || q0 + MQ - 1 > q_hi || (WIN && q0 + MQ - 1 - kw0 > a.window);
+        return q0 < kw0 + 31 || q0 + MQ - 1 > q_hi || (WIN && q0 + MQ - 1 - kw0 > a.window) || kw0 + 31 > kb_last;
     };
-    // mask bound: query qi sees this lane's key iff 0 <= qi - kj <= ub.  Lanes past the tile's last key are
-    // never written back, so their values do not matter.  An invisible step is masked, so computing it
-    // anyway adds exact zeros.
-    const int ub = WIN ? min(a.window, q_hi - kj) : q_hi - kj;
+    // mask bound: query qi sees this lane's key iff 0 <= qi - kj <= ub.  Lanes past the tile's last key see
+    // nothing (their key is moved 2^30 away, so the unsigned test fails): their dK/dV are never written back,
+    // and their dS blocks must hold zeros.  An invisible step is masked, so computing it anyway adds zeros.
+    const int ub = !kvalid ? 0 : WIN ? min(a.window, q_hi - kj) : q_hi - kj;
+    const int kjm = kvalid ? kj : kj + (1 << 30);
 
     auto sdp = [&](const DkdvTile &T, f32x16 &sacc, f32x16 &dpacc) {
         const u16 *qr = (const u16 *)T.qr, *orr = (const u16 *)T.orow;
         sacc = f32x16{};
         dpacc = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(qr + (c * QCH + swz384(c, 2 * s + hh)) * 8), kf[s], sacc);
+        for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(qr + (c * QCH + swz384t(c, 2 * s + hh)) * 8), kf[s], sacc);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(orr + (c * OCH + swz256(c, 2 * s + hh)) * 8), vf[s], dpacc);
+        for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(orr + (c * OCH + swz256t(c, 2 * s + hh)) * 8), vf[s], dpacc);
     };
-    // P and dS of one step (uba = the mask bound, or all-ones for a step that needs no mask)
-    auto softmax = [&](int step, const DkdvTile &T, const f32x16 &sacc, const f32x16 &dpacc, uint32_t uba,
-                       bf16x8 *pb, bf16x8 *sb) {
-        const int base = step_q0(step) - kj;   // qi - kj of this lane's first row
+    // ---- the fused step, scheduled by hand: 40 groups, each one MFMA and the LDS read of the operand that
+    // the MFMA DK_AHEAD groups later consumes; groups 0..15 also compute P and dS of one score of step st.
+    // Groups 0..19 are the S/dP products of step st+1 (tiles in nxt), groups 20..39 the dV/dK products of
+    // step st (tiles in cur, with P and dS of step st as B operands).  A scheduling fence closes every
+    // window of four groups: the compiler may interleave the four softmax chains of a window with its
+    // MFMAs, but keeps each read a window ahead of the MFMA that consumes it.
+    // operand k of the fused step: rows of q' / dO (S, dP of step st+1) or, read transposed, their columns
+    // (dV, dK of step st).  Transposed read r of k-step s covers rows 16 s + 8 r + 4 hh + t4 and the four
+    // columns 32 i + 16 (grp & 1) + 4 m4 .. + 3 of the operand's 32-row block i (lane il = 4 t4 + m4).
+    const int grp = lane >> 4, t4 = (lane & 15) >> 2, m4 = lane & 3;
+    auto tr_at = [&](const void *tile, int rowbytes, bool w384, int s, int r, int i) -> const char * {
+        const int R = 16 * s + 8 * r + 4 * hh + t4;
+        const int q = 4 * i + 2 * (grp & 1) + (m4 >> 1);
+        const int p = w384 ? swz384t(R, q) : swz256t(R, q);
+        return (const char *)tile + R * rowbytes + 16 * p + 8 * (m4 & 1);
+    };
+    auto load_op = [&](int k, const DkdvTile &cur, const DkdvTile &nxt) -> bf16x8 {
+        if (k < 12) return ld16((const u16 *)nxt.qr + (c * QCH + swz384t(c, 2 * k + hh)) * 8);
+        if (k < 20) return ld16((const u16 *)nxt.orow + (c * OCH + swz256t(c, 2 * (k - 12) + hh)) * 8);
+        if (k < 28) {
+            const int i = (k - 20) >> 1, sk = (k - 20) & 1;
+            return tr_pair(tr_at(cur.orow, OCH * 16, false, sk, 0, i), tr_at(cur.orow, OCH * 16, false, sk, 1, i));
+        }
+        const int i = (k - 28) >> 1, sk = (k - 28) & 1;
+        return tr_pair(tr_at(cur.qr, QCH * 16, true, sk, 0, i), tr_at(cur.qr, QCH * 16, true, sk, 1, i));
+    };
+    auto fused = [&](int q0, uint32_t uba, const DkdvTile &cur, const DkdvTile &nxt, const f32x16 &s0,
+                     const f32x16 &d0, f32x16 &s1, f32x16 &d1, bf16x8 *pb, bf16x8 *sb) {
+        const int base = q0 - kjm;   // qi - kj of this lane's first row
+        float4 L4[4], D4[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int ql = 8 * jj + 4 * hh;
-            const float4 L4 = *(const float4 *)(T.ld + ql);
-            const float4 D4 = *(const float4 *)(T.ld + MQ + ql);
-            const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-            const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+            L4[jj] = *(const float4 *)(cur.ld + 8 * jj + 4 * hh);
+            D4[jj] = *(const float4 *)(cur.ld + MQ + 8 * jj + 4 * hh);
+        }
+        constexpr int R = 2 * DK_AHEAD;
+        bf16x8 ob[R];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int j = 4 * jj + t;
-                float p = fast_exp2(sacc[j] * a.scale_log2 - Lv[t]);
-                p = (uint32_t)(base + ql + t) <= uba ? p : 0.f;
-                pb[j >> 3][j & 7] = f2bf(p);
-                sb[j >> 3][j & 7] = f2bf(p * (VSCALE * dpacc[j] - Dv[t]));
+        for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, cur, nxt);
+        s1 = f32x16{};
+        d1 = f32x16{};
+        float pf[16], df[16];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 40; ++k) {
+            if (k < 12) s1 = mfma32(ob[k % R], kf[k], s1);
+            else if (k < 20) d1 = mfma32(ob[k % R], vf[k - 12], d1);
+            else if (k < 28) dv[(k - 20) >> 1] = mfma32(ob[k % R], pb[(k - 20) & 1], dv[(k - 20) >> 1]);
+            else dk[(k - 28) >> 1] = mfma32(ob[k % R], sb[(k - 28) & 1], dk[(k - 28) >> 1]);
+            if (k + DK_AHEAD < 40) ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, cur, nxt);
+            if (k < 16) {
+                const int j = k, jj = j >> 2, t = j & 3;
+                const float Lv = t == 0 ? L4[jj].x : t == 1 ? L4[jj].y : t == 2 ? L4[jj].z : L4[jj].w;
+                const float Dv = t == 0 ? D4[jj].x : t == 1 ? D4[jj].y : t == 2 ? D4[jj].z : D4[jj].w;
+                float p = fast_exp2(s0[j] * a.scale_log2 - Lv);
+                p = (uint32_t)(base + 8 * jj + 4 * hh + t) <= uba ? p : 0.f;
+                pf[j] = p;
+                df[j] = p * (VSCALE * d0[j] - Dv);
+                if (j & 1) {
+                    pb[j >> 3][(j & 7) - 1] = f2bf(pf[j - 1]);
+                    pb[j >> 3][j & 7] = f2bf(pf[j]);
+                    sb[j >> 3][(j & 7) - 1] = f2bf(df[j - 1]);
+                    sb[j >> 3][j & 7] = f2bf(df[j]);
+                }
             }
+            if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // dV^T += dO^T P,  dK^T += Q'^T dS  (two 16-query k-steps)
-    auto dkdv_mm = [&](const DkdvTile &T, const bf16x8 *pb, const bf16x8 *sb) {
-        const u16 *ot = (const u16 *)T.ot, *qt = (const u16 *)T.qt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = 32 * i + c;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) dv[i] = mfma32(ld16(ot + (d * TCH + swz64(d, 2 * s + hh)) * 8), pb[s], dv[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int d = 32 * i + c;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) dk[i] = mfma32(ld16(qt + (d * TCH + swz64(d, 2 * s + hh)) * 8), sb[s], dk[i]);
-        }
+
+    // dS of a step into the stored-dS blocks (query tile n, key block kap = 4 tile + wave; see ds_row_width)
+    const int s16 = seq_start & ~15;
+    const int kap = 4 * tile + wave;
+    const int64_t ds_head = A.ds ? A.ds_index[a.batch] : 0, ds_seq = A.ds ? A.ds_index[bseq] : 0;
+    auto store_ds = [&](int step, const bf16x8 *sb) {
+        const int h = kvh * G + split * GS + step / nq;
+        const int q0 = step_q0(step);
+        const int n = (q0 - s16) >> 5;
+        const int64_t blk = (int64_t)h * ds_head + ds_seq + ds_rows_before(n, a.window) +
+                            (kap - ds_klo(q0, seq_start, a.window));
+        if (blk >= A.ds_cap) return false;   // only with a max_seqlen below the longest sequence
+        // streaming stores: the blocks are read back by another kernel, so keep them out of L2's way
+        // plane P holds sb[P] of every lane at row (lane ^ 8 hh ^ 4 P): each store writes a whole 1 KB plane
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 *dst = (u32x4 *)(A.ds + blk * 1024);
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[0]), dst + (lane ^ (8 * hh)));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), dst + 64 + (lane ^ (8 * hh) ^ 4));
+        return true;
     };
 
     // ---- three-stage tile ring.  At stage st the tiles of steps st and st+1 are read and step st+2 is
     // loaded: wait for all of this wave's loads (step st+1's tiles, issued one stage earlier), barrier (every
     // wave has landed its part and has finished stage st-1, whose buffer the new loads refill), issue.  Every
     // stage issues one tile set (the last step's again once the steps run out), so the waits stay uniform.
-    // The compute of a stage is the softmax of step st (its S/dP in s0/d0) with the S/dP of step st+1 (into
-    // s1/d1) interleaved, then dV/dK of step st: one basic block, so the scheduler can mix the two chains
-    // and keep the MFMA pipe busy while the VALU works; the group barriers ask for one MFMA, one LDS read and
-    // a run of VALU work in turn.
+    // The compute of a stage is the fused step above: the softmax of step st (its S/dP in s0/d0) between
+    // the S/dP products of step st+1 (into s1/d1), then the dV/dK products of step st.
     f32x16 sA = f32x16{}, dA = f32x16{}, sB = f32x16{}, dB = f32x16{};
     issue(0, t0s);
     issue(min(1, nsteps - 1), t1s);
     wait_vmcnt<DK_LOADS>();
     __builtin_amdgcn_s_barrier();
     sdp(t0s, sA, dA);
+    // vmcnt also counts stores, and counts complete in issue order: when the previous stage ended with its
+    // two dS stores, waiting for all but two vector memory operations lands the tiles issued before them
+    // without waiting for the stores to reach memory.
+    bool stored = false;
     auto stage = [&](int st, const DkdvTile &cur, const DkdvTile &nxt, DkdvTile &fill, const f32x16 &s0,
                      const f32x16 &d0, f32x16 &s1, f32x16 &d1) {
-        wait_vmcnt<0>();
+        if (stored) wait_vmcnt<2>();
+        else wait_vmcnt<0>();
+        stored = false;
         __builtin_amdgcn_s_barrier();
         issue(min(st + 2, nsteps - 1), fill);
         if (visible(st) || visible(st + 1)) {
-            const uint32_t uba = masked(st) ? (uint32_t)ub : 0xffffffffu;
             bf16x8 pb[2], sb[2];
-            softmax(st, cur, s0, d0, uba, pb, sb);
-            sdp(nxt, s1, d1);
-            dkdv_mm(cur, pb, sb);
-            // LDS operand reads run DK_AHEAD reads ahead of the MFMAs that consume them
-            __builtin_amdgcn_sched_group_barrier(0x100, 8 + DK_AHEAD, 0);   // LSE/D rows + first operands
-#pragma unroll
-            for (int i = 0; i < 20; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA (S, dP of step st+1)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);          // VALU (softmax of step st)
-            }
-#pragma unroll
-            for (int i = 0; i < 20; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA (dV, dK of step st)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);          // VALU
-            }
+            fused(step_q0(st), masked(st) ? (uint32_t)ub : 0xffffffffu, cur, nxt, s0, d0, s1, d1, pb, sb);
+            if (A.ds && visible(st)) stored = store_ds(st, sb);
         }
     };
     // unrolled by six: the tile ring has period three and the S/dP register pair period two
@@ -728,6 +802,155 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
     }
 }
 
+// ------------------------------------------------------------------------------------------------------
+// 5b. dQ from the stored dS blocks: dQ^T += K'^T dS^T per 32-key block, no recomputation.  A workgroup owns
+//     one query tile (32 queries) of four query heads of one KV group (one head per wave) and walks the key
+//     blocks the tile sees.  Per block the four waves share one row-major k' tile (32 keys x 192) and each
+//     loads its head's dS block; both MFMA operands come out of LDS through ds_read_b64_tr_b16, which hands
+//     every lane of a 16-lane group one 16-bit column element of four rows read by four other lanes:
+//     lane i, element t <- the 4-element row read by lane 4 t + i / 4, element i % 4.  The MFMA k index
+//     8 hh + 4 r + t of read r (0, 1) stands for key 16 s + 8 r + 4 hh + t in both operands.
+// ------------------------------------------------------------------------------------------------------
+constexpr int DSQ_NS = 5;                // ring stages (four block loads in flight: the kernel streams HBM)
+constexpr int DSQ_KL = 32 * KCH / 256;   // k' DMAs per thread per block (3)
+constexpr int DSQ_LOADS = DSQ_KL + 2;    // + this wave's dS block (2 KB: two per lane)
+
+struct DsqTile {
+    uint4 kr[32 * KCH];                  // k' rows, 16-byte chunk q of row r at q ^ (4 ((r >> 1) & 1))
+    uint4 ds[4][128];                    // one stored dS block per wave
+};
+
+
+template <bool WIN>
+__global__ __launch_bounds__(256, 1) void bwd_dq_ds_kernel(const BwdArgs A)
+{
+    const LayerArgs &a = A.L;
+    __shared__ __attribute__((aligned(16))) DsqTile ring[DSQ_NS];   // 100 KB
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, c = lane & 31, grp = lane >> 4, il = lane & 15;
+    const int G = a.hq / a.hkv, n_hg = G / 4;
+
+    // ---- work item: KV head fastest, then head group, then query tiles from the last sequence's last tile
+    const int x = blockIdx.x;
+    const int kvh = x % a.hkv;
+    const int hg = (x / a.hkv) % n_hg;
+    int tile = x / a.hkv / n_hg;
+    int seq_start = 0, seq_end = 0, bseq = -1, n = 0;
+    for (int b = a.batch - 1; b >= 0; --b) {
+        seq_start = a.cu[b];
+        seq_end = a.cu[b + 1];
+        const int nq = ds_nq(seq_start, seq_end);
+        if (tile < nq) {
+            bseq = b;
+            n = nq - 1 - tile;
+            break;
+        }
+        tile -= nq;
+    }
+    if (bseq < 0) return;
+    const int q0 = (seq_start & ~15) + 32 * n;
+    const int h = kvh * G + hg * 4 + wave;
+    const int klo = ds_klo(q0, seq_start, a.window);
+    const int khi = min(q0 + 31 - seq_start, seq_end - 1 - seq_start) >> 5;
+    const int nsteps = khi - klo + 1;
+    const int64_t blk0 = (int64_t)h * A.ds_index[a.batch] + A.ds_index[bseq] + ds_rows_before(n, a.window);
+    const u16 *ds_row = A.ds + blk0 * 1024;
+
+    // ---- loads of one key block: k' rows (swizzled 16-byte chunks) and this wave's dS block
+    const size_t kr_row = (size_t)a.hkv * DQK;
+    uint32_t o_kr[DSQ_KL];
+#pragma unroll
+    for (int j = 0; j < DSQ_KL; ++j) {
+        const int slot = 256 * j + tid, r = slot / KCH, p = slot % KCH;
+        o_kr[j] = (uint32_t)((r * kr_row + 8 * (p ^ (((r >> 1) & 1) << 2))) * 2);
+    }
+    auto issue = [&](int step, DsqTile &T) {
+        const int kb = seq_start + 32 * (klo + step);
+        const u16 *bk = A.W.kr + ((size_t)kb * a.hkv + kvh) * DQK;
+#pragma unroll
+        for (int j = 0; j < DSQ_KL; ++j) lds_dma16(bk, o_kr[j], T.kr + 256 * j + 64 * wave);
+        // (a block index past the workspace only arises from a max_seqlen below the truth: read block 0)
+        const u16 *bd = blk0 + step < A.ds_cap ? ds_row + (size_t)step * 1024 : A.ds;
+        lds_dma16_nt(bd, (uint32_t)(16 * lane), T.ds[wave]);
+        lds_dma16_nt(bd, (uint32_t)(16 * (64 + lane)), T.ds[wave] + 64);
+    };
+
+    // ---- per-lane parts of the transposed reads.  This lane supplies row (4 hh + t) of a 16-key step for
+    // t = il / 4, m = il % 4: k' read r covers dims 32 i + 16 (grp & 1) + 4 m .. + 3 of key 16 s + 8 r + 4 hh +
+    // t; the dS read covers queries 16 (grp & 1) + 4 m .. + 3 of that key (row key + 32 (m & 1) of the block,
+    // its halves swapped when m & 1).
+    const int t4 = il >> 2, m4 = il & 3;
+    const int krow = 4 * hh + t4;
+    const int ksw = ((krow >> 1) & 1) << 2;
+    const int kq = 2 * (grp & 1) + (m4 >> 1);                           // chunk within the 4-chunk block i
+    const int a_even = krow * KCH * 16 + ((kq ^ ksw) * 16) + 8 * (m4 & 1);        // dim block i even
+    const int a_odd = krow * KCH * 16 + (((4 + kq) ^ ksw) * 16) + 8 * (m4 & 1);   // dim block i odd (i - 1)
+    // dS read r of k-step s: plane grp & 1, row (key + 32 hq) ^ 8 hq ^ 4 (grp & 1) with hq = m4 & 1, key =
+    // 16 s + 8 r + krow, 8-byte half m4 >> 1 of the 16-byte row
+    const int hq_ = m4 & 1, pl = grp & 1;
+    const int b_off0 = pl * 1024 + (32 * hq_ + 8 * hq_ + (krow ^ (4 * pl))) * 16 + 8 * (m4 >> 1);
+    const int b_off1 = pl * 1024 + (32 * hq_ + 8 * (1 - hq_) + (krow ^ (4 * pl))) * 16 + 8 * (m4 >> 1);
+
+    f32x16 dq[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) dq[i] = f32x16{};
+
+    auto compute = [&](const DsqTile &T) {
+        const char *kb = (const char *)T.kr, *db = (const char *)T.ds[wave];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int rs = 16 * s;   // first key row of the k-step
+            const bf16x8 bop = tr_pair(db + b_off0 + rs * 16, db + b_off1 + rs * 16);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int ao = (i & 1 ? a_odd : a_even) + 64 * (i & ~1);
+                const bf16x8 aop = tr_pair(kb + ao + rs * KCH * 16, kb + ao + (rs + 8) * KCH * 16);
+                dq[i] = mfma32(aop, bop, dq[i]);
+            }
+        }
+    };
+
+    // ---- ring of DSQ_NS buffers, four block loads in flight: at stage st wait until block st landed (the
+    // three newer sets may still be in flight), barrier (every wave landed its part and finished stage
+    // st-1, whose buffer the next load refills), load block st+4, compute block st.  Every stage loads one
+    // set (the last block again once the blocks run out), so the waits stay uniform.  The buffer index is a
+    // run-time value (one loop body for all stages).
+    issue(0, ring[0]);
+    issue(min(1, nsteps - 1), ring[1]);
+    issue(min(2, nsteps - 1), ring[2]);
+    issue(min(3, nsteps - 1), ring[3]);
+    int cur = 0;
+    for (int st = 0; st < nsteps; ++st) {
+        const int fill = cur == 0 ? DSQ_NS - 1 : cur - 1;
+        wait_vmcnt<3 * DSQ_LOADS>();
+        __builtin_amdgcn_s_barrier();
+        issue(min(st + 4, nsteps - 1), ring[fill]);
+        compute(ring[cur]);
+        cur = cur == DSQ_NS - 1 ? 0 : cur + 1;
+    }
+    wait_vmcnt<0>();
+
+    // ---- epilogue: dq = R^T dQ^T / sqrt(192) for this lane's query
+    const int qt = q0 + c;
+    if (qt >= seq_start && qt < seq_end) {
+        const float2 *qcs = a.rope + (size_t)min(qt - seq_start, a.rope_len - 1) * NHALF;
+        rope_back(dq[0], dq[1], qcs, hh);
+        u16 *dqp = A.dq + ((size_t)qt * a.hq + h) * DQK + 4 * hh;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                bf16x4 w;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) w[t] = f2bf(dq[i][4 * jj + t] * RSQRT_DQK);
+                *(uint2 *)(dqp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+            }
+        }
+    }
+}
+
 template <int GP>
 hipError_t launch_dq(const BwdArgs &A, hipStream_t stream)
 {
@@ -769,8 +992,9 @@ hipError_t launch_zero_f32(float *p, int n, hipStream_t stream)
     return hipGetLastError();
 }
 
-// workspace: lse2 and D [hq, T_pad] fp32, q' [T_pad, hq, 192], q'^T [hq, 192, T_pad], dO^T [hq, 128, T_pad],
-// k' [T_pad, hkv, 192], k'^T [hkv, 192, T_pad] (bf16), each 256-byte aligned
+// workspace: lse2 and D [hq, T_pad] fp32, q' [T_pad, hq, 192], k' [T_pad, hkv, 192], k'^T [hkv, 192, T_pad]
+// (bf16), dk|dv partials when splits > 1, and for the stored-dS path the block index and the dS blocks; each
+// part 256-byte aligned
 // Causal layers with large groups split each key tile's query heads over several workgroups, so that the
 // first key tiles of a long sequence (which every later query sees) do not set the kernel's length alone.
 static int dkv_splits(int hq, int hkv, int window)
@@ -786,11 +1010,29 @@ size_t bwd_workspace_bytes(int T, int hq, int hkv, int window)
 {
     const size_t tp = (size_t)prep_tpad(T);
     const int sp = dkv_splits(hq, hkv, window);
-    return 2 * al(tp * hq * 4) + al(tp * hq * DQK * 2) + al(tp * hq * DQK * 2) + al(tp * hq * DVV * 2) +
-           al(tp * hkv * DQK * 2) + al(tp * hkv * DQK * 2) + (sp > 1 ? al((size_t)sp * tp * hkv * (DQK + DVV) * 4) : 0);
+    return 2 * al(tp * hq * 4) + al(tp * hq * DQK * 2) + al(tp * hkv * DQK * 2) + al(tp * hkv * DQK * 2) +
+           (sp > 1 ? al((size_t)sp * tp * hkv * (DQK + DVV) * 4) : 0);
 }
 
-void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A)
+// Stored-dS path: an upper bound on the dS blocks of one head, from the total tokens T, the number of
+// sequences and the longest one.  A sequence of L tokens has nq <= L / 32 + 1.44 query tiles; causal rows
+// hold nq (nq + 1) / 2 blocks (sum of L^2 <= T max_seqlen), sliding-window rows nq row-width blocks.
+static int64_t ds_blocks_bound(int T, int window, int batch, int max_seqlen)
+{
+    const int64_t t32 = (int64_t)T / 32 + 1;
+    if (window >= 0) return (t32 + 2 * (int64_t)batch + 1) * ds_row_width(window);
+    return ((int64_t)T * max_seqlen / 1024 + 4 * t32 + 4 * (int64_t)batch) / 2 + (int64_t)batch + 1;
+}
+
+// Only where the dQ kernel of the stored-dS path applies: query heads in groups of four per KV head.
+size_t bwd_workspace_bytes_ds(int T, int hq, int hkv, int window, int batch, int max_seqlen)
+{
+    if (hq % hkv || (hq / hkv) % 4 || T <= 0) return 0;
+    const int64_t blocks = ds_blocks_bound(T, window, batch, max_seqlen);
+    return bwd_workspace_bytes(T, hq, hkv, window) + al((size_t)(batch + 1) * 8) + al((size_t)hq * blocks * 2048);
+}
+
+void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A, bool stored_ds, int batch, int max_seqlen)
 {
     const size_t tp = (size_t)prep_tpad(T);
     char *p = (char *)ws;
@@ -801,16 +1043,21 @@ void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A)
     p += al(tp * hq * 4);
     A->W.qr = (u16 *)p;
     p += al(tp * hq * DQK * 2);
-    A->W.qrt = (u16 *)p;
-    p += al(tp * hq * DQK * 2);
-    A->W.dot = (u16 *)p;
-    p += al(tp * hq * DVV * 2);
     A->W.kr = (u16 *)p;
     p += al(tp * hkv * DQK * 2);
     A->W.krt = (u16 *)p;
     p += al(tp * hkv * DQK * 2);
     A->splits = dkv_splits(hq, hkv, A->L.window);
     A->dkv_part = A->splits > 1 ? (float *)p : nullptr;
+    if (A->splits > 1) p += al((size_t)A->splits * tp * hkv * (DQK + DVV) * 4);
+    A->ds = nullptr;
+    A->ds_index = nullptr;
+    if (stored_ds) {
+        A->ds_index = (int64_t *)p;
+        p += al((size_t)(batch + 1) * 8);
+        A->ds = (u16 *)p;
+        (void)max_seqlen;
+    }
 }
 
 hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
@@ -832,11 +1079,7 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     trace_begin(a.window >= 0 ? "bwd_prep_q_swa" : "bwd_prep_q_global", stream);
-    e = launch_row_prep<DQK, true>(a.q, a.hq, A.W.qr, A.W.qrt, a, A.T_pad, stream);
-    trace_end(stream);
-    if (e != hipSuccess) return e;
-    trace_begin(a.window >= 0 ? "bwd_prep_dout_swa" : "bwd_prep_dout_global", stream);
-    e = launch_row_prep<DVV, false>(A.dout, a.hq, nullptr, A.W.dot, a, A.T_pad, stream);
+    e = launch_row_prep<DQK, true>(a.q, a.hq, A.W.qr, nullptr, a, A.T_pad, stream);
     trace_end(stream);
     if (e != hipSuccess) return e;
     trace_begin(a.window >= 0 ? "bwd_prep_k_swa" : "bwd_prep_k_global", stream);
@@ -844,6 +1087,13 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     trace_end(stream);
     if (e != hipSuccess) return e;
 
+    if (A.ds) {
+        trace_begin(a.window >= 0 ? "bwd_ds_index_swa" : "bwd_ds_index_global", stream);
+        bwd_ds_index_kernel<<<1, 256, 0, stream>>>(A);
+        trace_end(stream);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const long kv_tiles = (long)(a.T + NKB - 1) / NKB + a.batch;
     const long kv_grid = kv_tiles * a.hkv * A.splits;
     if (kv_grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
@@ -862,6 +1112,15 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     const int G = a.hq / a.hkv;
+    if (A.ds) {
+        const long grid = ((long)a.T / 32 + 2L * a.batch) * (G / 4) * a.hkv;
+        if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        trace_begin(a.window >= 0 ? "bwd_dq_ds_swa" : "bwd_dq_ds_global", stream);
+        if (a.window >= 0) bwd_dq_ds_kernel<true><<<(unsigned)grid, 256, 0, stream>>>(A);
+        else bwd_dq_ds_kernel<false><<<(unsigned)grid, 256, 0, stream>>>(A);
+        trace_end(stream);
+        return hipGetLastError();
+    }
     if (G % 8 == 0) return launch_dq<8>(A, stream);
     if (G % 4 == 0) return launch_dq<4>(A, stream);
     if (G % 2 == 0) return launch_dq<2>(A, stream);

@@ -77,6 +77,16 @@ __device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, void
                  : "memory", "m0");
 }
 
+// The same with the non-temporal hint, for data read once (keeps it from displacing reused lines in L2).
+__device__ __forceinline__ void lds_dma16_nt(const void *sbase, uint32_t voff, void *lds_wave_base)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector-memory loads are still in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -93,6 +103,26 @@ __device__ __forceinline__ int swz384(int r, int q) { return (q & ~7) | ((q & 7)
 __device__ __forceinline__ int swz256(int r, int q) { return q ^ (r & 15); }
 __device__ __forceinline__ int swz128(int r, int q) { return q ^ ((r >> 1) & 7); }
 __device__ __forceinline__ int swz64(int r, int q) { return q ^ ((r >> 2) & 3); }
+// Swizzles for tiles that are also read transposed with ds_read_b64_tr_b16 (16 lanes read 4 consecutive
+// rows x 4 consecutive chunk halves; a half-wave of such reads must cover all 64 banks once): the XOR
+// term moves rows r and r + 2 into different 4-chunk groups while keeping the 16-row row reads above
+// conflict-free.  384-byte rows (24 chunks, XOR inside groups of 8) and 256-byte rows.
+__device__ __forceinline__ int swz384t(int r, int q) { return (q & ~7) | ((q & 7) ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))); }
+__device__ __forceinline__ int swz256t(int r, int q) { return q ^ ((4 * (r & 3) + ((r >> 2) & 3)) & 15); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 4-element row read
+// by lane 4 t + i / 4 as its element t.  Two such reads give an 8-element MFMA operand.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 ld_tr(const void *lds_addr)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(lds_void *)lds_addr);
+}
+__device__ __forceinline__ bf16x8 tr_pair(const char *p0, const char *p1)
+{
+    const s16x4 x = ld_tr(p0), y = ld_tr(p1);
+    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+    return __builtin_bit_cast(bf16x8, make_uint4(ux.x, ux.y, uy.x, uy.y));
+}
 
 // Rotate-half RoPE of one 8-wide chunk pair: x0 holds dims d..d+7 (d < 32), x1 dims d+32..d+39, cs the
 // (cos, sin) of the 8 matching frequencies.  Rounded back to bf16 (the MFMA operand precision).

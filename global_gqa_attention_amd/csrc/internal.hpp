@@ -35,8 +35,6 @@ struct FwdArgs {
 // DMA-ready copies the backward prepares in its workspace (see attn_bwd.hip).
 struct BwdPrep {
     uint16_t *qr;                  // bf16 [T_pad, hq, 192]   q with RoPE applied
-    uint16_t *qrt;                 // bf16 [hq, 192, T_pad]   the same, transposed (token chunks permuted)
-    uint16_t *dot;                 // bf16 [hq, 128, T_pad]   dO transposed (token chunks permuted)
     uint16_t *kr;                  // bf16 [T_pad, hkv, 192]  k with RoPE applied
     uint16_t *krt;                 // bf16 [hkv, 192, T_pad]  the same, transposed
 };
@@ -53,8 +51,14 @@ struct BwdArgs {
     float *dkv_part;               // workspace: fp32 dk|dv partials [splits, T_pad, hkv, 320] (splits > 1)
     int T_pad;
     int splits;                    // query heads of a group are split over this many key-tile workgroups
+    // stored-dS path (nullptr: dQ recomputes S and dP): the dK/dV kernel writes every 32 x 32 bf16 block of
+    // dS it computes, the dQ kernel reads them back.  ds_index[b] = first block of sequence b within a head,
+    // ds_index[batch] = blocks per head.
+    uint16_t *ds;
+    int64_t *ds_index;
+    int64_t ds_cap;                // blocks that fit in the workspace (guards a max_seqlen below the truth)
 };
-void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A);
+void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A, bool stored_ds, int batch, int max_seqlen);
 
 struct DecodeArgs {
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
@@ -87,6 +91,7 @@ bool decode_group_supported(int group);
 
 size_t fwd_workspace_bytes(int T, int hq, int hkv, int window);
 size_t bwd_workspace_bytes(int T, int hq, int hkv, int window);
+size_t bwd_workspace_bytes_ds(int T, int hq, int hkv, int window, int batch, int max_seqlen);   // 0: not available
 size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window);
 void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window, int *splits, int *split_len);
 

@@ -75,9 +75,20 @@ mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const f
 size_t mimo_attn_fwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
                                     int32_t window);
 
-/* Bytes of device workspace mimo_attn_bwd needs for these sizes (0 is never returned for valid sizes). */
+/* Least bytes of device workspace mimo_attn_bwd needs for these sizes (0 is never returned for valid
+ * sizes).  With this much the dq kernel recomputes the scores and dP of every (query, key) pair. */
 size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
                                     int32_t window);
+
+/* Bytes of device workspace for the faster backward: the dk/dv kernel keeps every 32 x 32 block of dS it
+ * computes (bf16, in the workspace) and the dq kernel reads them back instead of recomputing them.  The
+ * size is an upper bound from total_tokens, batch and max_seqlen (causal layers: about
+ * n_q_heads * total_tokens * max_seqlen bytes; sliding-window layers: n_q_heads * total_tokens * 384 bytes
+ * for window 128).  Equals mimo_attn_bwd_workspace_size() where this path does not apply (n_q_heads /
+ * n_kv_heads not a multiple of 4).  mimo_attn_bwd takes this path whenever workspace_bytes reaches this
+ * size; both paths give the same gradients up to fp32 summation order. */
+size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, int32_t max_seqlen,
+                                         int32_t n_q_heads, int32_t n_kv_heads, int32_t window);
 
 /* Backward of mimo_attn_fwd (the training backward, "given the forward outputs").
  *   q, k, v, sink, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base, heads: as the forward
@@ -88,8 +99,11 @@ size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int
  *   dk    bf16 [total_tokens, n_kv_heads, 192] gradient w.r.t. the un-rotated k (summed over the group)
  *   dv    bf16 [total_tokens, n_kv_heads, 128] gradient w.r.t. the unscaled v (summed over the group)
  *   dsink fp32 [n_q_heads] gradient of the sink logits; must be non-NULL exactly when sink is non-NULL
- *   workspace: device memory of at least mimo_attn_bwd_workspace_size() bytes, owned by the caller,
- *   needs no initialisation, and must not be shared with a concurrent call.
+ *   workspace: device memory of at least mimo_attn_bwd_workspace_size() bytes (at least
+ *   mimo_attn_bwd_workspace_size_fast() bytes selects the stored-dS path), owned by the caller, needs no
+ *   initialisation, and must not be shared with a concurrent call.  max_seqlen must not be below the longest
+ *   sequence (the stored-dS path sizes its blocks by it; a smaller value gives wrong gradients, never an
+ *   access outside the workspace).
  * dsink is summed in a fixed order (no float atomics), so it is bitwise repeatable.
  * Source: the exact gradient of the forward above; miles docs "MiMo-V2.6-Flash" section 5.4 (the trainer's
  * fused attention carries the sink in training). */

@@ -28,7 +28,7 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_fwd_workspace_size",
-              "mimo_attn_bwd_workspace_size",
+              "mimo_attn_bwd_workspace_size", "mimo_attn_bwd_workspace_size_fast",
               "mimo_attn_decode_workspace_size", "mimo_attn_status_string", "mimo_attn_last_error",
               "mimo_attn_release"):
         assert n in names
@@ -91,6 +91,43 @@ def test_workspace_sizes(L):
     assert n >= 32768 * 64 * 4
     assert L.mimo_attn_decode_workspace_size(64, 131072, 64, -1) > 0
     assert L.mimo_attn_bwd_workspace_size(-1, 64, 8, 128) == 0
+
+
+def _ds_blocks_per_head(lengths, window):
+    """dS blocks of one head as the stored-dS layout lays them out: sequence b has nq query tiles of 32 that
+    start at seq_start & ~15; causal rows hold n + 1 blocks, sliding-window rows (window + 62) // 32 + 1."""
+    tot, start = 0, 0
+    for L_ in lengths:
+        nq = (start + L_ - 1 - (start & ~15)) // 32 + 1 if L_ > 0 else 0
+        tot += nq * ((window + 62) // 32 + 1) if window >= 0 else nq * (nq + 1) // 2
+        start += L_
+    return tot
+
+
+@pytest.mark.parametrize("window", [-1, 128, 0])
+def test_fast_bwd_workspace_covers_every_batch(L, window):
+    import numpy as np
+
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        batch = int(rng.integers(1, 40))
+        lengths = [int(x) for x in rng.integers(0, 3000, size=batch)]
+        if rng.random() < 0.3:
+            lengths[int(rng.integers(batch))] = int(rng.integers(3000, 40000))
+        T, maxl = sum(lengths), max(lengths)
+        if T == 0:
+            continue
+        base = L.mimo_attn_bwd_workspace_size(T, 64, 4, window)
+        fast = L.mimo_attn_bwd_workspace_size_fast(T, batch, maxl, 64, 4, window)
+        need = 64 * _ds_blocks_per_head(lengths, window) * 2048 + (batch + 1) * 8
+        assert fast >= base + need, (lengths, window)
+
+
+def test_fast_bwd_workspace_falls_back_for_other_groups(L):
+    # the stored-dS dQ kernel takes query heads four at a time: other group sizes keep the least size
+    assert L.mimo_attn_bwd_workspace_size_fast(4096, 2, 4096, 6, 2, -1) == L.mimo_attn_bwd_workspace_size(4096, 6, 2, -1)
+    assert L.mimo_attn_bwd_workspace_size_fast(4096, 2, 4096, 64, 4, -1) > L.mimo_attn_bwd_workspace_size(4096, 64, 4, -1)
+    assert L.mimo_attn_bwd_workspace_size_fast(-1, 2, 4096, 64, 4, -1) == 0
 
 
 def test_decode_rejects_bad_arguments(L):

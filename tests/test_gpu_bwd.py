@@ -3,6 +3,8 @@
 The backward is given the forward outputs; both sides receive the same O (the oracle's forward rounded to
 bf16) and LSE (rounded to fp32), so D = rowsum(dO * O) uses the same O on both sides.  dq/dk/dv: max-abs
 2e-2 (widened by a bf16 half-ulp of |ref| where |ref| >= 8), mean-abs 2e-3; dsink: 1e-2 relative per head.
+Both backward paths run: "fast" (a workspace that keeps the dS blocks, which the dQ kernel reads back) and
+"least" (the least workspace: dQ recomputes S and dP).
 """
 import numpy as np
 import pytest
@@ -29,11 +31,18 @@ def _given_outputs(d, rows=None):
     return torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(l).to(torch.float32)
 
 
-def _run_bwd(ga, d, O, L, dO):
+def _run_bwd(ga, d, O, L, dO, path="fast"):
     dev = "cuda"
     sink = None if d["sink"] is None else d["sink"].to(dev)
+    T, hq, hkv = d["q"].shape[0], d["q"].shape[1], d["k"].shape[1]
+    maxl = max(d["lengths"] + [1])
+    if path == "fast":
+        n = ga.bwd_workspace_size(T, hq, hkv, d["window"], len(d["lengths"]), maxl)
+    else:
+        n = ga.bwd_workspace_size(T, hq, hkv, d["window"])
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     g = ga.bwd(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), sink, O.to(dev), L.to(dev), dO.to(dev),
-               d["cu_seqlens"].to(dev), max(d["lengths"] + [1]), d["window"], d["rope_base"])
+               d["cu_seqlens"].to(dev), maxl, d["window"], d["rope_base"], workspace=ws)
     torch.cuda.synchronize()
     return [None if x is None else x.cpu() for x in g]
 
@@ -46,15 +55,17 @@ def _run_bwd(ga, d, O, L, dO):
     ([70, 33, 257], 16, 8, 0, 1e4, True),
     ([100, 29], 12, 4, 40, 1e4, True),
     ([100, 29], 8, 1, -1, 1e4, False),
+    ([33, 1, 31, 47, 16, 17], 32, 8, 3, 1e4, True),
 ])
-def test_bwd_small_full(lengths, hq, hkv, window, base, sink):
+@pytest.mark.parametrize("path", ["fast", "least"])
+def test_bwd_small_full(lengths, hq, hkv, window, base, sink, path):
     ga = _gpu()
     d = mi.make_layer(lengths, hq, hkv, 9, sink)
     d.update(window=window, rope_base=base)
-    print(f"case lengths={lengths} hq={hq} hkv={hkv} window={window} sink={sink}", flush=True)
+    print(f"case lengths={lengths} hq={hq} hkv={hkv} window={window} sink={sink} path={path}", flush=True)
     O, L = _given_outputs(d)
     dO = mi.dout_like(sum(lengths), 4, hq)
-    dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO)
+    dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO, path)
     rq, rk, rv, rs = oracle.prefill_bwd(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], window, base,
                                         out_given=O)
     compare("dq", dq, rq, bf16_halfulp=True)
@@ -66,19 +77,28 @@ def test_bwd_small_full(lengths, hq, hkv, window, base, sink):
         assert ds is None
 
 
-def test_bwd_deterministic():
+@pytest.mark.parametrize("window,sink", [(128, True), (-1, False)])
+def test_bwd_deterministic_and_paths_agree(window, sink):
+    """Each path is bitwise repeatable; dk, dv and dsink come from the same kernels on both paths (the fast
+    one only also keeps dS), so they agree bitwise; dq agrees to fp32 summation order."""
     ga = _gpu()
-    d = mi.make_layer([700, 333], 64, 8, 10, True)
-    d.update(window=128, rope_base=1e4)
+    d = mi.make_layer([700, 333, 95], 64, 8 if window >= 0 else 4, 10, sink)
+    d.update(window=window, rope_base=1e4)
     O, L = _given_outputs(d)
-    dO = mi.dout_like(1033, 4)
-    a = _run_bwd(ga, d, O, L, dO)
-    b = _run_bwd(ga, d, O, L, dO)
+    dO = mi.dout_like(1128, 4)
+    print(f"case paths window={window}", flush=True)
+    a = _run_bwd(ga, d, O, L, dO, "fast")
+    b = _run_bwd(ga, d, O, L, dO, "fast")
+    c = _run_bwd(ga, d, O, L, dO, "least")
     for x, y in zip(a, b):
-        assert torch.equal(x, y)
+        assert (x is None and y is None) or torch.equal(x, y)
+    for x, y in zip(a[1:], c[1:]):
+        assert (x is None and y is None) or torch.equal(x, y)
+    diff = (a[0].float() - c[0].float()).abs()
+    assert float(diff.max()) <= 2e-2 and float(diff.mean()) <= 1e-4, (float(diff.max()), float(diff.mean()))
 
 
-def _sampled_bwd(ga, d, dO, nq, nk, heads, seed):
+def _sampled_bwd(ga, d, dO, nq, nk, heads, seed, path="fast"):
     """Full-size backward: the oracle computes the forward rows it needs, and then sampled dq rows, dk/dv rows
     near the ends of sequences (few queries see them under causal attention), and dsink for a few heads."""
     rng = np.random.default_rng(seed)
@@ -90,7 +110,7 @@ def _sampled_bwd(ga, d, dO, nq, nk, heads, seed):
     o, l = oracle.prefill_rows(d["q"], d["k"], d["v"], d["sink"], d["cu_seqlens"], d["window"], d["rope_base"])
     O[:] = torch.from_numpy(o.reshape(T, hq, 128)).to(torch.bfloat16)
     L[:] = torch.from_numpy(l.reshape(T, hq).T.copy()).to(torch.float32)
-    dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO)
+    dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO, path)
     qrows = rng.integers(0, T * hq, nq)
     rq = oracle.bwd_dq_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"], d["rope_base"],
                             qrows, out_given=O)
@@ -121,11 +141,12 @@ def test_bwd_thd_32k_swa_sampled():
     _sampled_bwd(ga, d, dO, 400, 60, [0, 17, 40, 63], 3)
 
 
-def test_bwd_global_small_batch_sampled():
+@pytest.mark.parametrize("path", ["fast", "least"])
+def test_bwd_global_small_batch_sampled(path):
     """Global layer on a 2 x 2048 batch (the oracle's full forward stays fast): sampled rows."""
     ga = _gpu()
     d = mi.make_layer([2048, 1999], 64, 4, 11, False)
     d.update(window=-1, rope_base=1e7)
     dO = mi.dout_like(4047, 4)
-    print("case global 2048+1999 bwd", flush=True)
-    _sampled_bwd(ga, d, dO, 300, 40, [], 4)
+    print(f"case global 2048+1999 bwd path={path}", flush=True)
+    _sampled_bwd(ga, d, dO, 300, 40, [], 4, path)
