@@ -812,25 +812,27 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
 //     8 hh + 4 r + t of read r (0, 1) stands for key 16 s + 8 r + 4 hh + t in both operands.
 // ------------------------------------------------------------------------------------------------------
 constexpr int DSQ_NS = 5;                // ring stages (four block loads in flight: the kernel streams HBM)
-constexpr int DSQ_KL = 32 * KCH / 256;   // k' DMAs per thread per block (3)
-constexpr int DSQ_LOADS = DSQ_KL + 2;    // + this wave's dS block (2 KB: two per lane)
 
+// NH waves per workgroup, one query head each: the NH heads share every k' tile (the k' rows are loaded
+// by the first 768 / 128 = 6 waves, two chunks per lane; every wave loads its own dS block)
+template <int NH>
 struct DsqTile {
     uint4 kr[32 * KCH];                  // k' rows, 16-byte chunk q of row r at q ^ (4 ((r >> 1) & 1))
-    uint4 ds[4][128];                    // one stored dS block per wave
+    uint4 ds[NH][128];                   // one stored dS block per wave
 };
 
-
-template <bool WIN>
-__global__ __launch_bounds__(256, 1) void bwd_dq_ds_kernel(const BwdArgs A)
+template <int NH, bool WIN>
+__global__ __launch_bounds__(64 * NH, 1) void bwd_dq_ds_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
-    __shared__ __attribute__((aligned(16))) DsqTile ring[DSQ_NS];   // 100 KB
+    constexpr int KL = NH == 4 ? 3 : 2;                  // k' DMAs per lane of a loading wave
+    constexpr int KW = 32 * KCH / (64 * KL);             // waves that load k' (4 or 6)
+    __shared__ __attribute__((aligned(16))) DsqTile<NH> ring[DSQ_NS];   // 100 KB (4 heads) / 140 KB (8)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c = lane & 31, grp = lane >> 4, il = lane & 15;
-    const int G = a.hq / a.hkv, n_hg = G / 4;
+    const int G = a.hq / a.hkv, n_hg = G / NH;
 
     // ---- work item: KV head fastest, then head group, then query tiles from the last sequence's last tile
     const int x = blockIdx.x;
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_ds_kernel(const BwdArgs A)
     }
     if (bseq < 0) return;
     const int q0 = (seq_start & ~15) + 32 * n;
-    const int h = kvh * G + hg * 4 + wave;
+    const int h = kvh * G + hg * NH + wave;
     const int klo = ds_klo(q0, seq_start, a.window);
     const int khi = min(q0 + 31 - seq_start, seq_end - 1 - seq_start) >> 5;
     const int nsteps = khi - klo + 1;
@@ -860,17 +862,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_ds_kernel(const BwdArgs A)
 
     // ---- loads of one key block: k' rows (swizzled 16-byte chunks) and this wave's dS block
     const size_t kr_row = (size_t)a.hkv * DQK;
-    uint32_t o_kr[DSQ_KL];
+    uint32_t o_kr[KL];
 #pragma unroll
-    for (int j = 0; j < DSQ_KL; ++j) {
-        const int slot = 256 * j + tid, r = slot / KCH, p = slot % KCH;
+    for (int j = 0; j < KL; ++j) {
+        const int slot = 64 * KW * j + 64 * min(wave, KW - 1) + lane, r = slot / KCH, p = slot % KCH;
         o_kr[j] = (uint32_t)((r * kr_row + 8 * (p ^ (((r >> 1) & 1) << 2))) * 2);
     }
-    auto issue = [&](int step, DsqTile &T) {
+    auto issue = [&](int step, DsqTile<NH> &T) {
         const int kb = seq_start + 32 * (klo + step);
         const u16 *bk = A.W.kr + ((size_t)kb * a.hkv + kvh) * DQK;
+        if (wave < KW) {
 #pragma unroll
-        for (int j = 0; j < DSQ_KL; ++j) lds_dma16(bk, o_kr[j], T.kr + 256 * j + 64 * wave);
+            for (int j = 0; j < KL; ++j) lds_dma16(bk, o_kr[j], T.kr + 64 * KW * j + 64 * wave);
+        }
         // (a block index past the workspace only arises from a max_seqlen below the truth: read block 0)
         const u16 *bd = blk0 + step < A.ds_cap ? ds_row + (size_t)step * 1024 : A.ds;
         lds_dma16_nt(bd, (uint32_t)(16 * lane), T.ds[wave]);
@@ -897,7 +901,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_ds_kernel(const BwdArgs A)
 #pragma unroll
     for (int i = 0; i < 6; ++i) dq[i] = f32x16{};
 
-    auto compute = [&](const DsqTile &T) {
+    auto compute = [&](const DsqTile<NH> &T) {
         const char *kb = (const char *)T.kr, *db = (const char *)T.ds[wave];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -924,7 +928,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_ds_kernel(const BwdArgs A)
     int cur = 0;
     for (int st = 0; st < nsteps; ++st) {
         const int fill = cur == 0 ? DSQ_NS - 1 : cur - 1;
-        wait_vmcnt<3 * DSQ_LOADS>();
+        // loads per stage: KL + 2 for the k'-loading waves, 2 for the others
+        if (wave < KW) wait_vmcnt<3 * (KL + 2)>();
+        else wait_vmcnt<3 * 2>();
         __builtin_amdgcn_s_barrier();
         issue(min(st + 4, nsteps - 1), ring[fill]);
         compute(ring[cur]);
@@ -1113,11 +1119,14 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     }
     const int G = a.hq / a.hkv;
     if (A.ds) {
-        const long grid = ((long)a.T / 32 + 2L * a.batch) * (G / 4) * a.hkv;
+        const int nh = G % 8 == 0 ? 8 : 4;
+        const long grid = ((long)a.T / 32 + 2L * a.batch) * (G / nh) * a.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         trace_begin(a.window >= 0 ? "bwd_dq_ds_swa" : "bwd_dq_ds_global", stream);
-        if (a.window >= 0) bwd_dq_ds_kernel<true><<<(unsigned)grid, 256, 0, stream>>>(A);
-        else bwd_dq_ds_kernel<false><<<(unsigned)grid, 256, 0, stream>>>(A);
+        if (nh == 8 && a.window >= 0) bwd_dq_ds_kernel<8, true><<<(unsigned)grid, 512, 0, stream>>>(A);
+        else if (nh == 8) bwd_dq_ds_kernel<8, false><<<(unsigned)grid, 512, 0, stream>>>(A);
+        else if (a.window >= 0) bwd_dq_ds_kernel<4, true><<<(unsigned)grid, 256, 0, stream>>>(A);
+        else bwd_dq_ds_kernel<4, false><<<(unsigned)grid, 256, 0, stream>>>(A);
         trace_end(stream);
         return hipGetLastError();
     }
