@@ -23,10 +23,15 @@
 //     the output accumulator is per lane.  O^T = V^T . P^T takes the score registers as its B operand, with
 //     V^T's 4-key chunks stored in the order the score registers hold the keys.  Q is rotated once in
 //     registers (cos/sin from a table built in fp64).
-//   * Online softmax in base 2 (scale folded into one multiply); the sink starts the running max and sum.
-//     The reference max moves only when a block's max exceeds it by 2^8, so most blocks skip the rescale
-//     of the accumulator (exact either way: numerator and denominator share the reference); the branch is
-//     wave-uniform.  Only blocks that cross a causal, window or sequence boundary evaluate the mask.
+//   * Per 32-key block a wave reads all 12 K operands before its S MFMAs, and the 8 V^T operands right
+//     after them, so the V reads land while the softmax runs; the other wave on the SIMD fills the matrix
+//     pipe meanwhile.
+//   * Online softmax in base 2: p = exp2(s * scale - m) is one fma and one v_exp; probabilities are packed
+//     to bf16 in pairs and the row sum adds exactly those packed values (v_dot2 with ones), so numerator
+//     and denominator agree.  The sink starts the running max and sum.  The reference max moves only when
+//     a block's max exceeds it by 2^8, so most blocks skip the rescale of the accumulator (exact either
+//     way: numerator and denominator share the reference); the branch is wave-uniform.  Only blocks that
+//     cross a causal, window or sequence boundary evaluate the mask (one wave-uniform branch per block).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -36,7 +41,9 @@ namespace {
 constexpr int BN = 64;         // keys per tile
 constexpr int KCH = DQK / 8;   // 16-byte chunks per K row (24)
 constexpr int VCH = BN / 8;    // 16-byte chunks per V^T row (8)
-constexpr float RESCALE_TH = 8.f;         // keep a stale running max until the true one exceeds it by 2^8
+constexpr float RESCALE_TH = 8.f;   // keep a stale running max until the true one exceeds it by 2^8
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // K tile in LDS: row r (key), 24 chunks of 16 B (384-byte rows); V^T tile: row d (dim), 8 chunks.
 __device__ __forceinline__ int kpos(int r, int q) { return swz384(r, q); }
@@ -163,7 +170,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-    // ---- one tile: S^T = K Q^T, online softmax, O^T += V^T P^T (two 32-key blocks)
+    // ---- one tile: S^T = K Q^T, online softmax, O^T += V^T P^T (two 32-key blocks).  The V^T operands of a
+    // block are read before its softmax, so they land while the softmax runs.
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    const uint32_t ub = (uint32_t)(WIN ? min(a.window, qt - seq_start) : qt - seq_start);
     auto compute_tile = [&](int k0, const uint4 *skb, const uint4 *svb) {
         const u16 *kt = (const u16 *)skb;
         const u16 *vtt = (const u16 *)svb;
@@ -172,24 +182,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
             const int kbase = k0 + 32 * kb;
             if (kbase > wkhi || kbase + 31 < wklo) continue;     // no row of this wave sees these 32 keys
             const int kr_ = 32 * kb + c;
+            bf16x8 kop[12];
+#pragma unroll
+            for (int s = 0; s < 12; ++s) kop[s] = ld16(kt + (kr_ * KCH + kpos(kr_, 2 * s + hh)) * 8);
             f32x16 sacc = f32x16{};
 #pragma unroll
-            for (int s = 0; s < 12; ++s)
-                sacc = mfma32(ld16(kt + (kr_ * KCH + kpos(kr_, 2 * s + hh)) * 8), qf[s], sacc);
-            const bool need_mask = (kbase + 31 > wt0) || (kbase < seq_start) || (WIN && kbase < wt1 - a.window);
-            float mx = -INFINITY;
+            for (int s = 0; s < 12; ++s) sacc = mfma32(kop[s], qf[s], sacc);
+            bf16x8 vop[8];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float sv = sacc[j] * a.scale_log2;
-                if (need_mask) {
-                    const int key = kbase + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    const bool ok = key <= qt && key >= seq_start && (!WIN || key >= qt - a.window);
-                    sv = ok ? sv : -INFINITY;
-                }
-                sacc[j] = sv;
-                mx = fmaxf(mx, sv);
+            for (int i = 0; i < 4; ++i) {
+                const int d = 32 * i + c;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) vop[2 * i + s] = ld16(vtt + (d * VCH + vpos(d, 4 * kb + 2 * s + hh)) * 8);
             }
-            mx = pair_max(mx);
+            __builtin_amdgcn_sched_barrier(0);
+            float sv[16];
+            float mxa = -INFINITY, mxb = -INFINITY;
+            const bool need_mask = (kbase + 31 > wt0) || (kbase < seq_start) || (WIN && kbase < wt1 - a.window);
+            if (need_mask) {
+                const int dlt = qt - (kbase + 4 * hh);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int cj = 8 * (j >> 2) + (j & 3);
+                    sv[j] = (uint32_t)(dlt - cj) <= ub ? sacc[j] : -INFINITY;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                mxa = fmaxf(mxa, sv[j]);
+                mxb = fmaxf(mxb, sv[j + 1]);
+            }
+            const float mx = pair_max(fmaxf(mxa, mxb)) * a.scale_log2;
             // lazy rescale: move the reference max only when the block max exceeds it by 2^8; the branch is
             // wave-uniform so the accumulators are touched only when some row needs it
             const bool grow = mx > m_run + RESCALE_TH;
@@ -200,22 +226,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
                 for (int i = 0; i < 4; ++i) o[i] *= alpha;
                 m_run = grow ? mx : m_run;
             }
-            const float mref = m_run == -INFINITY ? 0.f : m_run;
-            float psum = 0.f;
-            bf16x8 pf[2];
+            const float nref = m_run == -INFINITY ? 0.f : -m_run;
+            uint32_t pw[8];
+            float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float p = fast_exp2(sacc[j] - mref);
-                psum += p;
-                pf[j >> 3][j & 7] = f2bf(p);
+            for (int w = 0; w < 8; ++w) {
+                const float p0 = fast_exp2(__builtin_fmaf(sv[2 * w], a.scale_log2, nref));
+                const float p1 = fast_exp2(__builtin_fmaf(sv[2 * w + 1], a.scale_log2, nref));
+                pw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+                if (w & 1) ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), ones, ps1, false);
+                else ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), ones, ps0, false);
             }
-            l_run += psum;
+            l_run += ps0 + ps1;
+            const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+            const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int d = 32 * i + c;
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    o[i] = mfma32(ld16(vtt + (d * VCH + vpos(d, 4 * kb + 2 * s + hh)) * 8), pf[s], o[i]);
+                o[i] = mfma32(vop[2 * i], pf0, o[i]);
+                o[i] = mfma32(vop[2 * i + 1], pf1, o[i]);
             }
         }
     };
