@@ -225,13 +225,10 @@ __global__ __launch_bounds__(256) void row_prep_kernel(const u16 *x, int H, u16 
 // ------------------------------------------------------------------------------------------------------
 // 4. dK, dV (key-major)
 // ------------------------------------------------------------------------------------------------------
-constexpr int NKB = 128;                 // keys per workgroup (32 per wave)
+constexpr int NKB = 128;                 // keys per workgroup (four 32-key blocks)
 constexpr int MQ = 32;                   // queries per step
 constexpr int QCH = DQK / 8;             // 24 chunks per q' row
 constexpr int OCH = DVV / 8;             // 16 chunks per dO row
-constexpr int DK_QR = MQ * QCH / 256;    // DMAs per thread per step: q' rows (3)
-constexpr int DK_OR = MQ * OCH / 256;    // dO rows (2)
-constexpr int DK_LOADS = DK_QR + DK_OR + 1;   // + LSE/D (one per wave)
 constexpr int DK_AHEAD = 4;              // LDS operand reads in flight ahead of the MFMAs
 
 struct DkdvTile {
@@ -239,14 +236,21 @@ struct DkdvTile {
     float ld[2 * MQ];                    // LSE * log2(e) [MQ], then D [MQ]
 };
 
+// Eight waves, two per 32-key block: wave kb (0..3) computes S, P and dV^T += dO^T P of its keys, wave
+// 4 + kb the dP, dS and dK^T += Q'^T dS of the same keys one step later, taking P (fp32) from the first
+// through LDS.
+// Each wave holds half the state (k' or v, dV or dK), so two waves fit on a SIMD and interleave: one's
+// softmax VALU runs under the other's MFMAs.
 template <bool WIN>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
-    __shared__ __attribute__((aligned(16))) DkdvTile t0s, t1s, t2s;   // three-stage ring (121 KB)
+    __shared__ __attribute__((aligned(16))) DkdvTile ring[3];          // tiles of steps st-1, st, st+1
+    __shared__ __attribute__((aligned(16))) float4 pbuf[2][4][256];    // fp32 P of a step: 4 planes x 64 lanes
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int role = wave >> 2, kq = wave & 3;
     const int hh = lane >> 5, c = lane & 31;
     const int G = a.hq / a.hkv;
 
@@ -271,25 +275,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int kb0 = seq_start + tile * NKB;
     const int kb_last = min(kb0 + NKB - 1, seq_end - 1);
 
-    // ---- query steps: tiles of 32 queries from kb0 (aligned down to 16 for the transposed chunk order)
+    // ---- query steps: tiles of 32 queries from kb0 (aligned down to 16: the stored-dS row layout)
     const int q_lo = kb0 & ~15;
     const int q_hi = WIN ? min(seq_end - 1, kb_last + a.window) : seq_end - 1;
     const int nq = (q_hi - q_lo + MQ) / MQ;
     const int nsteps = nq * GS;
 
-    // ---- direct HBM -> LDS loads of one step's tiles: fixed per-lane byte offsets + wave-uniform bases
+    // ---- direct HBM -> LDS loads of one step's tiles (fixed per-lane byte offsets + wave-uniform bases):
+    // q' rows by waves 0..5 (two 16-byte chunks per lane), dO rows by all eight waves (one each), LSE*log2e
+    // and D by waves 6 and 7 (eight lanes each)
     const size_t qr_row = (size_t)a.hq * DQK, o_row = (size_t)a.hq * DVV;
-    uint32_t o_qr[DK_QR], o_or[DK_OR];
+    uint32_t o_qr[2];
 #pragma unroll
-    for (int j = 0; j < DK_QR; ++j) {
-        const int slot = 256 * j + tid, r = slot / QCH, p = slot % QCH;
+    for (int j = 0; j < 2; ++j) {
+        const int slot = 384 * j + 64 * min(wave, 5) + lane, r = slot / QCH, p = slot % QCH;
         o_qr[j] = (uint32_t)((r * qr_row + 8 * swz384t(r, p)) * 2);
     }
-#pragma unroll
-    for (int j = 0; j < DK_OR; ++j) {
-        const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
-        o_or[j] = (uint32_t)((r * o_row + 8 * swz256t(r, p)) * 2);
-    }
+    const int oslot_r = tid / OCH, oslot_p = tid % OCH;
+    const uint32_t o_or = (uint32_t)((oslot_r * o_row + 8 * swz256t(oslot_r, oslot_p)) * 2);
     // step -> (head, query tile): heads outer, query tiles from the sequence end down.  Every key tile of a
     // sequence walks the same absolute query tiles in the same order, so the workgroups running together
     // on an XCD read the same q'/dO tiles and mostly hit in L2.
@@ -297,53 +300,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     auto issue = [&](int step, DkdvTile &T) {
         const int h = kvh * G + split * GS + step / nq;
         const int q0 = step_q0(step);
-        const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
-        const u16 *bo = A.dout + ((size_t)q0 * a.hq + h) * DVV;
+        if (wave < 6) {
+            const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
 #pragma unroll
-        for (int j = 0; j < DK_QR; ++j) lds_dma16(bq, o_qr[j], T.qr + 256 * j + 64 * wave);
+            for (int j = 0; j < 2; ++j) lds_dma16(bq, o_qr[j], T.qr + 384 * j + 64 * wave);
+        }
         if (q0 + MQ <= a.T) {
-#pragma unroll
-            for (int j = 0; j < DK_OR; ++j) lds_dma16(bo, o_or[j], T.orow + 256 * j + 64 * wave);
+            lds_dma16(A.dout + ((size_t)q0 * a.hq + h) * DVV, o_or, T.orow + 64 * wave);
         } else {
             // dO is not padded: rows past its end are clamped to the last row (and masked)
-#pragma unroll
-            for (int j = 0; j < DK_OR; ++j) {
-                const int slot = 256 * j + tid, r = slot / OCH, p = slot % OCH;
-                const int row = min(q0 + r, a.T - 1);
-                lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256t(r, p), T.orow + 256 * j + 64 * wave);
-            }
+            const int row = min(q0 + oslot_r, a.T - 1);
+            lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256t(oslot_r, oslot_p), T.orow + 64 * wave);
         }
-        // LSE*log2e (waves 0, 1) and D (waves 2, 3): 2 x 128 bytes, four lanes of each wave load 16 bytes
-        const float *bld = (wave < 2 ? A.lse2 : A.delta) + (size_t)h * A.T_pad + q0 + 16 * (wave & 1);
-        if (lane < 4) lds_dma16(bld, (uint32_t)(16 * lane), (uint4 *)T.ld + 4 * wave);
+        if (wave >= 6) {
+            const float *bld = (wave == 6 ? A.lse2 : A.delta) + (size_t)h * A.T_pad + q0;
+            if (lane < 8) lds_dma16(bld, (uint32_t)(16 * lane), (uint4 *)T.ld + 8 * (wave - 6));
+        }
     };
 
-    // ---- this lane's key: rotated k and v as B operands
-    const int kw0 = kb0 + 32 * wave;
+    // ---- this wave's keys
+    const int kw0 = kb0 + 32 * kq;
     const int kj = kw0 + c;
     const bool kvalid = kj <= kb_last;
     const int kjl = kvalid ? kj : kb_last;
-    bf16x8 kf[12], vf[8];
-    {
-        const u16 *kp = A.W.kr + ((size_t)kjl * a.hkv + kvh) * DQK + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < 12; ++s) kf[s] = ld16(kp + 16 * s);
-        const u16 *vp = a.v + ((size_t)kjl * a.hkv + kvh) * DVV + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) vf[s] = ld16(vp + 16 * s);
-    }
 
-    f32x16 dk[6], dv[4];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) dk[i] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
-
-    // ---- one step = S, dP (MFMA) -> P, dS (VALU) -> dV, dK (MFMA).  Steps are software-pipelined: the S/dP
-    // products of step st+1 are issued between the softmax instructions of step st, so the MFMA pipe works
-    // while the VALU does; then the dV/dK products of step st follow.
-    //
-    // Which queries of a step does this wave need?  None (skip), all (no mask), or some (mask).
+    // Which queries of a step do these keys need?  None (skip), all (no mask), or some (mask).
     auto visible = [&](int step) {
         const int q0 = step_q0(step);
         return step < nsteps && !(q0 + MQ - 1 < kw0 || kw0 > kb_last || (WIN && q0 > kw0 + 31 + a.window));
@@ -354,194 +335,236 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs A)
     };
     // mask bound: query qi sees this lane's key iff 0 <= qi - kj <= ub.  Lanes past the tile's last key see
     // nothing (their key is moved 2^30 away, so the unsigned test fails): their dK/dV are never written back,
-    // and their dS blocks must hold zeros.  An invisible step is masked, so computing it anyway adds zeros.
+    // and their dS blocks must hold zeros.
     const int ub = !kvalid ? 0 : WIN ? min(a.window, q_hi - kj) : q_hi - kj;
     const int kjm = kvalid ? kj : kj + (1 << 30);
 
-    auto sdp = [&](const DkdvTile &T, f32x16 &sacc, f32x16 &dpacc) {
-        const u16 *qr = (const u16 *)T.qr, *orr = (const u16 *)T.orow;
-        sacc = f32x16{};
-        dpacc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 12; ++s) sacc = mfma32(ld16(qr + (c * QCH + swz384t(c, 2 * s + hh)) * 8), kf[s], sacc);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) dpacc = mfma32(ld16(orr + (c * OCH + swz256t(c, 2 * s + hh)) * 8), vf[s], dpacc);
-    };
-    // ---- the fused step, scheduled by hand: 40 groups, each one MFMA and the LDS read of the operand that
-    // the MFMA DK_AHEAD groups later consumes; groups 0..15 also compute P and dS of one score of step st.
-    // Groups 0..19 are the S/dP products of step st+1 (tiles in nxt), groups 20..39 the dV/dK products of
-    // step st (tiles in cur, with P and dS of step st as B operands).  A scheduling fence closes every
-    // window of four groups: the compiler may interleave the four softmax chains of a window with its
-    // MFMAs, but keeps each read a window ahead of the MFMA that consumes it.
-    // operand k of the fused step: rows of q' / dO (S, dP of step st+1) or, read transposed, their columns
-    // (dV, dK of step st).  Transposed read r of k-step s covers rows 16 s + 8 r + 4 hh + t4 and the four
-    // columns 32 i + 16 (grp & 1) + 4 m4 .. + 3 of the operand's 32-row block i (lane il = 4 t4 + m4).
+    // Transposed operand reads: read r of k-step s covers rows 16 s + 8 r + 4 hh + t4 and the four columns
+    // 32 i + 16 (grp & 1) + 4 m4 .. + 3 of the operand's 32-row block i (lane il = 4 t4 + m4).
     const int grp = lane >> 4, t4 = (lane & 15) >> 2, m4 = lane & 3;
-    auto tr_at = [&](const void *tile, int rowbytes, bool w384, int s, int r, int i) -> const char * {
+    auto tr_at = [&](const void *tile_, int rowbytes, bool w384, int s, int r, int i) -> const char * {
         const int R = 16 * s + 8 * r + 4 * hh + t4;
         const int q = 4 * i + 2 * (grp & 1) + (m4 >> 1);
         const int p = w384 ? swz384t(R, q) : swz256t(R, q);
-        return (const char *)tile + R * rowbytes + 16 * p + 8 * (m4 & 1);
-    };
-    auto load_op = [&](int k, const DkdvTile &cur, const DkdvTile &nxt) -> bf16x8 {
-        if (k < 12) return ld16((const u16 *)nxt.qr + (c * QCH + swz384t(c, 2 * k + hh)) * 8);
-        if (k < 20) return ld16((const u16 *)nxt.orow + (c * OCH + swz256t(c, 2 * (k - 12) + hh)) * 8);
-        if (k < 28) {
-            const int i = (k - 20) >> 1, sk = (k - 20) & 1;
-            return tr_pair(tr_at(cur.orow, OCH * 16, false, sk, 0, i), tr_at(cur.orow, OCH * 16, false, sk, 1, i));
-        }
-        const int i = (k - 28) >> 1, sk = (k - 28) & 1;
-        return tr_pair(tr_at(cur.qr, QCH * 16, true, sk, 0, i), tr_at(cur.qr, QCH * 16, true, sk, 1, i));
-    };
-    auto fused = [&](int q0, uint32_t uba, const DkdvTile &cur, const DkdvTile &nxt, const f32x16 &s0,
-                     const f32x16 &d0, f32x16 &s1, f32x16 &d1, bf16x8 *pb, bf16x8 *sb) {
-        const int base = q0 - kjm;   // qi - kj of this lane's first row
-        float4 L4[4], D4[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            L4[jj] = *(const float4 *)(cur.ld + 8 * jj + 4 * hh);
-            D4[jj] = *(const float4 *)(cur.ld + MQ + 8 * jj + 4 * hh);
-        }
-        constexpr int R = 2 * DK_AHEAD;
-        bf16x8 ob[R];
-#pragma unroll
-        for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, cur, nxt);
-        s1 = f32x16{};
-        d1 = f32x16{};
-        float pf[16], df[16];
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < 40; ++k) {
-            if (k < 12) s1 = mfma32(ob[k % R], kf[k], s1);
-            else if (k < 20) d1 = mfma32(ob[k % R], vf[k - 12], d1);
-            else if (k < 28) dv[(k - 20) >> 1] = mfma32(ob[k % R], pb[(k - 20) & 1], dv[(k - 20) >> 1]);
-            else dk[(k - 28) >> 1] = mfma32(ob[k % R], sb[(k - 28) & 1], dk[(k - 28) >> 1]);
-            if (k + DK_AHEAD < 40) ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, cur, nxt);
-            if (k < 16) {
-                const int j = k, jj = j >> 2, t = j & 3;
-                const float Lv = t == 0 ? L4[jj].x : t == 1 ? L4[jj].y : t == 2 ? L4[jj].z : L4[jj].w;
-                const float Dv = t == 0 ? D4[jj].x : t == 1 ? D4[jj].y : t == 2 ? D4[jj].z : D4[jj].w;
-                float p = fast_exp2(s0[j] * a.scale_log2 - Lv);
-                p = (uint32_t)(base + 8 * jj + 4 * hh + t) <= uba ? p : 0.f;
-                pf[j] = p;
-                df[j] = p * (VSCALE * d0[j] - Dv);
-                if (j & 1) {
-                    pb[j >> 3][(j & 7) - 1] = f2bf(pf[j - 1]);
-                    pb[j >> 3][j & 7] = f2bf(pf[j]);
-                    sb[j >> 3][(j & 7) - 1] = f2bf(df[j - 1]);
-                    sb[j >> 3][j & 7] = f2bf(df[j]);
-                }
-            }
-            if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
+        return (const char *)tile_ + R * rowbytes + 16 * p + 8 * (m4 & 1);
     };
 
-    // dS of a step into the stored-dS blocks (query tile n, key block kap = 4 tile + wave; see ds_row_width)
-    const int s16 = seq_start & ~15;
-    const int kap = 4 * tile + wave;
-    const int64_t ds_head = A.ds ? A.ds_index[a.batch] : 0, ds_seq = A.ds ? A.ds_index[bseq] : 0;
-    auto store_ds = [&](int step, const bf16x8 *sb) {
-        const int h = kvh * G + split * GS + step / nq;
-        const int q0 = step_q0(step);
-        const int n = (q0 - s16) >> 5;
-        const int64_t blk = (int64_t)h * ds_head + ds_seq + ds_rows_before(n, a.window) +
-                            (kap - ds_klo(q0, seq_start, a.window));
-        if (blk >= A.ds_cap) return false;   // only with a max_seqlen below the longest sequence
-        // streaming stores: the blocks are read back by another kernel, so keep them out of L2's way
-        // plane P holds sb[P] of every lane at row (lane ^ 8 hh ^ 4 P): each store writes a whole 1 KB plane
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 *dst = (u32x4 *)(A.ds + blk * 1024);
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[0]), dst + (lane ^ (8 * hh)));
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), dst + 64 + (lane ^ (8 * hh) ^ 4));
-        return true;
-    };
-
-    // ---- three-stage tile ring.  At stage st the tiles of steps st and st+1 are read and step st+2 is
-    // loaded: wait for all of this wave's loads (step st+1's tiles, issued one stage earlier), barrier (every
-    // wave has landed its part and has finished stage st-1, whose buffer the new loads refill), issue.  Every
-    // stage issues one tile set (the last step's again once the steps run out), so the waits stay uniform.
-    // The compute of a stage is the fused step above: the softmax of step st (its S/dP in s0/d0) between
-    // the S/dP products of step st+1 (into s1/d1), then the dV/dK products of step st.
-    f32x16 sA = f32x16{}, dA = f32x16{}, sB = f32x16{}, dB = f32x16{};
-    issue(0, t0s);
-    issue(min(1, nsteps - 1), t1s);
-    wait_vmcnt<DK_LOADS>();
-    __builtin_amdgcn_s_barrier();
-    sdp(t0s, sA, dA);
-    // vmcnt also counts stores, and counts complete in issue order: when the previous stage ended with its
-    // two dS stores, waiting for all but two vector memory operations lands the tiles issued before them
-    // without waiting for the stores to reach memory.
+    // ---- tile ring: at stage st the tiles of steps st (P waves) and st-1 (dS waves) are read and step
+    // st+1 is loaded: wait for this wave's loads (step st's tiles, issued one stage earlier; a dS wave's two
+    // dS stores of the previous stage may stay in flight, as vmcnt completes in issue order), make the P
+    // writes of the previous stage visible, barrier (every wave has landed its part and finished stage st-1;
+    // the buffer of step st-2 is free), load step st+1.  Every stage loads one tile set (the last step's
+    // again once the steps run out), so the waits stay uniform.  Both roles pass nsteps + 1 barriers.
+    issue(0, ring[0]);
     bool stored = false;
-    auto stage = [&](int st, const DkdvTile &cur, const DkdvTile &nxt, DkdvTile &fill, const f32x16 &s0,
-                     const f32x16 &d0, f32x16 &s1, f32x16 &d1) {
+    auto stage_start = [&](int st, DkdvTile &fill) {
         if (stored) wait_vmcnt<2>();
         else wait_vmcnt<0>();
         stored = false;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        issue(min(st + 2, nsteps - 1), fill);
-        if (visible(st) || visible(st + 1)) {
-            bf16x8 pb[2], sb[2];
-            fused(step_q0(st), masked(st) ? (uint32_t)ub : 0xffffffffu, cur, nxt, s0, d0, s1, d1, pb, sb);
-            if (A.ds && visible(st)) stored = store_ds(st, sb);
-        }
+        issue(min(st + 1, nsteps - 1), fill);
     };
-    // unrolled by six: the tile ring has period three and the S/dP register pair period two
-    for (int st = 0; st < nsteps; st += 6) {
-        stage(st, t0s, t1s, t2s, sA, dA, sB, dB);
-        if (st + 1 >= nsteps) break;
-        stage(st + 1, t1s, t2s, t0s, sB, dB, sA, dA);
-        if (st + 2 >= nsteps) break;
-        stage(st + 2, t2s, t0s, t1s, sA, dA, sB, dB);
-        if (st + 3 >= nsteps) break;
-        stage(st + 3, t0s, t1s, t2s, sB, dB, sA, dA);
-        if (st + 4 >= nsteps) break;
-        stage(st + 4, t1s, t2s, t0s, sA, dA, sB, dB);
-        if (st + 5 >= nsteps) break;
-        stage(st + 5, t2s, t0s, t1s, sB, dB, sA, dA);
-    }
-    wait_vmcnt<0>();
 
-    // ---- epilogue: dv = 0.707 * dV^T, dk = R^T dK^T / sqrt(192); with several head splits, fp32 partials
-    // that bwd_dkv_reduce sums in split order
-    if (kvalid && A.splits > 1) {
-        const float2 *cs = a.rope + (size_t)min(kj - seq_start, a.rope_len - 1) * NHALF;
-        rope_back(dk[0], dk[1], cs, hh);
-        float *pp = A.dkv_part + (((size_t)split * A.T_pad + kj) * a.hkv + kvh) * (DQK + DVV) + 4 * hh;
+    if (role == 0) {
+        // ================= P waves: S = Q'K'^T, P, dV^T += dO^T P
+        bf16x8 kf[12];
+        {
+            const u16 *kp = A.W.kr + ((size_t)kjl * a.hkv + kvh) * DQK + 8 * hh;
 #pragma unroll
-        for (int i = 0; i < 6; ++i)
+            for (int s = 0; s < 12; ++s) kf[s] = ld16(kp + 16 * s);
+        }
+        f32x16 dv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
+        // operand k: q' rows (S, k < 12), then dO^T columns (dV, k - 12 = 2 i + s)
+        auto load_op = [&](int k, const DkdvTile &T) -> bf16x8 {
+            if (k < 12) return ld16((const u16 *)T.qr + (c * QCH + swz384t(c, 2 * k + hh)) * 8);
+            const int i = (k - 12) >> 1, sk = (k - 12) & 1;
+            return tr_pair(tr_at(T.orow, OCH * 16, false, sk, 0, i), tr_at(T.orow, OCH * 16, false, sk, 1, i));
+        };
+        auto p_step = [&](int st, const DkdvTile &T, float4 *pslot) {
+            const uint32_t uba = masked(st) ? (uint32_t)ub : 0xffffffffu;
+            const int base = step_q0(st) - kjm;   // qi - kj of this lane's first row
+            constexpr int R = 2 * DK_AHEAD;
+            bf16x8 ob[R];
+#pragma unroll
+            for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, T);
+            float4 L4[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) L4[jj] = *(const float4 *)(T.ld + 8 * jj + 4 * hh);
+            f32x16 sacc = f32x16{};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 12; ++k) {
+                sacc = mfma32(ob[k % R], kf[k], sacc);
+                ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
+                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            bf16x8 pb[2];
+            float pv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int jj = j >> 2, t = j & 3;
+                const float Lv = t == 0 ? L4[jj].x : t == 1 ? L4[jj].y : t == 2 ? L4[jj].z : L4[jj].w;
+                pv[j] = fast_exp2(sacc[j] * a.scale_log2 - Lv);
+                pv[j] = (uint32_t)(base + 8 * jj + 4 * hh + t) <= uba ? pv[j] : 0.f;
+                pb[j >> 3][j & 7] = f2bf(pv[j]);
+            }
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                *(float4 *)(pp + 32 * i + 8 * jj) = make_float4(dk[i][4 * jj] * RSQRT_DQK, dk[i][4 * jj + 1] * RSQRT_DQK,
-                                                                dk[i][4 * jj + 2] * RSQRT_DQK, dk[i][4 * jj + 3] * RSQRT_DQK);
+                pslot[64 * jj + lane] = make_float4(pv[4 * jj], pv[4 * jj + 1], pv[4 * jj + 2], pv[4 * jj + 3]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int k = 12; k < 20; ++k) {
+                const int i = (k - 12) >> 1;
+                dv[i] = mfma32(ob[k % R], pb[(k - 12) & 1], dv[i]);
+                if (k + DK_AHEAD < 20) ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
+                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto stage = [&](int st, const DkdvTile &cur, DkdvTile &fill) {
+            stage_start(st, fill);
+            if (visible(st)) p_step(st, cur, pbuf[st & 1][kq]);
+        };
+        // unrolled by three: the ring's buffers by name (stage st reads ring[st % 3], fills ring[(st+1) % 3])
+        for (int st = 0; st <= nsteps; st += 3) {
+            stage(st, ring[0], ring[1]);
+            if (st + 1 > nsteps) break;
+            stage(st + 1, ring[1], ring[2]);
+            if (st + 2 > nsteps) break;
+            stage(st + 2, ring[2], ring[0]);
+        }
+        wait_vmcnt<0>();
+        // ---- epilogue: dv = 0.707 dV^T (fp32 partials with several head splits)
+        if (kvalid && A.splits > 1) {
+            float *pp = A.dkv_part + (((size_t)split * A.T_pad + kj) * a.hkv + kvh) * (DQK + DVV) + DQK + 4 * hh;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                *(float4 *)(pp + DQK + 32 * i + 8 * jj) = make_float4(dv[i][4 * jj] * VSCALE, dv[i][4 * jj + 1] * VSCALE,
-                                                                      dv[i][4 * jj + 2] * VSCALE, dv[i][4 * jj + 3] * VSCALE);
-    } else if (kvalid) {
-        u16 *dvp = A.dv + ((size_t)kj * a.hkv + kvh) * DVV + 4 * hh;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+                for (int jj = 0; jj < 4; ++jj)
+                    *(float4 *)(pp + 32 * i + 8 * jj) = make_float4(dv[i][4 * jj] * VSCALE, dv[i][4 * jj + 1] * VSCALE,
+                                                                    dv[i][4 * jj + 2] * VSCALE, dv[i][4 * jj + 3] * VSCALE);
+        } else if (kvalid) {
+            u16 *dvp = A.dv + ((size_t)kj * a.hkv + kvh) * DVV + 4 * hh;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                bf16x4 w;
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) w[t] = f2bf(dv[i][4 * jj + t] * VSCALE);
-                *(uint2 *)(dvp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                for (int jj = 0; jj < 4; ++jj) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) w[t] = f2bf(dv[i][4 * jj + t] * VSCALE);
+                    *(uint2 *)(dvp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                }
             }
         }
-        const float2 *cs = a.rope + (size_t)min(kj - seq_start, a.rope_len - 1) * NHALF;
+    } else {
+        // ================= dS waves: dP = dO V^T, dS = P (0.707 dP - D), dK^T += Q'^T dS (one step behind)
+        bf16x8 vf[8];
+        {
+            const u16 *vp = a.v + ((size_t)kjl * a.hkv + kvh) * DVV + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) vf[s] = ld16(vp + 16 * s);
+        }
+        f32x16 dk[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) dk[i] = f32x16{};
+        // operand k: dO rows (dP, k < 8), then q'^T columns (dK, k - 8 = 2 i + s)
+        auto load_op = [&](int k, const DkdvTile &T) -> bf16x8 {
+            if (k < 8) return ld16((const u16 *)T.orow + (c * OCH + swz256t(c, 2 * k + hh)) * 8);
+            const int i = (k - 8) >> 1, sk = (k - 8) & 1;
+            return tr_pair(tr_at(T.qr, QCH * 16, true, sk, 0, i), tr_at(T.qr, QCH * 16, true, sk, 1, i));
+        };
+        // dS of a step into the stored-dS blocks (query tile n, key block 4 tile + kq; see ds_row_width)
+        const int s16 = seq_start & ~15;
+        const int kap = 4 * tile + kq;
+        const int64_t ds_head = A.ds ? A.ds_index[a.batch] : 0, ds_seq = A.ds ? A.ds_index[bseq] : 0;
+        auto store_ds = [&](int step, const bf16x8 *sb) {
+            const int h = kvh * G + split * GS + step / nq;
+            const int q0 = step_q0(step);
+            const int n = (q0 - s16) >> 5;
+            const int64_t blk = (int64_t)h * ds_head + ds_seq + ds_rows_before(n, a.window) +
+                                (kap - ds_klo(q0, seq_start, a.window));
+            if (blk >= A.ds_cap) return false;   // only with a max_seqlen below the longest sequence
+            // streaming stores (the blocks are read back by another kernel); plane P holds sb[P] of every lane
+            // at row (lane ^ 8 hh ^ 4 P): each store writes a whole 1 KB plane
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            u32x4 *dst = (u32x4 *)(A.ds + blk * 1024);
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[0]), dst + (lane ^ (8 * hh)));
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), dst + 64 + (lane ^ (8 * hh) ^ 4));
+            return true;
+        };
+        auto ds_step = [&](int st, const DkdvTile &T, const float4 *pslot) {
+            constexpr int R = 2 * DK_AHEAD;
+            bf16x8 ob[R];
+#pragma unroll
+            for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, T);
+            f32x16 dpacc = f32x16{};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                dpacc = mfma32(ob[k % R], vf[k], dpacc);
+                ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
+                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            float4 P4[4], D4[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) P4[jj] = pslot[64 * jj + lane];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) D4[jj] = *(const float4 *)(T.ld + MQ + 8 * jj + 4 * hh);
+            bf16x8 sb[2];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int jj = j >> 2, t = j & 3;
+                const float Dv = t == 0 ? D4[jj].x : t == 1 ? D4[jj].y : t == 2 ? D4[jj].z : D4[jj].w;
+                const float pv = t == 0 ? P4[jj].x : t == 1 ? P4[jj].y : t == 2 ? P4[jj].z : P4[jj].w;
+                sb[j >> 3][j & 7] = f2bf(pv * (VSCALE * dpacc[j] - Dv));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 8; k < 20; ++k) {
+                const int i = (k - 8) >> 1;
+                dk[i] = mfma32(ob[k % R], sb[(k - 8) & 1], dk[i]);
+                if (k + DK_AHEAD < 20) ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
+                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            if (A.ds) stored = store_ds(st, sb);
+        };
+        auto stage = [&](int st, const DkdvTile &prev, DkdvTile &fill) {
+            stage_start(st, fill);
+            if (st >= 1 && visible(st - 1)) ds_step(st - 1, prev, pbuf[(st - 1) & 1][kq]);
+        };
+        // stage st reads ring[(st - 1) % 3] and fills ring[(st + 1) % 3]
+        for (int st = 0; st <= nsteps; st += 3) {
+            stage(st, ring[2], ring[1]);
+            if (st + 1 > nsteps) break;
+            stage(st + 1, ring[0], ring[2]);
+            if (st + 2 > nsteps) break;
+            stage(st + 2, ring[1], ring[0]);
+        }
+        wait_vmcnt<0>();
+        // ---- epilogue: dk = R^T dK^T / sqrt(192) (fp32 partials with several head splits)
+        const float2 *cs = a.rope + (size_t)min(kjl - seq_start, a.rope_len - 1) * NHALF;
         rope_back(dk[0], dk[1], cs, hh);
-        u16 *dkp = A.dk + ((size_t)kj * a.hkv + kvh) * DQK + 4 * hh;
+        if (kvalid && A.splits > 1) {
+            float *pp = A.dkv_part + (((size_t)split * A.T_pad + kj) * a.hkv + kvh) * (DQK + DVV) + 4 * hh;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
+            for (int i = 0; i < 6; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                bf16x4 w;
+                for (int jj = 0; jj < 4; ++jj)
+                    *(float4 *)(pp + 32 * i + 8 * jj) = make_float4(dk[i][4 * jj] * RSQRT_DQK, dk[i][4 * jj + 1] * RSQRT_DQK,
+                                                                    dk[i][4 * jj + 2] * RSQRT_DQK, dk[i][4 * jj + 3] * RSQRT_DQK);
+        } else if (kvalid) {
+            u16 *dkp = A.dk + ((size_t)kj * a.hkv + kvh) * DQK + 4 * hh;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) w[t] = f2bf(dk[i][4 * jj + t] * RSQRT_DQK);
-                *(uint2 *)(dkp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+            for (int i = 0; i < 6; ++i) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) w[t] = f2bf(dk[i][4 * jj + t] * RSQRT_DQK);
+                    *(uint2 *)(dkp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                }
             }
         }
     }
@@ -1104,8 +1127,8 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     const long kv_grid = kv_tiles * a.hkv * A.splits;
     if (kv_grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     trace_begin(a.window >= 0 ? "bwd_dkdv_swa" : "bwd_dkdv_global", stream);
-    if (a.window >= 0) bwd_dkdv_kernel<true><<<(unsigned)kv_grid, 256, 0, stream>>>(A);
-    else bwd_dkdv_kernel<false><<<(unsigned)kv_grid, 256, 0, stream>>>(A);
+    if (a.window >= 0) bwd_dkdv_kernel<true><<<(unsigned)kv_grid, 512, 0, stream>>>(A);
+    else bwd_dkdv_kernel<false><<<(unsigned)kv_grid, 512, 0, stream>>>(A);
     trace_end(stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
