@@ -35,6 +35,9 @@
 namespace mimo {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr float RSQRT_DQK = 0.07216878364870322f;   // 1 / sqrt(192)
 
 __device__ __forceinline__ int seq_start_of(const int32_t *cu, int batch, int t)
@@ -401,16 +404,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
                 ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
                 if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
-            bf16x8 pb[2];
             float pv[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int jj = j >> 2, t = j & 3;
                 const float Lv = t == 0 ? L4[jj].x : t == 1 ? L4[jj].y : t == 2 ? L4[jj].z : L4[jj].w;
-                pv[j] = fast_exp2(sacc[j] * a.scale_log2 - Lv);
-                pv[j] = (uint32_t)(base + 8 * jj + 4 * hh + t) <= uba ? pv[j] : 0.f;
-                pb[j >> 3][j & 7] = f2bf(pv[j]);
+                pv[j] = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lv));
             }
+            if (uba != 0xffffffffu) {   // only steps that cross the causal / window / sequence edge
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    pv[j] = (uint32_t)(base + 8 * (j >> 2) + 4 * hh + (j & 3)) <= uba ? pv[j] : 0.f;
+            }
+            uint32_t pw[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+                pw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{pv[2 * w], pv[2 * w + 1]}, bf16x2));
+            const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3])),
+                                  __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]))};
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
                 pslot[64 * jj + lane] = make_float4(pv[4 * jj], pv[4 * jj + 1], pv[4 * jj + 2], pv[4 * jj + 3]);
@@ -500,26 +511,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
 #pragma unroll
             for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, T);
             f32x16 dpacc = f32x16{};
+            float4 P4[4], D4[4];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 dpacc = mfma32(ob[k % R], vf[k], dpacc);
                 ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
+                if (k == 3) {   // P and D of the step, read under the second half of the dP MFMAs
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) P4[jj] = pslot[64 * jj + lane];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) D4[jj] = *(const float4 *)(T.ld + MQ + 8 * jj + 4 * hh);
+                }
                 if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
-            float4 P4[4], D4[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) P4[jj] = pslot[64 * jj + lane];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) D4[jj] = *(const float4 *)(T.ld + MQ + 8 * jj + 4 * hh);
-            bf16x8 sb[2];
+            float dsv[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int jj = j >> 2, t = j & 3;
                 const float Dv = t == 0 ? D4[jj].x : t == 1 ? D4[jj].y : t == 2 ? D4[jj].z : D4[jj].w;
                 const float pv = t == 0 ? P4[jj].x : t == 1 ? P4[jj].y : t == 2 ? P4[jj].z : P4[jj].w;
-                sb[j >> 3][j & 7] = f2bf(pv * (VSCALE * dpacc[j] - Dv));
+                dsv[j] = pv * __builtin_fmaf(VSCALE, dpacc[j], -Dv);
             }
+            uint32_t sw[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+                sw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{dsv[2 * w], dsv[2 * w + 1]}, bf16x2));
+            const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
+                                  __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 8; k < 20; ++k) {
