@@ -261,20 +261,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int x = blockIdx.x;
     const int kvh = x % a.hkv;
     const int split = (x / a.hkv) % A.splits;
-    int tile = x / a.hkv / A.splits;
     const int GS = G / A.splits;      // query heads handled by this workgroup
-    int seq_start = 0, seq_end = 0, bseq = -1;
-    for (int b = a.batch - 1; b >= 0; --b) {
-        seq_start = a.cu[b];
-        seq_end = a.cu[b + 1];
-        const int nt = (seq_end - seq_start + NKB - 1) / NKB;
-        if (tile < nt) {
-            bseq = b;
-            break;
-        }
-        tile -= nt;
-    }
-    if (bseq < 0) return;
+    const SeqPos sp = seq_lookup_rev(a.cu, a.batch, x / a.hkv / A.splits, [](int s, int e) { return (e - s + NKB - 1) / NKB; });
+    if (sp.b < 0) return;
+    const int seq_start = sp.start, seq_end = sp.end, bseq = sp.b, tile = sp.j;
     const int kb0 = seq_start + tile * NKB;
     const int kb_last = min(kb0 + NKB - 1, seq_end - 1);
 
@@ -645,18 +635,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
     const int rest = x / a.hkv;
     const int hgi = rest % n_hg;
     const int tile = rest / n_hg;
-    int ntiles = 0;
-    for (int b = 0; b < a.batch; ++b) ntiles += (a.cu[b + 1] - a.cu[b] + TT - 1) / TT;
-    if (tile >= ntiles) return;
-    int tr = ntiles - 1 - tile;
-    int seq_start = 0, seq_end = 0;
-    for (int b = 0; b < a.batch; ++b) {
-        seq_start = a.cu[b];
-        seq_end = a.cu[b + 1];
-        const int nt = (seq_end - seq_start + TT - 1) / TT;
-        if (tr < nt) break;
-        tr -= nt;
-    }
+    const SeqPos sp = seq_lookup_rev(a.cu, a.batch, tile, [](int s, int e) { return (e - s + TT - 1) / TT; });
+    if (sp.b < 0) return;
+    const int seq_start = sp.start, seq_end = sp.end;
+    const int tr = (seq_end - seq_start + TT - 1) / TT - 1 - sp.j;
     const int t0 = seq_start + tr * TT;
     const int t_last = min(t0 + TT - 1, seq_end - 1);
     const int h0 = kvh * G + hgi * GP;
@@ -880,20 +862,10 @@ __global__ __launch_bounds__(64 * NH, 1) void bwd_dq_ds_kernel(const BwdArgs A)
     const int x = blockIdx.x;
     const int kvh = x % a.hkv;
     const int hg = (x / a.hkv) % n_hg;
-    int tile = x / a.hkv / n_hg;
-    int seq_start = 0, seq_end = 0, bseq = -1, n = 0;
-    for (int b = a.batch - 1; b >= 0; --b) {
-        seq_start = a.cu[b];
-        seq_end = a.cu[b + 1];
-        const int nq = ds_nq(seq_start, seq_end);
-        if (tile < nq) {
-            bseq = b;
-            n = nq - 1 - tile;
-            break;
-        }
-        tile -= nq;
-    }
-    if (bseq < 0) return;
+    const SeqPos sp = seq_lookup_rev(a.cu, a.batch, x / a.hkv / n_hg, [](int s, int e) { return ds_nq(s, e); });
+    if (sp.b < 0) return;
+    const int seq_start = sp.start, seq_end = sp.end, bseq = sp.b;
+    const int n = ds_nq(seq_start, seq_end) - 1 - sp.j;
     const int q0 = (seq_start & ~15) + 32 * n;
     const int h = kvh * G + hg * NH + wave;
     const int klo = ds_klo(q0, seq_start, a.window);

@@ -38,22 +38,26 @@
 namespace mimo {
 namespace {
 
-constexpr int BN = 64;         // keys per tile
 constexpr int KCH = DQK / 8;   // 16-byte chunks per K row (24)
-constexpr int VCH = BN / 8;    // 16-byte chunks per V^T row (8)
 constexpr float RESCALE_TH = 8.f;   // keep a stale running max until the true one exceeds it by 2^8
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// K tile in LDS: row r (key), 24 chunks of 16 B (384-byte rows); V^T tile: row d (dim), 8 chunks.
+// K tile in LDS: row r (key), 24 chunks of 16 B (384-byte rows); V^T tile: row d (dim), BN / 8 chunks
+// (128-byte rows for 64-key tiles, 64-byte rows for 32-key tiles).
 __device__ __forceinline__ int kpos(int r, int q) { return swz384(r, q); }
-__device__ __forceinline__ int vpos(int d, int q) { return swz128(d, q); }
+template <int BN>
+__device__ __forceinline__ int vpos(int d, int q) { return BN == 64 ? swz128(d, q) : swz64(d, q); }
 
-// NW waves per workgroup (32 query rows each) share one stream of K/V tiles: 8 for causal layers (half
-// the L2 -> LDS tile traffic), 4 for sliding-window layers (shorter key span per workgroup).
-template <int NW, int GP, bool SINK, bool WIN>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs A)
+// NW waves per workgroup (32 query rows each) share one stream of BN-key K/V tiles.  Causal layers: 8
+// waves, 64-key tiles in a 3-stage ring (120 KB), one workgroup per CU, all 12 K operands of a block read
+// up front (KA = 12).  Sliding-window layers: 4 waves, 32-key tiles double-buffered (40 KB) and KA = 4 so
+// that three workgroups fit on a CU (OCC): these short work items wait mostly on HBM (Q and the first
+// tiles), and more resident workgroups keep more loads in flight.
+template <int NW, int GP, bool SINK, bool WIN, int BN, int KA, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
 {
+    constexpr int VCH = BN / 8;                // 16-byte chunks per V^T row
     constexpr int NT = 64 * NW;                // threads per workgroup
     constexpr int BM = 32 * NW;                // query rows per workgroup
     constexpr int KLOADS = BN * KCH / NT;      // global_load_lds per thread per K tile
@@ -81,18 +85,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
     const int rest = x / a.hkv;
     const int hgi = rest % n_hg;
     const int tile = rest / n_hg;
-    int ntiles = 0;
-    for (int b = 0; b < a.batch; ++b) ntiles += (a.cu[b + 1] - a.cu[b] + TT - 1) / TT;
-    if (tile >= ntiles) return;
-    int tr = ntiles - 1 - tile;
-    int seq_start = 0, seq_end = 0;
-    for (int b = 0; b < a.batch; ++b) {
-        seq_start = a.cu[b];
-        seq_end = a.cu[b + 1];
-        const int nt = (seq_end - seq_start + TT - 1) / TT;
-        if (tr < nt) break;
-        tr -= nt;
-    }
+    // token tiles counted from the last tile of the last sequence
+    const SeqPos sp = seq_lookup_rev(a.cu, a.batch, tile, [](int s, int e) { return (e - s + TT - 1) / TT; });
+    if (sp.b < 0) return;
+    const int seq_start = sp.start, seq_end = sp.end;
+    const int tr = (seq_end - seq_start + TT - 1) / TT - 1 - sp.j;
     const int t0 = seq_start + tr * TT;
     const int t_last = min(t0 + TT - 1, seq_end - 1);
     const int h0 = kvh * G + hgi * GP;
@@ -118,7 +115,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
 #pragma unroll
     for (int j = 0; j < VLOADS; ++j) {
         const int slot = NT * j + tid, d = slot / VCH, p = slot % VCH;
-        voff[j] = (uint32_t)(((size_t)d * A.P.T_pad + 8 * vpos(d, p)) * 2);
+        voff[j] = (uint32_t)(((size_t)d * A.P.T_pad + 8 * vpos<BN>(d, p)) * 2);
     }
     auto issue_tile = [&](int k0, uint4 *sk, uint4 *sv) {
         const u16 *kb = kr_base + (size_t)k0 * kr_row;
@@ -178,22 +175,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
         const u16 *kt = (const u16 *)skb;
         const u16 *vtt = (const u16 *)svb;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < BN / 32; ++kb) {
             const int kbase = k0 + 32 * kb;
             if (kbase > wkhi || kbase + 31 < wklo) continue;     // no row of this wave sees these 32 keys
             const int kr_ = 32 * kb + c;
-            bf16x8 kop[12];
+            bf16x8 kop[KA];
 #pragma unroll
-            for (int s = 0; s < 12; ++s) kop[s] = ld16(kt + (kr_ * KCH + kpos(kr_, 2 * s + hh)) * 8);
+            for (int s = 0; s < KA; ++s) kop[s] = ld16(kt + (kr_ * KCH + kpos(kr_, 2 * s + hh)) * 8);
             f32x16 sacc = f32x16{};
 #pragma unroll
-            for (int s = 0; s < 12; ++s) sacc = mfma32(kop[s], qf[s], sacc);
-            bf16x8 vop[8];
+            for (int s = 0; s < 12; ++s) {
+                sacc = mfma32(kop[s % KA], qf[s], sacc);
+                if (s + KA < 12) kop[s % KA] = ld16(kt + (kr_ * KCH + kpos(kr_, 2 * (s + KA) + hh)) * 8);
+            }
+            // V^T operand m = 2 i + s (rows 32 i + c, k-step s); KA == 12: all eight read before the softmax,
+            // else two at a time during the P V MFMAs (fewer registers)
+            auto vread = [&](int m) {
+                const int d = 32 * (m >> 1) + c;
+                return ld16(vtt + (d * VCH + vpos<BN>(d, 4 * kb + 2 * (m & 1) + hh)) * 8);
+            };
+            constexpr int VA = KA == 12 ? 8 : 2;
+            bf16x8 vop[VA];
+            if constexpr (VA == 8) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = 32 * i + c;
-#pragma unroll
-                for (int s = 0; s < 2; ++s) vop[2 * i + s] = ld16(vtt + (d * VCH + vpos(d, 4 * kb + 2 * s + hh)) * 8);
+                for (int m = 0; m < 8; ++m) vop[m] = vread(m);
             }
             __builtin_amdgcn_sched_barrier(0);
             float sv[16];
@@ -238,12 +243,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const FwdArgs
                 else ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), ones, ps0, false);
             }
             l_run += ps0 + ps1;
-            const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-            const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+            const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3])),
+                                  __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]))};
+            if constexpr (VA < 8) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[i] = mfma32(vop[2 * i], pf0, o[i]);
-                o[i] = mfma32(vop[2 * i + 1], pf1, o[i]);
+                for (int m = 0; m < VA; ++m) vop[m] = vread(m);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                o[m >> 1] = mfma32(vop[m % VA], pf[m & 1], o[m >> 1]);
+                if (VA < 8 && m + VA < 8) vop[m % VA] = vread(m + VA);
             }
         }
     };
@@ -324,10 +333,10 @@ hipError_t launch_gp(const FwdArgs &A, hipStream_t stream)
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     trace_begin(win ? "attn_fwd_swa" : "attn_fwd_global", stream);
-    if (sink && win) attn_fwd_kernel<4, GP, true, true><<<(unsigned)grid, 256, 0, stream>>>(A);
-    else if (win) attn_fwd_kernel<4, GP, false, true><<<(unsigned)grid, 256, 0, stream>>>(A);
-    else if (sink) attn_fwd_kernel<8, GP, true, false><<<(unsigned)grid, 512, 0, stream>>>(A);
-    else attn_fwd_kernel<8, GP, false, false><<<(unsigned)grid, 512, 0, stream>>>(A);
+    if (sink && win) attn_fwd_kernel<4, GP, true, true, 32, 4, 3><<<(unsigned)grid, 256, 0, stream>>>(A);
+    else if (win) attn_fwd_kernel<4, GP, false, true, 32, 4, 3><<<(unsigned)grid, 256, 0, stream>>>(A);
+    else if (sink) attn_fwd_kernel<8, GP, true, false, 64, 12, 1><<<(unsigned)grid, 512, 0, stream>>>(A);
+    else attn_fwd_kernel<8, GP, false, false, 64, 12, 1><<<(unsigned)grid, 512, 0, stream>>>(A);
     trace_end(stream);
     return hipGetLastError();
 }

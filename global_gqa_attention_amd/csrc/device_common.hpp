@@ -124,6 +124,48 @@ __device__ __forceinline__ bf16x8 tr_pair(const char *p0, const char *p1)
     return __builtin_bit_cast(bf16x8, make_uint4(ux.x, ux.y, uy.x, uy.y));
 }
 
+// THD work items: sequence b (bounds cu[b] .. cu[b + 1]) holds count(start, end) items, numbered from the
+// last sequence backwards (item 0 is the last sequence's item 0).  Returns the sequence holding item idx,
+// its bounds and the item's index inside it (b = -1 past the last item); all wave-uniform.  The lanes read
+// cu_seqlens in parallel (one load per 64 sequences) and a wave prefix sum locates the item, instead of a
+// chain of dependent loads, one per sequence.
+struct SeqPos {
+    int b, start, end, j;
+};
+template <typename Count>
+__device__ __forceinline__ SeqPos seq_lookup_rev(const int *cu, int batch, int idx, Count count)
+{
+    const int lane = threadIdx.x & 63;
+    int before = 0;   // items of the sequences already passed
+    for (int c0 = 0; c0 < batch; c0 += 64) {
+        const int b = batch - 1 - (c0 + lane);
+        int s = 0, e = 0, n = 0;
+        if (b >= 0) {
+            s = cu[b];
+            e = cu[b + 1];
+            n = count(s, e);
+        }
+        int incl = n;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        const unsigned long long hit = __ballot(before + incl > idx);
+        if (hit) {
+            const int L = __builtin_ctzll(hit);
+            SeqPos r;
+            r.b = __builtin_amdgcn_readlane(b, L);
+            r.start = __builtin_amdgcn_readlane(s, L);
+            r.end = __builtin_amdgcn_readlane(e, L);
+            r.j = idx - before - (__builtin_amdgcn_readlane(incl, L) - __builtin_amdgcn_readlane(n, L));
+            return r;
+        }
+        before += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return SeqPos{-1, 0, 0, 0};
+}
+
 // Rotate-half RoPE of one 8-wide chunk pair: x0 holds dims d..d+7 (d < 32), x1 dims d+32..d+39, cs the
 // (cos, sin) of the 8 matching frequencies.  Rounded back to bf16 (the MFMA operand precision).
 __device__ __forceinline__ void rope_pair(bf16x8 &x0, bf16x8 &x1, const float2 *cs)
