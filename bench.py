@@ -154,6 +154,8 @@ def setup_layers(ga, torch, mi, dev):
         g["max_seqlen"] = max(d["lengths"])
         g["out"] = torch.empty(T, hq, 128, dtype=torch.bfloat16, device=dev)
         g["lse"] = torch.empty(hq, T, dtype=torch.float32, device=dev)
+        # the forward's rotated q, handed to the backward (a training step keeps it like out and lse)
+        g["q_rot"] = torch.empty(T, hq, 192, dtype=torch.bfloat16, device=dev)
         g["grads"] = (torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"]),
                       torch.empty(hq, dtype=torch.float32, device=dev) if g["sink"] is not None else None)
         # the workspace that keeps the dS blocks (the dQ kernel reads them back instead of recomputing)
@@ -166,9 +168,9 @@ def setup_layers(ga, torch, mi, dev):
     def step():
         for g in layers.values():
             ga.fwd(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], g["max_seqlen"], g["window"], g["rope_base"],
-                   out=g["out"], lse=g["lse"])
+                   out=g["out"], lse=g["lse"], q_rot=g["q_rot"])
             ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], dout, g["cu_seqlens"], g["max_seqlen"],
-                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"])
+                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"], q_rot=g["q_rot"])
 
     return thd, dout_cpu, layers, step
 

@@ -39,13 +39,13 @@ def lib():
             raise MimoAttnError(f"{LIB_PATH} is missing: build it with `python -m global_gqa_attention_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
-        L.mimo_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, sz, P]
+        L.mimo_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, sz, P]
         L.mimo_attn_fwd_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_fwd_workspace_size.restype = sz
         L.mimo_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_bwd_workspace_size_fast.argtypes = [i32, i32, i32, i32, i32, i32]
         L.mimo_attn_bwd_workspace_size_fast.restype = sz
-        L.mimo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
+        L.mimo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
         L.mimo_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_decode.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
         L.mimo_attn_status_string.argtypes = [ctypes.c_int]
@@ -118,8 +118,9 @@ def fwd_workspace_size(total_tokens, n_q_heads, n_kv_heads, window) -> int:
 
 
 def fwd(q, k, v, sink, cu_seqlens, max_seqlen, window, rope_base, out=None, lse=None, return_lse=True,
-        workspace=None):
-    """Forward of one layer.  Returns (out bf16 [T,hq,128], lse fp32 [hq,T] or None)."""
+        workspace=None, q_rot=None):
+    """Forward of one layer.  Returns (out bf16 [T,hq,128], lse fp32 [hq,T] or None).  A given q_rot (bf16
+    [T,hq,192]) receives q with RoPE applied, for the backward."""
     T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
     if workspace is None:
         workspace = torch.empty((max(fwd_workspace_size(T, hq, hkv, window), 1),), dtype=torch.uint8,
@@ -131,9 +132,11 @@ def fwd(q, k, v, sink, cu_seqlens, max_seqlen, window, rope_base, out=None, lse=
         lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (hq, T))
+    if q_rot is not None:
+        _need(q_rot, "q_rot", torch.bfloat16, (T, hq, DQK))
     rc = lib().mimo_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(cu_seqlens), batch, T, int(max_seqlen),
-                             int(window), float(rope_base), hq, hkv, _ptr(out), _ptr(lse), _ptr(workspace),
-                             workspace.numel(), _stream(q.device))
+                             int(window), float(rope_base), hq, hkv, _ptr(out), _ptr(lse), _ptr(q_rot),
+                             _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(rc, "mimo_attn_fwd")
     return out, lse
 
@@ -148,9 +151,11 @@ def bwd_workspace_size(total_tokens, n_q_heads, n_kv_heads, window, batch=None, 
                                                        int(n_q_heads), int(n_kv_heads), int(window)))
 
 
-def bwd(q, k, v, sink, out, lse, dout, cu_seqlens, max_seqlen, window, rope_base, workspace=None, grads=None):
+def bwd(q, k, v, sink, out, lse, dout, cu_seqlens, max_seqlen, window, rope_base, workspace=None, grads=None,
+        q_rot=None):
     """Backward of one layer.  Returns (dq, dk, dv, dsink or None).  Without a workspace one of the fast size
-    (stored dS) is allocated; a given workspace selects the path by its size."""
+    (stored dS) is allocated; a given workspace selects the path by its size.  q_rot: the forward's rotated q
+    for the same inputs (saves the backward's own rotation pass), or None."""
     T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
     _need(out, "out", torch.bfloat16, (T, hq, DV))
     _need(dout, "dout", torch.bfloat16, (T, hq, DV))
@@ -165,7 +170,9 @@ def bwd(q, k, v, sink, out, lse, dout, cu_seqlens, max_seqlen, window, rope_base
     if workspace is None:
         need = bwd_workspace_size(T, hq, hkv, window, batch, max_seqlen)
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
-    rc = lib().mimo_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout),
+    if q_rot is not None:
+        _need(q_rot, "q_rot", torch.bfloat16, (T, hq, DQK))
+    rc = lib().mimo_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout), _ptr(q_rot),
                              _ptr(cu_seqlens), batch, T, int(max_seqlen), int(window), float(rope_base), hq, hkv,
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), _ptr(workspace), workspace.numel(),
                              _stream(q.device))

@@ -218,7 +218,7 @@ void mimo_attn_release(void)
 mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
-                            int32_t n_kv_heads, void *out, float *lse, void *workspace,
+                            int32_t n_kv_heads, void *out, float *lse, void *q_rot, void *workspace,
                             size_t workspace_bytes, void *stream)
 {
     mimo_status_t s = check_layer(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base,
@@ -249,6 +249,7 @@ mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const f
     a.L.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kDQK));
     a.out = (uint16_t *)out;
     a.lse = lse;
+    a.q_rot = (uint16_t *)q_rot;
     hipError_t e = mimo::launch_fwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return ok();
@@ -277,7 +278,7 @@ size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, in
 }
 
 mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const float *sink,
-                            const void *out, const float *lse, const void *dout,
+                            const void *out, const float *lse, const void *dout, const void *q_rot,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
                             int32_t n_kv_heads, void *dq, void *dk, void *dv, float *dsink,
@@ -328,6 +329,12 @@ mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const f
                                                         max_seqlen);
     const bool stored_ds = ds_need > 0 && workspace_bytes >= ds_need;
     mimo::bwd_carve(workspace, total_tokens, n_q_heads, n_kv_heads, &a, stored_ds, batch, max_seqlen);
+    a.qr_rows = a.T_pad;
+    a.qr_given = q_rot != nullptr;
+    if (q_rot) {   // the forward's rotated q replaces the workspace copy (read only)
+        a.W.qr = (uint16_t *)q_rot;
+        a.qr_rows = total_tokens;
+    }
     if (stored_ds) a.ds_cap = (int64_t)((ds_need - (size_t)((char *)a.ds - (char *)workspace)) / 2048);
     hipError_t e = mimo::launch_bwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "backward launch");

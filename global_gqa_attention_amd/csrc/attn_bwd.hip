@@ -294,9 +294,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         const int h = kvh * G + split * GS + step / nq;
         const int q0 = step_q0(step);
         if (wave < 6) {
-            const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
+            if (q0 + MQ <= A.qr_rows) {
+                const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) lds_dma16(bq, o_qr[j], T.qr + 384 * j + 64 * wave);
+                for (int j = 0; j < 2; ++j) lds_dma16(bq, o_qr[j], T.qr + 384 * j + 64 * wave);
+            } else {
+                // a caller's q_rot has exactly T rows: rows past its end are clamped to the last (and masked)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int slot = 384 * j + 64 * min(wave, 5) + lane, r = slot / QCH, p = slot % QCH;
+                    const int row = min(q0 + r, A.qr_rows - 1);
+                    lds_dma16(A.W.qr + ((size_t)row * a.hq + h) * DQK + 8 * swz384t(r, p), T.qr + 384 * j + 64 * wave);
+                }
+            }
         }
         if (q0 + MQ <= a.T) {
             lds_dma16(A.dout + ((size_t)q0 * a.hq + h) * DVV, o_or, T.orow + 64 * wave);
@@ -1098,10 +1108,12 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    trace_begin(a.window >= 0 ? "bwd_prep_q_swa" : "bwd_prep_q_global", stream);
-    e = launch_row_prep<DQK, true>(a.q, a.hq, A.W.qr, nullptr, a, A.T_pad, stream);
-    trace_end(stream);
-    if (e != hipSuccess) return e;
+    if (!A.qr_given) {
+        trace_begin(a.window >= 0 ? "bwd_prep_q_swa" : "bwd_prep_q_global", stream);
+        e = launch_row_prep<DQK, true>(a.q, a.hq, A.W.qr, nullptr, a, A.T_pad, stream);
+        trace_end(stream);
+        if (e != hipSuccess) return e;
+    }
     trace_begin(a.window >= 0 ? "bwd_prep_k_swa" : "bwd_prep_k_global", stream);
     e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.W.krt, a, A.T_pad, stream);
     trace_end(stream);

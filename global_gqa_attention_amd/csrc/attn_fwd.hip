@@ -147,6 +147,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         }
         rope_pair(qf[0], qf[2], c0);
         rope_pair(qf[1], qf[3], c1);
+        if (A.q_rot && qvalid) {   // the rotated q for the backward: this lane's 12 chunks of its row
+            u16 *qo = A.q_rot + ((size_t)qt * a.hq + qh) * DQK + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < 12; ++s) st16(qo + 16 * s, qf[s]);
+        }
     }
 
     // this wave's rows span tokens [wt0, wt1]; 32-key blocks outside [wklo, wkhi] are skipped

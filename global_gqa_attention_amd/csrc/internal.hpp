@@ -30,6 +30,7 @@ struct FwdArgs {
     KVPrep P;
     uint16_t *out;                 // bf16 [T,hq,128]
     float *lse;                    // fp32 [hq,T] or nullptr
+    uint16_t *q_rot;               // bf16 [T,hq,192] rotated q, or nullptr
 };
 
 // DMA-ready copies the backward prepares in its workspace (see attn_bwd.hip).
@@ -50,6 +51,8 @@ struct BwdArgs {
     float *lse2;                   // workspace: LSE * log2(e) [hq,T_pad]
     float *dkv_part;               // workspace: fp32 dk|dv partials [splits, T_pad, hkv, 320] (splits > 1)
     int T_pad;
+    int qr_rows;                   // rows of W.qr that may be read: T_pad (prepared here) or T (the caller's)
+    bool qr_given;                 // W.qr is the forward's q_rot: no prep pass for q
     int splits;                    // query heads of a group are split over this many key-tile workgroups
     // stored-dS path (nullptr: dQ recomputes S and dP): the dK/dV kernel writes every 32 x 32 bf16 block of
     // dS it computes, the dQ kernel reads them back.  ds_index[b] = first block of sequence b within a head,

@@ -60,6 +60,9 @@ typedef enum {
  *   window   -1 (causal) or >= 0 (the query plus `window` previous keys)
  *   out   bf16 [total_tokens, n_q_heads, 128]
  *   lse   fp32 [n_q_heads, total_tokens] natural-log softmax denominator incl. the sink, or NULL
+ *   q_rot bf16 [total_tokens, n_q_heads, 192] or NULL: when given, receives q with RoPE applied, exactly
+ *         the values the scores use; a training caller passes it on to mimo_attn_bwd, which then skips
+ *         rotating q again
  *   workspace: device memory of at least mimo_attn_fwd_workspace_size() bytes, owned by the caller; needs
  *   no initialisation and must not be shared with a concurrent call.
  * Source: miles docs "MiMo-V2.6-Flash" sections 1, 5.1, 5.4; miles PR "feat(models): add MiMo-V2.6-Flash-RL
@@ -67,7 +70,7 @@ typedef enum {
 mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
-                            int32_t n_kv_heads, void *out, float *lse, void *workspace,
+                            int32_t n_kv_heads, void *out, float *lse, void *q_rot, void *workspace,
                             size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace mimo_attn_fwd needs: RoPE-rotated K and per-head transposed V (about
@@ -95,6 +98,8 @@ size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, in
  *   out   bf16 [total_tokens, n_q_heads, 128]  forward output (used for D = rowsum(dO * O))
  *   lse   fp32 [n_q_heads, total_tokens]       forward LSE
  *   dout  bf16 [total_tokens, n_q_heads, 128]  upstream gradient dO
+ *   q_rot bf16 [total_tokens, n_q_heads, 192]  the forward's q_rot output for these q and positions, or
+ *         NULL (the backward then rotates q itself into the workspace); read only
  *   dq    bf16 [total_tokens, n_q_heads, 192]  gradient w.r.t. the un-rotated q
  *   dk    bf16 [total_tokens, n_kv_heads, 192] gradient w.r.t. the un-rotated k (summed over the group)
  *   dv    bf16 [total_tokens, n_kv_heads, 128] gradient w.r.t. the unscaled v (summed over the group)
@@ -108,7 +113,7 @@ size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, in
  * Source: the exact gradient of the forward above; miles docs "MiMo-V2.6-Flash" section 5.4 (the trainer's
  * fused attention carries the sink in training). */
 mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const float *sink,
-                            const void *out, const float *lse, const void *dout,
+                            const void *out, const float *lse, const void *dout, const void *q_rot,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
                             int32_t n_kv_heads, void *dq, void *dk, void *dv, float *dsink,

@@ -50,10 +50,11 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails ho
 
 def fwd(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, sink=None, cu=FAKE, batch=1, T=16, max_seqlen=16, window=128,
-             base=1e4, hq=64, hkv=8, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
+             base=1e4, hq=64, hkv=8, out=FAKE, lse=None, q_rot=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return L.mimo_attn_fwd(a["q"], a["k"], a["v"], a["sink"], a["cu"], a["batch"], a["T"], a["max_seqlen"],
-                           a["window"], a["base"], a["hq"], a["hkv"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+                           a["window"], a["base"], a["hq"], a["hkv"], a["out"], a["lse"], a["q_rot"], a["ws"],
+                           a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -73,8 +74,8 @@ def test_empty_batch_is_a_no_op(L):
 def bwd(L, **kw):
     a = dict(sink=None, dsink=None, ws=FAKE, wsb=1 << 30, hkv=8, T=16, window=128)
     a.update(kw)
-    return L.mimo_attn_bwd(FAKE, FAKE, FAKE, a["sink"], FAKE, FAKE, FAKE, FAKE, 1, a["T"], 16, a["window"], 1e4,
-                           64, a["hkv"], FAKE, FAKE, FAKE, a["dsink"], a["ws"], a["wsb"], None)
+    return L.mimo_attn_bwd(FAKE, FAKE, FAKE, a["sink"], FAKE, FAKE, FAKE, None, FAKE, 1, a["T"], 16, a["window"],
+                           1e4, 64, a["hkv"], FAKE, FAKE, FAKE, a["dsink"], a["ws"], a["wsb"], None)
 
 
 def test_bwd_rejects_bad_arguments(L):

@@ -31,7 +31,7 @@ def _given_outputs(d, rows=None):
     return torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(l).to(torch.float32)
 
 
-def _run_bwd(ga, d, O, L, dO, path="fast"):
+def _run_bwd(ga, d, O, L, dO, path="fast", q_rot=None):
     dev = "cuda"
     sink = None if d["sink"] is None else d["sink"].to(dev)
     T, hq, hkv = d["q"].shape[0], d["q"].shape[1], d["k"].shape[1]
@@ -42,7 +42,7 @@ def _run_bwd(ga, d, O, L, dO, path="fast"):
         n = ga.bwd_workspace_size(T, hq, hkv, d["window"])
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     g = ga.bwd(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), sink, O.to(dev), L.to(dev), dO.to(dev),
-               d["cu_seqlens"].to(dev), maxl, d["window"], d["rope_base"], workspace=ws)
+               d["cu_seqlens"].to(dev), maxl, d["window"], d["rope_base"], workspace=ws, q_rot=q_rot)
     torch.cuda.synchronize()
     return [None if x is None else x.cpu() for x in g]
 
@@ -150,3 +150,26 @@ def test_bwd_global_small_batch_sampled(path):
     dO = mi.dout_like(4047, 4)
     print(f"case global 2048+1999 bwd path={path}", flush=True)
     _sampled_bwd(ga, d, dO, 300, 40, [], 4, path)
+
+
+@pytest.mark.parametrize("lengths,hkv,window", [([33, 1, 31, 47, 16, 17], 8, 3), ([700, 333, 95], 4, -1)])
+@pytest.mark.parametrize("path", ["fast", "least"])
+def test_bwd_with_forward_q_rot(lengths, hkv, window, path):
+    """Handing the backward the forward's rotated q gives bitwise the gradients of the backward's own
+    rotation pass (the same table and rounding), including the last query tile, which reads past the T rows
+    of the caller's buffer (clamped)."""
+    ga = _gpu()
+    d = mi.make_layer(lengths, 64, hkv, 12, window >= 0)
+    d.update(window=window, rope_base=1e4)
+    print(f"case q_rot bwd lengths={lengths} path={path}", flush=True)
+    dev = "cuda"
+    qr = torch.empty(d["q"].shape, dtype=torch.bfloat16, device=dev)
+    sink = None if d["sink"] is None else d["sink"].to(dev)
+    O, L = ga.fwd(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), sink, d["cu_seqlens"].to(dev), max(lengths),
+                  window, 1e4, q_rot=qr)
+    O, L = O.cpu(), L.cpu()
+    dO = mi.dout_like(sum(lengths), 4)
+    a = _run_bwd(ga, d, O, L, dO, path)
+    b = _run_bwd(ga, d, O, L, dO, path, q_rot=qr)
+    for x, y in zip(a, b):
+        assert (x is None and y is None) or torch.equal(x, y)

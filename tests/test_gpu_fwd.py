@@ -122,3 +122,32 @@ def test_fwd_thd_32k_sampled():
                                      d["rope_base"], rows)
         compare(f"{name} out", out.reshape(-1, 128)[rows], ro)
         compare(f"{name} lse", lse.T.reshape(-1)[rows], rl)
+
+
+@pytest.mark.parametrize("lengths,hkv,window,base", [
+    ([1, 5, 63, 64, 65, 129, 200, 0, 300], 8, 128, 1e4),
+    ([17, 130, 1], 4, -1, 1e7),
+])
+def test_fwd_q_rot_output(lengths, hkv, window, base):
+    """The optional rotated-q output: RoPE applied at each token's position in its own sequence (the oracle's
+    fp64 rotation, to one bf16 rounding), and out / lse unchanged by asking for it."""
+    ga = _gpu()
+    d = _case(lengths, 64, hkv, window, base, window >= 0, 8)
+    print(f"case q_rot lengths={lengths} window={window}", flush=True)
+    dev = "cuda"
+    q, k, v = d["q"].to(dev), d["k"].to(dev), d["v"].to(dev)
+    sink = None if d["sink"] is None else d["sink"].to(dev)
+    cu = d["cu_seqlens"].to(dev)
+    maxl = max(lengths)
+    qr = torch.full_like(q, float("nan"))
+    o1, l1 = ga.fwd(q, k, v, sink, cu, maxl, window, base, q_rot=qr)
+    o2, l2 = ga.fwd(q, k, v, sink, cu, maxl, window, base)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    T = sum(lengths)
+    pos = np.concatenate([np.arange(n) for n in lengths]).astype(np.int32)
+    ref = oracle.rope(d["q"].reshape(T * 64, 192), np.repeat(pos, 64), base)
+    got = qr.cpu().float().numpy().reshape(T * 64, 192)
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all()
+    assert (err <= 2.0 ** -8 * np.abs(ref) + 1e-6).all(), float(err.max())
