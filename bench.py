@@ -292,6 +292,42 @@ def stats_summary(csv_path, title, command):
               f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
 
 
+def run_prefill(ga, torch, layers, reps=10):
+    """Prefill (inference) forward of each layer alone, without the training-only rotated-q output: median
+    per-launch times of its kernels over `reps` calls, algorithmic FLOPs and the forward kernel's algorithmic
+    HBM bytes (q and K/V read once, out and LSE written once)."""
+    res = {}
+    for lname, g in layers.items():
+        T, hq, hkv = g["q"].shape[0], g["q"].shape[1], g["k"].shape[1]
+        ws = torch.empty(ga.fwd_workspace_size(T, hq, hkv, g["window"]), dtype=torch.uint8, device=g["q"].device)
+        call = lambda: ga.fwd(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], g["max_seqlen"], g["window"],
+                              g["rope_base"], out=g["out"], lse=g["lse"], workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ga.trace_read(clear=True)
+        ga.trace_enable(True)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        ga.trace_enable(False)
+        per = {}
+        for name, ms in ga.trace_read(clear=True):
+            per.setdefault(name.rsplit("_", 1)[0], []).append(ms)
+        med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
+        attn = med.get("attn_fwd", 0.0)
+        total = attn + med.get("kv_prep", 0.0)
+        flop = g["pairs"] * FWD_FLOP_PER_PAIR
+        hbm = T * hq * (2 * 192 + 2 * 128 + 4) + T * hkv * 2 * (192 + 128)
+        res[lname] = {"ms": round(total, 4), "attn_fwd_ms": round(attn, 4),
+                      "TFLOP/s": round(flop / (total * 1e-3) / 1e12, 1),
+                      "frac_of_mfma_peak": round(flop / (total * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "attn_fwd_TFLOP/s": round(flop / (attn * 1e-3) / 1e12, 1),
+                      "attn_fwd_GB/s": round(hbm / (attn * 1e-3) / 1e9, 1),
+                      "attn_fwd_hbm_frac": round(hbm / (attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -397,6 +433,7 @@ def main():
         "frac_of_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "layers": layer_tflops, "kernels": kernels, "roofline": roofline,
     }
+    line["prefill"] = run_prefill(ga, torch, layers)
     if not args.no_decode:
         line["decode"] = run_decode(ga, torch, mi)
     if not args.no_cpu_baseline:

@@ -173,3 +173,25 @@ def test_bwd_with_forward_q_rot(lengths, hkv, window, path):
     b = _run_bwd(ga, d, O, L, dO, path, q_rot=qr)
     for x, y in zip(a, b):
         assert (x is None and y is None) or torch.equal(x, y)
+
+
+@pytest.mark.parametrize("window,hkv,sink", [(128, 4, True), (-1, 4, False)])
+@pytest.mark.parametrize("path", ["fast", "least"])
+def test_bwd_many_sequences(window, hkv, sink, path):
+    """More than 64 sequences (work items are located 64 sequences at a time): 100 ragged sequences."""
+    ga = _gpu()
+    rng = np.random.default_rng(22)
+    lengths = [int(x) for x in rng.integers(0, 41, 100)]
+    d = mi.make_layer(lengths, 16, hkv, 14, sink)
+    d.update(window=window, rope_base=1e4)
+    print(f"case bwd many sequences window={window} path={path}", flush=True)
+    O, L = _given_outputs(d)
+    dO = mi.dout_like(sum(lengths), 4, 16)
+    dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO, path)
+    rq, rk, rv, rs = oracle.prefill_bwd(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], window, 1e4,
+                                        out_given=O)
+    compare("dq", dq, rq, bf16_halfulp=True)
+    compare("dk", dk, rk, bf16_halfulp=True)
+    compare("dv", dv, rv, bf16_halfulp=True)
+    if sink:
+        compare_rel("dsink", ds, rs)

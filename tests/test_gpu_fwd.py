@@ -151,3 +151,18 @@ def test_fwd_q_rot_output(lengths, hkv, window, base):
     err = np.abs(got - ref)
     assert np.isfinite(got).all()
     assert (err <= 2.0 ** -8 * np.abs(ref) + 1e-6).all(), float(err.max())
+
+
+@pytest.mark.parametrize("window,hkv,sink", [(128, 8, True), (-1, 4, False)])
+def test_fwd_many_sequences(window, hkv, sink):
+    """More than 64 sequences (the work-item lookup reads cu_seqlens 64 at a time): 100 ragged sequences,
+    lengths 0..40, every output."""
+    ga = _gpu()
+    rng = np.random.default_rng(21)
+    lengths = [int(x) for x in rng.integers(0, 41, 100)]
+    d = _case(lengths, 16, hkv, window, 1e4, sink, 13)
+    print(f"case many sequences window={window}", flush=True)
+    out, lse = _run_fwd(ga, d)
+    ro, rl = oracle.prefill(d["q"], d["k"], d["v"], d["sink"], d["cu_seqlens"], window, 1e4)
+    compare("out", out, ro)
+    compare("lse", lse, rl)
