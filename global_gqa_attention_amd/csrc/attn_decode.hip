@@ -9,11 +9,14 @@
 //
 // Design: the step is HBM-bound (640 bytes of cache per key and KV head against 16 x 640 flops), so the
 // kernel streams each cache row exactly once.  A one-wave workgroup owns (sequence, KV head, split of
-// up to split_len rows) and walks it in 32-row chunks: K goes straight from HBM into MFMA A operands
-// (S^T = K q^T with the G query heads of the group as MFMA columns), V is staged transposed through LDS
-// for O^T = V^T P^T.  The next chunk is loaded while the current one is computed.  Each split writes an
-// unnormalised partial (o, running max, running sum); the combine kernel merges the splits with the sink
-// and the new token (whose rotation is computed there in double precision).
+// up to split_len rows) and walks it in 32-row chunks.  Each chunk's K and V rows are copied HBM -> LDS by
+// direct-to-LDS loads whose 64 lanes cover whole rows (coalesced: the rows of one KV head are 1.5 KB
+// apart in the cache); S^T = K q^T takes K rows from LDS as MFMA A operands (the G query heads of the
+// group are the MFMA columns) and O^T = V^T P^T reads V transposed.  The chunk after the current one is
+// in flight while the current one is computed; two 20 KB buffers let four workgroups share a CU, which
+// keeps more bytes in flight than deeper rings with fewer workgroups.  Each split writes an unnormalised
+// partial (o, running max, running sum); the combine kernel merges the splits with the sink and the new
+// token (whose rotation is computed there in double precision).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -21,20 +24,33 @@ namespace mimo {
 namespace {
 
 constexpr int CH = 32;            // cache rows per chunk
-constexpr int VTS = CH + 8;       // LDS stride of the V^T chunk
-
-__device__ __forceinline__ int vcol(int key4)
-{
-    const int c4 = (key4 >> 2) & 3;
-    return (key4 & ~15) | ((((c4 & 1) << 1) | (c4 >> 1)) << 2);
-}
 
 __device__ __forceinline__ double inv_freq(double base, int d) { return pow(base, -(double)d / (double)NHALF); }
 
+// LDS ring of a decode wave: chunk of CH cache rows of one KV head, K rows (chunk q of row r at
+// swz384(r, q): conflict-free 16-row operand reads) and V rows (chunk q at swz256t(r, q): conflict-free
+// transposed reads).  Two buffers: the next chunk is in flight while one is computed.
+constexpr int DKC = DQK / 8;      // 16-byte chunks per K row (24)
+constexpr int DVC = DVV / 8;      // per V row (16)
+struct DecTile {
+    uint4 k[CH * DKC];
+    uint4 v[CH * DVC];
+};
+
+// A pointer the whole wave holds the same value of, moved to scalar registers (the DMA base operand must
+// be scalar; the compiler cannot always prove uniformity through the chunk loop).
+__device__ __forceinline__ const u16 *wave_uniform(const u16 *p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const u16 *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
 {
-    __shared__ __attribute__((aligned(16))) u16 sVT[DVV * VTS];
+    __shared__ __attribute__((aligned(256))) DecTile ring[2];
     const int lane = threadIdx.x, hh = lane >> 5, c = lane & 31;
+    const int grp = lane >> 4, t4 = (lane & 15) >> 2, m4 = lane & 3;
     const int G = A.hq / A.hkv;
     const int ngrp = (G + 31) / 32;          // the group's query heads in blocks of 32 MFMA columns
     int w = blockIdx.x;
@@ -46,8 +62,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     const int b = w / A.hkv;
     if (b >= A.batch) return;
 
-    int c0 = A.cu_cache[b];
-    const int c1 = A.cu_cache[b + 1];
+    int c0 = __builtin_amdgcn_readfirstlane(A.cu_cache[b]);
+    const int c1 = __builtin_amdgcn_readfirstlane(A.cu_cache[b + 1]);
     if (A.window >= 0 && c1 - c0 > A.window) c0 = c1 - A.window;
     const int n = c1 - c0;
     const int ks = split * A.split_len;
@@ -69,6 +85,47 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
         return;
     }
 
+    // ---- the split's cache rows stream HBM -> LDS (coalesced 16-byte chunks of whole rows, fixed per-lane
+    // offsets from a wave-uniform chunk base); rows past the split's end are clamped to its last row
+    const size_t krow = (size_t)A.hkv * DQK, vrow = (size_t)A.hkv * DVV;
+    uint32_t koff[CH * DKC / 64], voff[CH * DVC / 64];
+#pragma unroll
+    for (int j = 0; j < CH * DKC / 64; ++j) {
+        const int slot = 64 * j + lane, r = slot / DKC, q = slot % DKC;
+        koff[j] = (uint32_t)((r * krow + 8 * swz384(r, q)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < CH * DVC / 64; ++j) {
+        const int slot = 64 * j + lane, r = slot / DVC, q = slot % DVC;
+        voff[j] = (uint32_t)((r * vrow + 8 * swz256t(r, q)) * 2);
+    }
+    const int klast = ks + (ke - ks - 1) / CH * CH;   // first row of the split's last chunk
+    auto issue = [&](int k, DecTile &T) __attribute__((always_inline)) {
+        k = __builtin_amdgcn_readfirstlane(min(k, klast));   // past the end: the last chunk again (uniform waits)
+        if (k + CH <= ke) {
+            const u16 *kb = wave_uniform(A.k_cache + ((size_t)(c0 + k) * A.hkv + kvh) * DQK);
+            const u16 *vb = wave_uniform(A.v_cache + ((size_t)(c0 + k) * A.hkv + kvh) * DVV);
+#pragma unroll
+            for (int j = 0; j < CH * DKC / 64; ++j) lds_dma16_nt(kb, koff[j], T.k + 64 * j);
+#pragma unroll
+            for (int j = 0; j < CH * DVC / 64; ++j) lds_dma16_nt(vb, voff[j], T.v + 64 * j);
+        } else {
+#pragma unroll
+            for (int j = 0; j < CH * DKC / 64; ++j) {
+                const int slot = 64 * j + lane, r = slot / DKC, q = slot % DKC;
+                const int row = c0 + min(k + r, ke - 1);
+                lds_dma16(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
+            }
+#pragma unroll
+            for (int j = 0; j < CH * DVC / 64; ++j) {
+                const int slot = 64 * j + lane, r = slot / DVC, q = slot % DVC;
+                const int row = c0 + min(k + r, ke - 1);
+                lds_dma16(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
+            }
+        }
+    };
+    issue(ks, ring[0]);
+
     // rotated query (bf16) as the B operand: column = head, dims 16s + 8hh + t
     bf16x8 qf[12];
     {
@@ -87,6 +144,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
             }
             rope_pair(qf[s], qf[s + 2], cs);
         }
+        // every q register is complete before the chunk loop: otherwise the compiler's own load waits for
+        // them, placed inside the loop, also stall on the cache loads in flight
+#pragma unroll
+        for (int s = 0; s < 12; ++s) asm volatile("" : "+v"(qf[s]));
     }
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -94,54 +155,30 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-    const u16 *kbase = A.k_cache + (size_t)kvh * DQK + 8 * hh;
-    const u16 *vbase = A.v_cache + (size_t)kvh * DVV;
-    const size_t krow = (size_t)A.hkv * DQK, vrow = (size_t)A.hkv * DVV;
-    const int vdc = lane & 15, vk4 = lane >> 4;   // V staging: dims 8vdc..+7, keys 4vk4..+3 (+16 second pass)
-
-    uint4 kreg[12], vreg[8];
-    auto load_chunk = [&](int k) {
-        const size_t row = (size_t)c0 + min(k + c, ke - 1);
-#pragma unroll
-        for (int s = 0; s < 12; ++s) kreg[s] = ldu4(kbase + row * krow + 16 * s);
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t vr = (size_t)c0 + min(k + 16 * p + 4 * vk4 + i, ke - 1);
-                vreg[4 * p + i] = ldu4(vbase + vr * vrow + 8 * vdc);
-            }
+    // transposed V read r of k-step s covers rows 16 s + 8 r + 4 hh + t4 and columns 32 i + 16 (grp & 1)
+    // + 4 m4 .. + 3 (the order in which the score registers hold the keys)
+    auto vtr = [&](const DecTile &T, int s, int r, int i) __attribute__((always_inline)) -> const char * {
+        const int R = 16 * s + 8 * r + 4 * hh + t4;
+        const int q = 4 * i + 2 * (grp & 1) + (m4 >> 1);
+        return (const char *)T.v + R * (DVC * 16) + 16 * swz256t(R, q) + 8 * (m4 & 1);
     };
-
-    load_chunk(ks);
-    for (int k = ks; k < ke; k += CH) {
-        __syncthreads();
+    auto chunk = [&](int k, const DecTile &T) __attribute__((always_inline)) {
+        bf16x8 kop[12];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int col = vcol(16 * p + 4 * vk4);
-            const u16 *v0 = (const u16 *)&vreg[4 * p + 0], *v1 = (const u16 *)&vreg[4 * p + 1];
-            const u16 *v2 = (const u16 *)&vreg[4 * p + 2], *v3 = (const u16 *)&vreg[4 * p + 3];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint2 wv;
-                wv.x = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
-                wv.y = (uint32_t)v2[e] | ((uint32_t)v3[e] << 16);
-                *(uint2 *)(sVT + (8 * vdc + e) * VTS + col) = wv;
-            }
-        }
+        for (int s = 0; s < 12; ++s) kop[s] = ld16((const u16 *)T.k + (c * DKC + swz384(c, 2 * s + hh)) * 8);
         f32x16 sacc = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 12; ++s) sacc = mfma32(__builtin_bit_cast(bf16x8, kreg[s]), qf[s], sacc);
-        __syncthreads();
-        if (k + CH < ke) load_chunk(k + CH);
-
+        for (int s = 0; s < 12; ++s) sacc = mfma32(kop[s], qf[s], sacc);
+        bf16x8 vop[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) vop[m] = tr_pair(vtr(T, m & 1, 0, m >> 1), vtr(T, m & 1, 1, m >> 1));
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int key = k + 8 * (j >> 2) + 4 * hh + (j & 3);
-            const float s = key < ke ? sacc[j] * A.scale_log2 : -INFINITY;
-            sacc[j] = s;
-            mx = fmaxf(mx, s);
+            const float sv = key < ke ? sacc[j] * A.scale_log2 : -INFINITY;
+            sacc[j] = sv;
+            mx = fmaxf(mx, sv);
         }
         mx = pair_max(mx);
         const float m_new = fmaxf(m_run, mx);
@@ -150,20 +187,33 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
         bf16x8 pf[2];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float p = fast_exp2(sacc[j] - m_new);
-            psum += p;
-            pf[j >> 3][j & 7] = f2bf(p);
+            const float pj = fast_exp2(sacc[j] - m_new);
+            psum += pj;
+            pf[j >> 3][j & 7] = f2bf(pj);
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             o[i] *= alpha;
-            const u16 *vr = sVT + (32 * i + c) * VTS + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) o[i] = mfma32(ld16(vr + 16 * s), pf[s], o[i]);
+            o[i] = mfma32(vop[2 * i], pf[0], o[i]);
+            o[i] = mfma32(vop[2 * i + 1], pf[1], o[i]);
         }
+    };
+
+    // ---- two-buffer ring: wait for chunk k (the only loads in flight), load chunk k + CH into the buffer
+    // computed in the previous step (its LDS reads have completed: their results were consumed), then
+    // compute chunk k; unrolled by two so each step names its buffers
+    for (int k = ks; k < ke; k += 2 * CH) {
+        wait_vmcnt<0>();
+        issue(k + CH, ring[1]);
+        chunk(k, ring[0]);
+        if (k + CH >= ke) break;
+        wait_vmcnt<0>();
+        issue(k + 2 * CH, ring[0]);
+        chunk(k + CH, ring[1]);
     }
+    wait_vmcnt<0>();                        // no load may still target this workgroup's LDS at exit
 
     const float l_tot = pair_sum(l_run);
     if (hvalid) {
