@@ -18,8 +18,8 @@
 //                 (0, 2, 1, 3), the order in which the score registers hold tokens).
 //   4. bwd_dkdv:  key-major.  A workgroup owns 128 keys of one KV head (32 per wave; the key is the MFMA
 //                 column, so each lane owns one key with its rotated k and v resident in registers) and
-//                 walks every (query head of the group, 32-query tile) that sees them: S = Q'K'^T, P,
-//                 dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q'^T dS.  The q' and dO row tiles and
+//                 walks every (query head of the group, 32-query tile) that sees them: S = Q'K'^T and
+//                 dP = dO V^T, P and dS, then dV^T += dO^T P and dK^T += Q'^T dS.  The q' and dO row tiles and
 //                 LSE/D stream HBM -> LDS with global_load_lds (three-stage ring, XOR-swizzled); the
 //                 transposed operands of dV and dK come from the same tiles through ds_read_b64_tr_b16.
 //                 With the stored-dS workspace it also writes every dS block it computes.
@@ -239,17 +239,17 @@ struct DkdvTile {
     float ld[2 * MQ];                    // LSE * log2(e) [MQ], then D [MQ]
 };
 
-// Eight waves, two per 32-key block: wave kb (0..3) computes S, P and dV^T += dO^T P of its keys, wave
-// 4 + kb the dP, dS and dK^T += Q'^T dS of the same keys one step later, taking P (fp32) from the first
-// through LDS.
-// Each wave holds half the state (k' or v, dV or dK), so two waves fit on a SIMD and interleave: one's
-// softmax VALU runs under the other's MFMAs.
+// Eight waves, two per 32-key block.  Score wave kb (0..3) holds the keys' k' and v and computes S and dP
+// from the row tiles, then P and dS; gradient wave 4 + kb holds dV and dK and, one step later, takes P and
+// dS (bf16) from the score wave through LDS for dV^T += dO^T P and dK^T += Q'^T dS (transposed operands).
+// Each wave holds half the state, so two waves fit on a SIMD and interleave: the score wave's softmax
+// and dS VALU run under the gradient wave's MFMAs.
 template <bool WIN>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
     __shared__ __attribute__((aligned(16))) DkdvTile ring[3];          // tiles of steps st-1, st, st+1
-    __shared__ __attribute__((aligned(16))) float4 pbuf[2][4][256];    // fp32 P of a step: 4 planes x 64 lanes
+    __shared__ __attribute__((aligned(16))) uint4 pbuf[2][4][256];     // P and dS (bf16) of a step: 4 planes x 64 lanes
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -370,121 +370,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     };
 
     if (role == 0) {
-        // ================= P waves: S = Q'K'^T, P, dV^T += dO^T P
-        bf16x8 kf[12];
+        // ================= score waves: S = Q'K'^T and dP = dO V^T, then P and dS = P (0.707 dP - D); P and
+        // dS (bf16) go to the gradient wave of the same keys through LDS, dS also to the stored-dS blocks
+        bf16x8 kf[12], vf[8];
         {
             const u16 *kp = A.W.kr + ((size_t)kjl * a.hkv + kvh) * DQK + 8 * hh;
 #pragma unroll
             for (int s = 0; s < 12; ++s) kf[s] = ld16(kp + 16 * s);
-        }
-        f32x16 dv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
-        // operand k: q' rows (S, k < 12), then dO^T columns (dV, k - 12 = 2 i + s)
-        auto load_op = [&](int k, const DkdvTile &T) -> bf16x8 {
-            if (k < 12) return ld16((const u16 *)T.qr + (c * QCH + swz384t(c, 2 * k + hh)) * 8);
-            const int i = (k - 12) >> 1, sk = (k - 12) & 1;
-            return tr_pair(tr_at(T.orow, OCH * 16, false, sk, 0, i), tr_at(T.orow, OCH * 16, false, sk, 1, i));
-        };
-        auto p_step = [&](int st, const DkdvTile &T, float4 *pslot) {
-            const uint32_t uba = masked(st) ? (uint32_t)ub : 0xffffffffu;
-            const int base = step_q0(st) - kjm;   // qi - kj of this lane's first row
-            constexpr int R = 2 * DK_AHEAD;
-            bf16x8 ob[R];
-#pragma unroll
-            for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, T);
-            float4 L4[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) L4[jj] = *(const float4 *)(T.ld + 8 * jj + 4 * hh);
-            f32x16 sacc = f32x16{};
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 0; k < 12; ++k) {
-                sacc = mfma32(ob[k % R], kf[k], sacc);
-                ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
-                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-            }
-            float pv[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int jj = j >> 2, t = j & 3;
-                const float Lv = t == 0 ? L4[jj].x : t == 1 ? L4[jj].y : t == 2 ? L4[jj].z : L4[jj].w;
-                pv[j] = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lv));
-            }
-            if (uba != 0xffffffffu) {   // only steps that cross the causal / window / sequence edge
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    pv[j] = (uint32_t)(base + 8 * (j >> 2) + 4 * hh + (j & 3)) <= uba ? pv[j] : 0.f;
-            }
-            uint32_t pw[8];
-#pragma unroll
-            for (int w = 0; w < 8; ++w)
-                pw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{pv[2 * w], pv[2 * w + 1]}, bf16x2));
-            const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3])),
-                                  __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]))};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                pslot[64 * jj + lane] = make_float4(pv[4 * jj], pv[4 * jj + 1], pv[4 * jj + 2], pv[4 * jj + 3]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 12; k < 20; ++k) {
-                const int i = (k - 12) >> 1;
-                dv[i] = mfma32(ob[k % R], pb[(k - 12) & 1], dv[i]);
-                if (k + DK_AHEAD < 20) ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
-                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        auto stage = [&](int st, const DkdvTile &cur, DkdvTile &fill) {
-            stage_start(st, fill);
-            if (visible(st)) p_step(st, cur, pbuf[st & 1][kq]);
-        };
-        // unrolled by three: the ring's buffers by name (stage st reads ring[st % 3], fills ring[(st+1) % 3])
-        for (int st = 0; st <= nsteps; st += 3) {
-            stage(st, ring[0], ring[1]);
-            if (st + 1 > nsteps) break;
-            stage(st + 1, ring[1], ring[2]);
-            if (st + 2 > nsteps) break;
-            stage(st + 2, ring[2], ring[0]);
-        }
-        wait_vmcnt<0>();
-        // ---- epilogue: dv = 0.707 dV^T (fp32 partials with several head splits)
-        if (kvalid && A.splits > 1) {
-            float *pp = A.dkv_part + (((size_t)split * A.T_pad + kj) * a.hkv + kvh) * (DQK + DVV) + DQK + 4 * hh;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    *(float4 *)(pp + 32 * i + 8 * jj) = make_float4(dv[i][4 * jj] * VSCALE, dv[i][4 * jj + 1] * VSCALE,
-                                                                    dv[i][4 * jj + 2] * VSCALE, dv[i][4 * jj + 3] * VSCALE);
-        } else if (kvalid) {
-            u16 *dvp = A.dv + ((size_t)kj * a.hkv + kvh) * DVV + 4 * hh;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    bf16x4 w;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) w[t] = f2bf(dv[i][4 * jj + t] * VSCALE);
-                    *(uint2 *)(dvp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
-                }
-            }
-        }
-    } else {
-        // ================= dS waves: dP = dO V^T, dS = P (0.707 dP - D), dK^T += Q'^T dS (one step behind)
-        bf16x8 vf[8];
-        {
             const u16 *vp = a.v + ((size_t)kjl * a.hkv + kvh) * DVV + 8 * hh;
 #pragma unroll
             for (int s = 0; s < 8; ++s) vf[s] = ld16(vp + 16 * s);
         }
-        f32x16 dk[6];
-#pragma unroll
-        for (int i = 0; i < 6; ++i) dk[i] = f32x16{};
-        // operand k: dO rows (dP, k < 8), then q'^T columns (dK, k - 8 = 2 i + s)
+        // operand k: q' rows (S, k < 12), then dO rows (dP, k - 12)
         auto load_op = [&](int k, const DkdvTile &T) -> bf16x8 {
-            if (k < 8) return ld16((const u16 *)T.orow + (c * OCH + swz256t(c, 2 * k + hh)) * 8);
-            const int i = (k - 8) >> 1, sk = (k - 8) & 1;
-            return tr_pair(tr_at(T.qr, QCH * 16, true, sk, 0, i), tr_at(T.qr, QCH * 16, true, sk, 1, i));
+            if (k < 12) return ld16((const u16 *)T.qr + (c * QCH + swz384t(c, 2 * k + hh)) * 8);
+            return ld16((const u16 *)T.orow + (c * OCH + swz256t(c, 2 * (k - 12) + hh)) * 8);
         };
         // dS of a step into the stored-dS blocks (query tile n, key block 4 tile + kq; see ds_row_width)
         const int s16 = seq_start & ~15;
@@ -505,53 +405,125 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), dst + 64 + (lane ^ (8 * hh) ^ 4));
             return true;
         };
-        auto ds_step = [&](int st, const DkdvTile &T, const float4 *pslot) {
+        auto s_step = [&](int st, const DkdvTile &T, uint4 *pslot) {
+            const uint32_t uba = masked(st) ? (uint32_t)ub : 0xffffffffu;
+            const int base = step_q0(st) - kjm;   // qi - kj of this lane's first row
             constexpr int R = 2 * DK_AHEAD;
             bf16x8 ob[R];
 #pragma unroll
             for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, T);
-            f32x16 dpacc = f32x16{};
-            float4 P4[4], D4[4];
+            float4 L4[4], D4[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) L4[jj] = *(const float4 *)(T.ld + 8 * jj + 4 * hh);
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                dpacc = mfma32(ob[k % R], vf[k], dpacc);
+            for (int k = 0; k < 12; ++k) {
+                sacc = mfma32(ob[k % R], kf[k], sacc);
                 ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
-                if (k == 3) {   // P and D of the step, read under the second half of the dP MFMAs
+                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            // the dP MFMAs, each followed by two of the sixteen exponentials: VALU work that needs no MFMA
+            // result of its own runs while the MFMA does
+            float pv[16];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) P4[jj] = pslot[64 * jj + lane];
+            for (int k = 12; k < 20; ++k) {
+                dpacc = mfma32(ob[k % R], vf[k - 12], dpacc);
+                if (k + DK_AHEAD < 20) ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
+#pragma unroll
+                for (int j = 2 * (k - 12); j < 2 * (k - 12) + 2; ++j) {
+                    const int jj = j >> 2, t = j & 3;
+                    const float Lv = t == 0 ? L4[jj].x : t == 1 ? L4[jj].y : t == 2 ? L4[jj].z : L4[jj].w;
+                    pv[j] = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lv));
+                }
+                if (k == 15) {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) D4[jj] = *(const float4 *)(T.ld + MQ + 8 * jj + 4 * hh);
                 }
-                if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            if (uba != 0xffffffffu) {   // only steps that cross the causal / window / sequence edge
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    pv[j] = (uint32_t)(base + 8 * (j >> 2) + 4 * hh + (j & 3)) <= uba ? pv[j] : 0.f;
+            }
+            // hand-over planes (1 KB each, lane-major): P (bf16) values 0..7 and 8..15, then dS the same way
+            uint32_t pw[8], sw[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+                pw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{pv[2 * w], pv[2 * w + 1]}, bf16x2));
+            pslot[lane] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+            pslot[64 + lane] = make_uint4(pw[4], pw[5], pw[6], pw[7]);
             float dsv[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int jj = j >> 2, t = j & 3;
                 const float Dv = t == 0 ? D4[jj].x : t == 1 ? D4[jj].y : t == 2 ? D4[jj].z : D4[jj].w;
-                const float pv = t == 0 ? P4[jj].x : t == 1 ? P4[jj].y : t == 2 ? P4[jj].z : P4[jj].w;
-                dsv[j] = pv * __builtin_fmaf(VSCALE, dpacc[j], -Dv);
+                dsv[j] = pv[j] * __builtin_fmaf(VSCALE, dpacc[j], -Dv);
             }
-            uint32_t sw[8];
 #pragma unroll
             for (int w = 0; w < 8; ++w)
                 sw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{dsv[2 * w], dsv[2 * w + 1]}, bf16x2));
             const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
                                   __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
+            pslot[128 + lane] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+            pslot[192 + lane] = make_uint4(sw[4], sw[5], sw[6], sw[7]);
+            if (A.ds) stored = store_ds(st, sb);
+        };
+        auto stage = [&](int st, const DkdvTile &cur, DkdvTile &fill) {
+            stage_start(st, fill);
+            if (visible(st)) s_step(st, cur, pbuf[st & 1][kq]);
+        };
+        // unrolled by three: the ring's buffers by name (stage st reads ring[st % 3], fills ring[(st+1) % 3])
+        for (int st = 0; st <= nsteps; st += 3) {
+            stage(st, ring[0], ring[1]);
+            if (st + 1 > nsteps) break;
+            stage(st + 1, ring[1], ring[2]);
+            if (st + 2 > nsteps) break;
+            stage(st + 2, ring[2], ring[0]);
+        }
+        wait_vmcnt<0>();
+    } else {
+        // ================= gradient waves (one step behind): dV^T += dO^T P and dK^T += Q'^T dS, with the
+        // transposed operands read from the step's row tiles and P, dS from the score wave of these keys
+        f32x16 dv[4], dk[6];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < 6; ++i) dk[i] = f32x16{};
+        // operand k: dO^T columns (dV, k = 2 i + s), then q'^T columns (dK, k - 8 = 2 i + s)
+        auto load_op = [&](int k, const DkdvTile &T) -> bf16x8 {
+            if (k < 8) {
+                const int i = k >> 1, sk = k & 1;
+                return tr_pair(tr_at(T.orow, OCH * 16, false, sk, 0, i), tr_at(T.orow, OCH * 16, false, sk, 1, i));
+            }
+            const int i = (k - 8) >> 1, sk = (k - 8) & 1;
+            return tr_pair(tr_at(T.qr, QCH * 16, true, sk, 0, i), tr_at(T.qr, QCH * 16, true, sk, 1, i));
+        };
+        auto g_step = [&](const DkdvTile &T, const uint4 *pslot) {
+            constexpr int R = 2 * DK_AHEAD;
+            bf16x8 ob[R];
+#pragma unroll
+            for (int k = 0; k < DK_AHEAD; ++k) ob[k] = load_op(k, T);
+            bf16x8 pb[2], sb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) pb[i] = __builtin_bit_cast(bf16x8, pslot[64 * i + lane]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int k = 8; k < 20; ++k) {
-                const int i = (k - 8) >> 1;
-                dk[i] = mfma32(ob[k % R], sb[(k - 8) & 1], dk[i]);
+            for (int k = 0; k < 20; ++k) {
+                if (k < 8) dv[k >> 1] = mfma32(ob[k % R], pb[k & 1], dv[k >> 1]);
+                else dk[(k - 8) >> 1] = mfma32(ob[k % R], sb[(k - 8) & 1], dk[(k - 8) >> 1]);
                 if (k + DK_AHEAD < 20) ob[(k + DK_AHEAD) % R] = load_op(k + DK_AHEAD, T);
+                if (k == 1) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) sb[i] = __builtin_bit_cast(bf16x8, pslot[128 + 64 * i + lane]);
+                }
                 if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
-            if (A.ds) stored = store_ds(st, sb);
         };
         auto stage = [&](int st, const DkdvTile &prev, DkdvTile &fill) {
             stage_start(st, fill);
-            if (st >= 1 && visible(st - 1)) ds_step(st - 1, prev, pbuf[(st - 1) & 1][kq]);
+            if (st >= 1 && visible(st - 1)) g_step(prev, pbuf[(st - 1) & 1][kq]);
         };
         // stage st reads ring[(st - 1) % 3] and fills ring[(st + 1) % 3]
         for (int st = 0; st <= nsteps; st += 3) {
@@ -562,7 +534,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             stage(st + 2, ring[1], ring[0]);
         }
         wait_vmcnt<0>();
-        // ---- epilogue: dk = R^T dK^T / sqrt(192) (fp32 partials with several head splits)
+        // ---- epilogue: dv = 0.707 dV^T, dk = R^T dK^T / sqrt(192) (fp32 partials with several head splits)
         const float2 *cs = a.rope + (size_t)min(kjl - seq_start, a.rope_len - 1) * NHALF;
         rope_back(dk[0], dk[1], cs, hh);
         if (kvalid && A.splits > 1) {
@@ -573,6 +545,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
                 for (int jj = 0; jj < 4; ++jj)
                     *(float4 *)(pp + 32 * i + 8 * jj) = make_float4(dk[i][4 * jj] * RSQRT_DQK, dk[i][4 * jj + 1] * RSQRT_DQK,
                                                                     dk[i][4 * jj + 2] * RSQRT_DQK, dk[i][4 * jj + 3] * RSQRT_DQK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    *(float4 *)(pp + DQK + 32 * i + 8 * jj) = make_float4(dv[i][4 * jj] * VSCALE, dv[i][4 * jj + 1] * VSCALE,
+                                                                          dv[i][4 * jj + 2] * VSCALE, dv[i][4 * jj + 3] * VSCALE);
         } else if (kvalid) {
             u16 *dkp = A.dk + ((size_t)kj * a.hkv + kvh) * DQK + 4 * hh;
 #pragma unroll
@@ -583,6 +561,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
 #pragma unroll
                     for (int t = 0; t < 4; ++t) w[t] = f2bf(dk[i][4 * jj + t] * RSQRT_DQK);
                     *(uint2 *)(dkp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                }
+            }
+            u16 *dvp = A.dv + ((size_t)kj * a.hkv + kvh) * DVV + 4 * hh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) w[t] = f2bf(dv[i][4 * jj + t] * VSCALE);
+                    *(uint2 *)(dvp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
                 }
             }
         }
