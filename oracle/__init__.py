@@ -59,9 +59,11 @@ def _load():
                                                i32]
         lib.oracle_decode_rows.argtypes = [P, P, P, P, P, P, P, P, i32, i32, f64, i32, i32, P, i64, P, P, i32,
                                            i32]
+        lib.oracle_prefill_cached_rows.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, f64, i32, i32, P, i64,
+                                                   P, P, i32, i32]
         lib.oracle_rope.argtypes = [P, P, i64, f64, i32, P]
         for name in ("oracle_prefill_rows", "oracle_prefill_bwd", "oracle_bwd_dq_rows", "oracle_bwd_dkv_rows",
-                     "oracle_bwd_dsink_heads", "oracle_decode_rows", "oracle_rope"):
+                     "oracle_bwd_dsink_heads", "oracle_decode_rows", "oracle_prefill_cached_rows", "oracle_rope"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -239,6 +241,25 @@ def decode_rows(q, k_new, v_new, k_cache, v_cache, cu_cache, positions, sink, wi
                                     int(window), float(rope_base), hq, hkv, _p(r), n, _p(out), _p(lse), f64,
                                     int(nthreads))
     _check(rc, "decode_rows")
+    return out, lse
+
+
+def prefill_cached_rows(q, k, v, k_cache, v_cache, cu_seqlens_q, cu_cache, positions, sink, window, rope_base,
+                        rows=None, nthreads=0):
+    """Prefill of new tokens over a cached prefix.  rows: None (all t*hq+h) or a list.  Returns (out [n,128],
+    lse [n]) in fp64."""
+    qb, kb, vb, kcb, vcb, f64 = _same(q, k, v, k_cache, v_cache)
+    cuq, cuc, pos, sk = _i32(cu_seqlens_q), _i32(cu_cache), _i32(positions), _f64(sink)
+    T, hq, hkv = qb.shape[0], qb.shape[1], kb.shape[1]
+    B = len(cuq) - 1
+    r = None if rows is None else _i64(rows)
+    n = T * hq if r is None else len(r)
+    out = np.zeros((n, DV), np.float64)
+    lse = np.zeros((n,), np.float64)
+    rc = _load().oracle_prefill_cached_rows(_p(qb), _p(kb), _p(vb), _p(kcb), _p(vcb), _p(cuq), _p(cuc), _p(pos),
+                                            _p(sk), B, int(window), float(rope_base), hq, hkv, _p(r), n, _p(out),
+                                            _p(lse), f64, int(nthreads))
+    _check(rc, "prefill_cached_rows")
     return out, lse
 
 

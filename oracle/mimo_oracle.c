@@ -44,6 +44,8 @@
  *     dq = RoPE^T(dq') = RoPE(dq', -p), dk likewise.
  *   Decode: the forward for one query at an explicit position against cache rows that already hold
  *   rotated K and unscaled V, plus the current token (rotated here).
+ *   Cached prefill: the forward for a chunk of new tokens at explicit positions against cache rows (the
+ *   keys just before the chunk, rotated K, unscaled V) plus the chunk's own keys, causally.
  */
 #include <math.h>
 #include <pthread.h>
@@ -626,6 +628,107 @@ int oracle_decode_rows(const void *q, const void *k_new, const void *v_new, cons
     dec_ctx C = {q, k_new, v_new, k_cache, v_cache, cu_cache, positions, sink, batch, n_q_heads,
                  n_kv_heads, window, rope_base, rows, out, lse, f64};
     return run_pool(dec_unit, &C, n_rows, nthreads, (size_t)maxn);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Prefill of a chunk of new tokens over a cached prefix (the rollout engine prefills long prompts in
+ * chunks against the KV cache: miles docs "MiMo-V2.6-Flash", section 3.2, chunked prefill size; the cache
+ * holds rotated K and unscaled V as in decode).  Sequence b has n_b cache rows cu_cache[b] ..
+ * cu_cache[b+1]-1, the keys at positions positions[b]-n_b .. positions[b]-1 in that order, and new tokens
+ * cu_q[b] .. cu_q[b+1]-1 at positions positions[b], positions[b]+1, ...  New token i attends the cache
+ * rows and the new tokens 0..i, limited to key positions >= its own position - window when window >= 0,
+ * with the sink in the denominator.  With no cache rows and positions 0 this is the plain prefill; a
+ * chunk of one token is decode.
+ * ------------------------------------------------------------------------------------------- */
+typedef struct {
+    const void *q, *k, *v, *kc, *vc;
+    const int32_t *cuq, *cuc, *pos;
+    const double *sink;
+    int batch, hq, hkv, window;
+    double base;
+    const int64_t *rows;
+    double *out, *lse;
+    int f64;
+} pc_ctx;
+
+static void pc_unit(void *c, int64_t r, double *s)
+{
+    pc_ctx *C = (pc_ctx *)c;
+    int64_t row = C->rows ? C->rows[r] : r;
+    int64_t t = row / C->hq;
+    int h = (int)(row % C->hq);
+    int kv = h / (C->hq / C->hkv);
+    int b = seq_of(C->cuq, C->batch, t);
+    int64_t i = t - C->cuq[b];                       /* index of the token inside its chunk */
+    int64_t n = C->cuc[b + 1] - C->cuc[b];           /* cache rows of the sequence */
+    double p = (double)C->pos[b] + (double)i;        /* position of this query */
+    double scale = 1.0 / sqrt((double)DQK);
+    double qr[DQK], kr[DQK];
+    for (int d = 0; d < DQK; ++d) qr[d] = X(C->q, ((size_t)t * C->hq + h) * DQK + d, C->f64);
+    rope(qr, p, C->base, 1.0);
+    /* keys in position order: cache rows j = 0 .. n-1, then new tokens j = n .. n+i; key j sits at
+     * position pos[b] - n + j, and the window keeps positions >= p - window */
+    int64_t nk = n + i + 1;
+    int64_t j0 = 0;
+    if (C->window >= 0 && nk - 1 - C->window > 0) j0 = nk - 1 - C->window;
+    double m = -INFINITY;
+    for (int64_t j = j0; j < nk; ++j) {
+        double acc = 0.0;
+        if (j < n) {
+            size_t kb = ((size_t)(C->cuc[b] + j) * C->hkv + kv) * DQK;
+            for (int d = 0; d < DQK; ++d) acc += qr[d] * X(C->kc, kb + d, C->f64);
+        } else {
+            size_t kb = ((size_t)(C->cuq[b] + j - n) * C->hkv + kv) * DQK;
+            for (int d = 0; d < DQK; ++d) kr[d] = X(C->k, kb + d, C->f64);
+            rope(kr, (double)C->pos[b] + (double)(j - n), C->base, 1.0);
+            for (int d = 0; d < DQK; ++d) acc += qr[d] * kr[d];
+        }
+        s[j - j0] = acc * scale;
+        if (s[j - j0] > m) m = s[j - j0];
+    }
+    double sk = C->sink ? C->sink[h] : -INFINITY;
+    if (sk > m) m = sk;
+    double z = (sk == -INFINITY) ? 0.0 : exp(sk - m);
+    for (int64_t j = j0; j < nk; ++j) z += exp(s[j - j0] - m);
+    double l = m + log(z);
+    double o[DV] = {0};
+    for (int64_t j = j0; j < nk; ++j) {
+        double pj = exp(s[j - j0] - l);
+        const void *vt = (j < n) ? C->vc : C->v;
+        size_t vb = (j < n) ? ((size_t)(C->cuc[b] + j) * C->hkv + kv) * DV
+                            : ((size_t)(C->cuq[b] + j - n) * C->hkv + kv) * DV;
+        for (int e = 0; e < DV; ++e) o[e] += pj * (VSCALE * X(vt, vb + e, C->f64));
+    }
+    memcpy(C->out + (size_t)r * DV, o, sizeof o);
+    if (C->lse) C->lse[r] = l;
+}
+
+int oracle_prefill_cached_rows(const void *q, const void *k, const void *v, const void *k_cache,
+                               const void *v_cache, const int32_t *cu_q, const int32_t *cu_cache,
+                               const int32_t *positions, const double *sink, int batch, int window,
+                               double rope_base, int n_q_heads, int n_kv_heads, const int64_t *rows,
+                               int64_t n_rows, double *out, double *lse, int f64, int nthreads)
+{
+    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || window < -1)
+        return -1;
+    if (batch == 0) return 0;
+    if (cu_q[0] != 0 || cu_cache[0] != 0) return -1;
+    int64_t maxk = 1;
+    for (int b = 0; b < batch; ++b) {
+        if (cu_q[b + 1] < cu_q[b] || cu_cache[b + 1] < cu_cache[b]) return -1;
+        int64_t n = cu_cache[b + 1] - cu_cache[b];
+        if (positions[b] < n) return -1;             /* the cache rows precede the chunk */
+        int64_t nk = n + (cu_q[b + 1] - cu_q[b]);
+        if (nk > maxk) maxk = nk;
+    }
+    int64_t all = (int64_t)cu_q[batch] * n_q_heads;
+    if (rows == NULL) n_rows = all;
+    for (int64_t r = 0; rows && r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= all) return -1;
+    if (n_rows == 0) return 0;
+    pc_ctx C = {q, k, v, k_cache, v_cache, cu_q, cu_cache, positions, sink, batch, n_q_heads, n_kv_heads,
+                window, rope_base, rows, out, lse, f64};
+    return run_pool(pc_unit, &C, n_rows, nthreads, (size_t)maxk);
 }
 
 /* The rotation alone, for tests: rows of 192 bf16 values at the given positions -> rotated fp64. */

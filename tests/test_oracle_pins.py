@@ -445,6 +445,79 @@ def test_decode_window_takes_last_rows():
     np.testing.assert_array_equal(a, b)
 
 
+# --------------------------------------------------------------------------------------------------------
+# cached prefill (a chunk of new tokens over a cached prefix)
+# --------------------------------------------------------------------------------------------------------
+def split_for_cache(q, k, v, lengths, splits, base, keep=None):
+    """The second parts of the sequences as a chunk over a cache that holds the first parts' rotated K
+    (independent complex RoPE) and V; keep: cache only the last `keep` rows of each first part."""
+    starts = np.concatenate([[0], np.cumsum(lengths)])
+    qc, kn, vn, kc, vc, cuq, cuc, pos, rows = [], [], [], [], [], [0], [0], [], []
+    for b, (n, s) in enumerate(zip(lengths, splits)):
+        first = np.arange(starts[b], starts[b] + s)
+        second = np.arange(starts[b] + s, starts[b] + n)
+        c = first if keep is None else first[max(0, s - keep):]
+        kc.append(torch.from_numpy(rope_complex(k[c].numpy(), c - starts[b], base)))
+        vc.append(v[c])
+        qc.append(q[second]); kn.append(k[second]); vn.append(v[second])
+        cuq.append(cuq[-1] + len(second)); cuc.append(cuc[-1] + len(c)); pos.append(s)
+        rows.extend(second.tolist())
+    return (torch.cat(qc), torch.cat(kn), torch.cat(vn), torch.cat(kc), torch.cat(vc), np.array(cuq),
+            np.array(cuc), np.array(pos), np.array(rows))
+
+
+@pytest.mark.parametrize("window,base,with_sink,keep", [(128, 1e4, True, None), (7, 1e4, True, 7),
+                                                        (-1, 1e7, False, None), (0, 1e4, True, 0)])
+def test_cached_prefill_continues_a_prefill(window, base, with_sink, keep):
+    """Prefill of the later tokens over a cache of the earlier ones equals the same rows of the whole
+    prefill (the cache may drop rows outside the window)."""
+    lengths, splits = [300, 140, 5, 1, 33], [170, 0, 5, 0, 32]
+    q, k, v, s, cu = f64_layer(lengths, 8, 2, 31, with_sink)
+    o_pre, l_pre = oracle.prefill(q, k, v, s, cu, window, base, nthreads=2)
+    qc, kn, vn, kc, vc, cuq, cuc, pos, rows = split_for_cache(q, k, v, lengths, splits, base, keep)
+    out, lse = oracle.prefill_cached_rows(qc, kn, vn, kc, vc, cuq, cuc, pos, s, window, base, nthreads=2)
+    np.testing.assert_allclose(out.reshape(-1, 8, DV), o_pre[rows], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(lse.reshape(-1, 8), l_pre[:, rows].T, rtol=0, atol=1e-10)
+
+
+def test_cached_prefill_without_cache_is_prefill():
+    lengths = [40, 0, 17]
+    q, k, v, s, cu = f64_layer(lengths, 4, 2, 32)
+    for window in (5, -1):
+        o_pre, l_pre = oracle.prefill(q, k, v, s, cu, window, 1e4)
+        empty = torch.zeros(0, 2, DQK, dtype=torch.float64)
+        out, lse = oracle.prefill_cached_rows(q, k, v, empty, torch.zeros(0, 2, DV, dtype=torch.float64), cu,
+                                              np.zeros(4, np.int32), np.zeros(3, np.int32), s, window, 1e4)
+        np.testing.assert_allclose(out.reshape(-1, 4, DV), o_pre, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse.reshape(-1, 4), l_pre.T, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [-1, 6, 50])
+def test_cached_prefill_chunk_of_one_is_decode(window):
+    g = torch.Generator().manual_seed(33)
+    B, hq, hkv, n = 3, 4, 2, 20
+    q = torch.randn(B, hq, DQK, generator=g, dtype=torch.float64)
+    kn = torch.randn(B, hkv, DQK, generator=g, dtype=torch.float64)
+    vn = torch.randn(B, hkv, DV, generator=g, dtype=torch.float64)
+    kc = torch.randn(B * n, hkv, DQK, generator=g, dtype=torch.float64)
+    vc = torch.randn(B * n, hkv, DV, generator=g, dtype=torch.float64)
+    cc = np.arange(B + 1) * n
+    pos = np.array([20, 900, 131072])
+    sink = torch.randn(hq, generator=g, dtype=torch.float64)
+    a, la = oracle.decode_rows(q, kn, vn, kc, vc, cc, pos, sink, window, 1e4)
+    b, lb = oracle.prefill_cached_rows(q, kn, vn, kc, vc, np.arange(B + 1), cc, pos, sink, window, 1e4)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-12)
+
+
+def test_cached_prefill_rejects_cache_longer_than_position():
+    q, k, v, s, cu = f64_layer([4], 2, 1, 34)
+    kc = torch.zeros(5, 1, DQK, dtype=torch.float64)
+    vc = torch.zeros(5, 1, DV, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        oracle.prefill_cached_rows(q, k, v, kc, vc, cu, np.array([0, 5]), np.array([4]), s, -1, 1e4)
+
+
 def test_oracle_rejects_bad_arguments():
     q, k, v, s, cu = f64_layer([10], 4, 3, 27)
     with pytest.raises(ValueError):
