@@ -6,7 +6,9 @@ One step = the whole hot path of one training pass over the synthetic batch: the
 the timed region.  FLOPs are algorithmic: attended (query, key) pairs x 640 (forward) and x 1664 (backward).
 
 The decode step (batch 64, SWA ring of 128 + sink; global cache lengths in [8192, 131072]) is timed in the
-same run and reported as GB/s of cache traffic under "decode"; it is not part of the step's value.
+same run and reported as GB/s of cache traffic under "decode"; the prefill forward alone ("prefill") and a
+prefill of 16 chunks over cached prefixes ("prefill_cached") likewise.  None of them is part of the step's
+value.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 
@@ -328,6 +330,60 @@ def run_prefill(ga, torch, layers, reps=10):
     return res
 
 
+def cached_pairs(chunks, cache_rows, window):
+    """Attended (query, key) pairs per head of a chunk over cached prefixes: new token i of a sequence with n
+    cache rows (the keys just before it) sees n + i + 1 keys, at most window + 1."""
+    tot = 0
+    for L, n in zip(chunks, cache_rows):
+        for i in range(L):
+            keys = n + i + 1
+            tot += keys if window < 0 else min(keys, window + 1)
+    return tot
+
+
+def run_prefill_cached(ga, torch, mi, reps=10):
+    """Prefill of a chunk over cached prefixes (16 sequences, prefixes 2048..8192, chunks 1024..2048), each
+    layer alone: median per-launch times of its kernels over `reps` calls and algorithmic FLOPs."""
+    res = {}
+    both = mi.chunked_16(device="cuda")
+    for lname in ("swa", "glb"):
+        d = both[lname]
+        T, hq, hkv = d["q"].shape[0], d["q"].shape[1], d["k"].shape[1]
+        Tc = d["k_cache"].shape[0]
+        ws = torch.empty(ga.prefill_cached_workspace_size(T, Tc, hkv), dtype=torch.uint8, device="cuda")
+        out = torch.empty(T, hq, 128, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(hq, T, dtype=torch.float32, device="cuda")
+        call = lambda: ga.prefill_cached(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["sink"],  # noqa
+                                         d["cu_seqlens"], d["cu_cache"], d["positions"], max(d["lengths"]),
+                                         d["max_position"], d["window"], d["rope_base"], out=out, lse=lse,
+                                         workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ga.trace_read(clear=True)
+        ga.trace_enable(True)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        ga.trace_enable(False)
+        per = {}
+        for name, ms in ga.trace_read(clear=True):
+            per.setdefault(name.rsplit("_", 1)[0], []).append(ms)
+        med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
+        attn = med.get("attn_fwd", 0.0)
+        total = attn + med.get("kv_prep_cached", 0.0)
+        pairs = cached_pairs(d["lengths"], d["cache_rows"], d["window"]) * hq
+        flop = pairs * FWD_FLOP_PER_PAIR
+        res[lname] = {"new_tokens": T, "cache_rows": Tc, "ms": round(total, 4), "attn_fwd_ms": round(attn, 4),
+                      "TFLOP/s": round(flop / (total * 1e-3) / 1e12, 1),
+                      "frac_of_mfma_peak": round(flop / (total * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "attn_fwd_TFLOP/s": round(flop / (attn * 1e-3) / 1e12, 1)}
+        del d, ws, out, lse
+    del both
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -434,6 +490,7 @@ def main():
         "layers": layer_tflops, "kernels": kernels, "roofline": roofline,
     }
     line["prefill"] = run_prefill(ga, torch, layers)
+    line["prefill_cached"] = run_prefill_cached(ga, torch, mi)
     if not args.no_decode:
         line["decode"] = run_decode(ga, torch, mi)
     if not args.no_cpu_baseline:

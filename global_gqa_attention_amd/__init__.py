@@ -48,6 +48,10 @@ def lib():
         L.mimo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
         L.mimo_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_decode.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
+        L.mimo_attn_prefill_cached_workspace_size.argtypes = [i32, i32, i32]
+        L.mimo_attn_prefill_cached_workspace_size.restype = sz
+        L.mimo_attn_prefill_cached.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32,
+                                               i32, P, P, P, sz, P]
         L.mimo_attn_status_string.argtypes = [ctypes.c_int]
         L.mimo_attn_last_error.argtypes = []
         L.mimo_attn_release.argtypes = []
@@ -59,7 +63,7 @@ def lib():
         L.mimo_attn_trace_count.restype = i32
         L.mimo_attn_trace_read.restype = ctypes.c_int
         L.mimo_attn_trace_clear.restype = None
-        for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode"):
+        for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_prefill_cached"):
             getattr(L, f).restype = ctypes.c_int
         L.mimo_attn_bwd_workspace_size.restype = sz
         L.mimo_attn_decode_workspace_size.restype = sz
@@ -212,6 +216,41 @@ def decode(q, k_new, v_new, k_cache, v_cache, cu_cache, positions, sink, max_cac
                                 hq, hkv, _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(rc, "mimo_attn_decode")
     return out
+
+
+def prefill_cached_workspace_size(total_tokens, total_cache, n_kv_heads) -> int:
+    return int(lib().mimo_attn_prefill_cached_workspace_size(int(total_tokens), int(total_cache), int(n_kv_heads)))
+
+
+def prefill_cached(q, k, v, k_cache, v_cache, sink, cu_seqlens, cu_cache, positions, max_seqlen, max_position,
+                   window, rope_base, out=None, lse=None, return_lse=True, workspace=None):
+    """Prefill of new tokens (q, k, v THD-packed by cu_seqlens) over cached prefixes (k_cache rotated, v_cache,
+    rows of sequence b: cu_cache[b] .. cu_cache[b+1]-1; first new token at positions[b]).  Returns (out bf16
+    [T,hq,128], lse fp32 [hq,T] or None)."""
+    T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16)
+    Tc = k_cache.shape[0]
+    _need(k_cache, "k_cache", torch.bfloat16, (Tc, hkv, DQK))
+    _need(v_cache, "v_cache", torch.bfloat16, (Tc, hkv, DV))
+    _need(cu_cache, "cu_cache", torch.int32, (batch + 1,))
+    _need(positions, "positions", torch.int32, (batch,))
+    if workspace is None:
+        workspace = torch.empty((max(prefill_cached_workspace_size(T, Tc, hkv), 1),), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((T, hq, DV), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (T, hq, DV))
+    if return_lse and lse is None:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (hq, T))
+    rc = lib().mimo_attn_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(sink),
+                                        _ptr(cu_seqlens), _ptr(cu_cache), _ptr(positions), batch, T, Tc,
+                                        int(max_seqlen), int(max_position), int(window), float(rope_base), hq, hkv,
+                                        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(rc, "mimo_attn_prefill_cached")
+    return out, lse
 
 
 def release():

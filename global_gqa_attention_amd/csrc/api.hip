@@ -262,6 +262,68 @@ size_t mimo_attn_fwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int
     return mimo::fwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
 }
 
+size_t mimo_attn_prefill_cached_workspace_size(int32_t total_tokens, int32_t total_cache, int32_t n_kv_heads)
+{
+    if (total_tokens < 0 || total_cache < 0 || n_kv_heads <= 0) return 0;
+    if ((long long)total_tokens + total_cache > 0x7fffff00LL) return 0;
+    return mimo::prep_bytes(total_tokens + total_cache, n_kv_heads);
+}
+
+mimo_status_t mimo_attn_prefill_cached(const void *q, const void *k, const void *v, const void *k_cache,
+                                       const void *v_cache, const float *sink, const int32_t *cu_seqlens,
+                                       const int32_t *cu_cache, const int32_t *positions, int32_t batch,
+                                       int32_t total_tokens, int32_t total_cache, int32_t max_seqlen,
+                                       int32_t max_position, int32_t window, double rope_base,
+                                       int32_t n_q_heads, int32_t n_kv_heads, void *out, float *lse,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    mimo_status_t s = check_layer(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base,
+                                  n_q_heads, n_kv_heads);
+    if (s != MIMO_OK) return s;
+    if (total_cache < 0) return fail(MIMO_ERR_INVALID_ARG, "total_cache must be >= 0 (got %d)", total_cache);
+    if ((long long)total_tokens + total_cache > 0x7fffff00LL)
+        return fail(MIMO_ERR_UNSUPPORTED, "total_tokens + total_cache too large");
+    if (max_position < max_seqlen)
+        return fail(MIMO_ERR_INVALID_ARG, "max_position (%d) must be >= max_seqlen (%d)", max_position, max_seqlen);
+    if (batch > 0 && (!cu_cache || !positions)) return fail(MIMO_ERR_INVALID_ARG, "cu_cache or positions is null");
+    if (total_cache > 0 && (!k_cache || !v_cache)) return fail(MIMO_ERR_INVALID_ARG, "null cache pointer");
+    if (total_tokens > 0 && !out) return fail(MIMO_ERR_INVALID_ARG, "out is null");
+    if (!mimo::fwd_group_supported(n_q_heads / n_kv_heads))
+        return fail(MIMO_ERR_UNSUPPORTED, "no forward kernel for group size %d", n_q_heads / n_kv_heads);
+    if (total_tokens == 0) return ok();
+    if ((long long)(total_tokens + total_cache) * n_kv_heads * kDQK > (1LL << 40))
+        return fail(MIMO_ERR_UNSUPPORTED, "tensor too large");
+    const size_t need = mimo::prep_bytes(total_tokens + total_cache, n_kv_heads);
+    if (!workspace || workspace_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    mimo::FwdArgs a{};
+    mimo::prep_carve(workspace, total_tokens + total_cache, n_kv_heads, &a.P);
+    s = rope_table(rope_base, max_position, st, &a.L.rope, &a.L.rope_len);
+    if (s != MIMO_OK) return s;
+    a.L.q = (const uint16_t *)q;
+    a.L.k = (const uint16_t *)k;
+    a.L.v = (const uint16_t *)v;
+    a.L.sink = sink;
+    a.L.cu = cu_seqlens;
+    a.L.batch = batch;
+    a.L.T = total_tokens;
+    a.L.window = window;
+    a.L.hq = n_q_heads;
+    a.L.hkv = n_kv_heads;
+    a.L.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kDQK));
+    a.C.k_cache = (const uint16_t *)k_cache;
+    a.C.v_cache = (const uint16_t *)v_cache;
+    a.C.cu_cache = cu_cache;
+    a.C.positions = positions;
+    a.C.Tc = total_cache;
+    a.out = (uint16_t *)out;
+    a.lse = lse;
+    hipError_t e = mimo::launch_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "cached prefill launch");
+    return ok();
+}
+
 size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
                                     int32_t window)
 {

@@ -93,12 +93,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     const int t0 = seq_start + tr * TT;
     const int t_last = min(t0 + TT - 1, seq_end - 1);
     const int h0 = kvh * G + hgi * GP;
+    // key stream of the sequence: its first key is kseq, query token t sits at key index t + kofs and at
+    // RoPE position t + pofs (without a cache: the tokens themselves, positions from the sequence start)
+    int kofs = 0, kseq = seq_start, pofs = -seq_start;
+    if (A.C.cu_cache) {
+        const int c0 = A.C.cu_cache[sp.b], c1 = A.C.cu_cache[sp.b + 1];
+        kofs = c1;
+        kseq = c0 + seq_start;
+        pofs = A.C.positions[sp.b] - seq_start;
+    }
 
-    // ---- key range: tiles start on a 16-token boundary (the V^T chunk order is per 16 tokens); keys of a
+    // ---- key range: tiles start on a 16-key boundary (the V^T chunk order is per 16 keys); keys of a
     // previous sequence that this brings in are masked
-    const int klo = WIN ? max(seq_start, t0 - a.window) : seq_start;
+    const int klo = WIN ? max(kseq, t0 + kofs - a.window) : kseq;
     const int kstart = klo & ~15;
-    const int khi = t_last;
+    const int khi = t_last + kofs;
     const int nkt = (khi - kstart + BN) / BN;
 
     // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = NT j + tid of each array): the
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         const u16 *qp = a.q + ((size_t)qtl * a.hq + qh) * DQK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
-        const float2 *cs = a.rope + (size_t)min(qtl - seq_start, a.rope_len - 1) * NHALF + 8 * hh;
+        const float2 *cs = a.rope + (size_t)min(max(qtl + pofs, 0), a.rope_len - 1) * NHALF + 8 * hh;
         float2 c0[8], c1[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -154,10 +163,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         }
     }
 
-    // this wave's rows span tokens [wt0, wt1]; 32-key blocks outside [wklo, wkhi] are skipped
-    const int wt0 = t0 + (wave * 32) / GP;
-    const int wt1 = min(t0 + (wave * 32 + 31) / GP, seq_end - 1);
-    const int wklo = WIN ? max(seq_start, wt0 - a.window) : seq_start;
+    // this wave's rows sit at key indices [wt0, wt1]; 32-key blocks outside [wklo, wkhi] are skipped
+    const int wt0 = t0 + (wave * 32) / GP + kofs;
+    const int wt1 = min(t0 + (wave * 32 + 31) / GP, seq_end - 1) + kofs;
+    const int wklo = WIN ? max(kseq, wt0 - a.window) : kseq;
     const int wkhi = wt1;
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -175,7 +184,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     // ---- one tile: S^T = K Q^T, online softmax, O^T += V^T P^T (two 32-key blocks).  The V^T operands of a
     // block are read before its softmax, so they land while the softmax runs.
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-    const uint32_t ub = (uint32_t)(WIN ? min(a.window, qt - seq_start) : qt - seq_start);
+    const int qk = qt + kofs;   // this row's key index
+    const uint32_t ub = (uint32_t)(WIN ? min(a.window, qk - kseq) : qk - kseq);
     auto compute_tile = [&](int k0, const uint4 *skb, const uint4 *svb) {
         const u16 *kt = (const u16 *)skb;
         const u16 *vtt = (const u16 *)svb;
@@ -208,9 +218,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
             __builtin_amdgcn_sched_barrier(0);
             float sv[16];
             float mxa = -INFINITY, mxb = -INFINITY;
-            const bool need_mask = (kbase + 31 > wt0) || (kbase < seq_start) || (WIN && kbase < wt1 - a.window);
+            const bool need_mask = (kbase + 31 > wt0) || (kbase < kseq) || (WIN && kbase < wt1 - a.window);
             if (need_mask) {
-                const int dlt = qt - (kbase + 4 * hh);
+                const int dlt = qk - (kbase + 4 * hh);
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int cj = 8 * (j >> 2) + (j & 3);
@@ -364,7 +374,7 @@ bool fwd_group_supported(int group) { return group >= 1; }
 hipError_t launch_fwd(const FwdArgs &A, hipStream_t stream)
 {
     const LayerArgs &a = A.L;
-    hipError_t e = launch_kv_prep(a, A.P, stream);
+    hipError_t e = A.C.cu_cache ? launch_kv_prep_cached(a, A.P, A.C, stream) : launch_kv_prep(a, A.P, stream);
     if (e != hipSuccess) return e;
     const int G = a.hq / a.hkv;
     // pack up to 8 heads of a group: 32 tokens x 8 heads per workgroup for sliding-window layers (short key

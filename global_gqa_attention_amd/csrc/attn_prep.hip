@@ -9,7 +9,8 @@
 //                              stored in the order (0, 2, 1, 3): an MFMA operand read of 8 consecutive
 //                              elements then returns the keys in the order the score registers hold them.
 // Tokens T .. T_pad-1 are written as zeros (tiles may read them; they are masked, and zero values keep the
-// masked products finite).
+// masked products finite).  For a prefill over a cached prefix the same two tensors cover one key stream
+// per sequence: its cache rows (K already rotated), then its new tokens.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -95,6 +96,105 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const LayerArgs a, KVPrep 
     }
 }
 
+// Sequence b of the combined key stream (cache rows, then new tokens) that holds key index u: the b with
+// cu_cache[b] + cu[b] <= u < cu_cache[b+1] + cu[b+1].
+__device__ __forceinline__ int seq_of_keys(const int32_t *cu, const int32_t *cuc, int batch, int u)
+{
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cuc[mid] + cu[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// The same layout as kv_prep_kernel over the combined key stream of a cached prefill: key u of sequence b
+// is cache row cu_cache[b] + j (already rotated: copied) for j = u - (cu_cache[b] + cu[b]) < n_b, else new
+// token cu[b] + j - n_b, rotated at position positions[b] + j - n_b.
+__global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, KVPrep p, const CacheArgs C)
+{
+    __shared__ __attribute__((aligned(16))) u16 sV[PT * (DVV + 8)];
+    const int tid = threadIdx.x;
+    const int kvh = blockIdx.y;
+    const int t0 = blockIdx.x * PT;
+    const int Tk = a.T + C.Tc;
+    // source rows of key u: (K row, V row, rotation position or -1 for a cache row)
+    auto source = [&](int u, const u16 *&ks, const u16 *&vs, int &pos) {
+        const int b = seq_of_keys(a.cu, C.cu_cache, a.batch, u);
+        const int j = u - (C.cu_cache[b] + a.cu[b]);
+        const int n = C.cu_cache[b + 1] - C.cu_cache[b];
+        if (j < n) {
+            const size_t row = (size_t)(C.cu_cache[b] + j) * a.hkv + kvh;
+            ks = C.k_cache + row * DQK;
+            vs = C.v_cache + row * DVV;
+            pos = -1;
+        } else {
+            const size_t row = (size_t)(a.cu[b] + j - n) * a.hkv + kvh;
+            ks = a.k + row * DQK;
+            vs = a.v + row * DVV;
+            pos = C.positions[b] + j - n;
+        }
+    };
+
+    // ---- K: key t0 + tid/4, chunk group tid%4 (chunks cg, cg+4 rotated for new tokens; 8+cg+4i copied)
+    {
+        const int u = t0 + (tid >> 2), cg = tid & 3;
+        u16 *dst = p.kr + ((size_t)u * a.hkv + kvh) * DQK;
+        if (u < Tk) {
+            const u16 *src, *vs;
+            int pos;
+            source(u, src, vs, pos);
+            bf16x8 x0 = ld16(src + 8 * cg), x1 = ld16(src + 8 * (cg + 4));
+            if (pos >= 0) {
+                const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;
+                float2 c8[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c8[i] = cs[i];
+                rope_pair(x0, x1, c8);
+            }
+            st16(dst + 8 * cg, x0);
+            st16(dst + 8 * (cg + 4), x1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), ldu4(src + 8 * (8 + cg + 4 * i)));
+        } else if (u < p.T_pad) {
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            st16u(dst + 8 * cg, z);
+            st16u(dst + 8 * (cg + 4), z);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), z);
+        }
+    }
+    // ---- V^T: stage 64 keys x 128 dims in LDS, then write rows of 8 keys (permuted order)
+    {
+        const int r = tid >> 2, cg = tid & 3;
+        const int u = t0 + r;
+        const u16 *ks = nullptr, *vs = nullptr;
+        int pos = 0;
+        if (u < Tk) source(u, ks, vs, pos);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = cg + 4 * i;
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (u < Tk) x = ldu4(vs + 8 * ch);
+            *(uint4 *)(sV + r * (DVV + 8) + 8 * ch) = x;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int item = tid + 256 * i;          // 128 dims x 8 column chunks
+        const int d = item >> 3, cc = item & 7;  // cc: columns 8cc..8cc+7 of the tile
+        if (t0 + 8 * cc >= p.T_pad) continue;
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tok = vperm16(8 * cc + e);
+            w[e] = __builtin_bit_cast(__bf16, sV[tok * (DVV + 8) + d]);
+        }
+        st16(p.vt + ((size_t)kvh * DVV + d) * p.T_pad + t0 + 8 * cc, w);
+    }
+}
+
 }  // namespace
 
 size_t prep_bytes(int T, int hkv)
@@ -111,6 +211,15 @@ void prep_carve(void *ws, int T, int hkv, KVPrep *p)
     p->kr = (uint16_t *)ws;
     const size_t kr = ((size_t)p->T_pad * hkv * DQK * 2 + 255) & ~(size_t)255;
     p->vt = (uint16_t *)((char *)ws + kr);
+}
+
+hipError_t launch_kv_prep_cached(const LayerArgs &a, const KVPrep &p, const CacheArgs &c, hipStream_t stream)
+{
+    dim3 grid((p.T_pad + PT - 1) / PT, a.hkv);
+    trace_begin(a.window >= 0 ? "kv_prep_cached_swa" : "kv_prep_cached_global", stream);
+    kv_prep_cached_kernel<<<grid, 256, 0, stream>>>(a, p, c);
+    trace_end(stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_kv_prep(const LayerArgs &a, const KVPrep &p, hipStream_t stream)

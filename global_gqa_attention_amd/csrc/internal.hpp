@@ -25,9 +25,22 @@ inline int prep_tpad(int T) { return (T + 15) / 16 * 16 + 64; }
 size_t prep_bytes(int T, int hkv);
 void prep_carve(void *ws, int T, int hkv, KVPrep *p);
 
+// A cached prefix in front of the new tokens (prefill of a chunk against the KV cache).  Sequence b has
+// cache rows cu_cache[b] .. cu_cache[b+1]-1: the keys just before its new tokens, in position order, with
+// RoPE already applied to K and V unscaled; its first new token sits at positions[b].  The prep kernel
+// lays the cache rows and the new tokens' keys out as one key stream per sequence (sequence b's keys start
+// at cu_cache[b] + cu[b]), so the key index of new token t is t + cu_cache[b+1].
+struct CacheArgs {
+    const uint16_t *k_cache, *v_cache;   // bf16 [Tc,hkv,192] (rotated), [Tc,hkv,128]
+    const int32_t *cu_cache;             // [batch+1], or nullptr: no cache (plain prefill)
+    const int32_t *positions;            // [batch]
+    int Tc;                              // cache rows in all
+};
+
 struct FwdArgs {
     LayerArgs L;
-    KVPrep P;
+    KVPrep P;                      // keys of the cached prefix and the new tokens when C.cu_cache is set
+    CacheArgs C;
     uint16_t *out;                 // bf16 [T,hq,128]
     float *lse;                    // fp32 [hq,T] or nullptr
     uint16_t *q_rot;               // bf16 [T,hq,192] rotated q, or nullptr
@@ -81,6 +94,7 @@ void trace_end(hipStream_t stream);
 
 // Returns hipSuccess or the launch error.  Each launcher picks its kernel variant from the arguments.
 hipError_t launch_kv_prep(const LayerArgs &a, const KVPrep &p, hipStream_t stream);
+hipError_t launch_kv_prep_cached(const LayerArgs &a, const KVPrep &p, const CacheArgs &c, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -145,6 +145,41 @@ mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_n
                                double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace mimo_attn_prefill_cached needs (0 for invalid sizes). */
+size_t mimo_attn_prefill_cached_workspace_size(int32_t total_tokens, int32_t total_cache, int32_t n_kv_heads);
+
+/* Prefill of a chunk of new tokens over a cached prefix: the serving engine prefills long prompts in chunks
+ * (up to 49152 tokens) against its KV cache.  Source: SGLang cookbook page "MiMo-V2.6", section 2
+ * "Configuration tips", "Context length and memory" (chunked prefill size, page size 1).
+ *   q, k, v   the new tokens, THD-packed as in mimo_attn_fwd: bf16 [total_tokens, n_q_heads, 192],
+ *             [total_tokens, n_kv_heads, 192] (both un-rotated), [total_tokens, n_kv_heads, 128] (unscaled)
+ *   k_cache   bf16 [total_cache, n_kv_heads, 192]  cached keys, ALREADY rotated at their own positions
+ *   v_cache   bf16 [total_cache, n_kv_heads, 128]  cached values, unscaled
+ *   sink      fp32 [n_q_heads] or NULL
+ *   cu_seqlens int32 [batch + 1] device: new tokens of sequence b are cu_seqlens[b] .. cu_seqlens[b+1]-1
+ *   cu_cache  int32 [batch + 1] device: sequence b's cache rows cu_cache[b] .. cu_cache[b+1]-1 are the n_b
+ *             keys just before its new tokens, in position order (a sliding-window layer may keep only the
+ *             last rows; rows older than the window are never read by the math, so they may be absent)
+ *   positions int32 [batch] device: position of sequence b's first new token; cache row j of b sits at
+ *             position positions[b] - n_b + j, new token i at positions[b] + i.  positions[b] >= n_b.
+ *   max_seqlen >= every new-token count; max_position >= every positions[b] + (new tokens of b) (the RoPE
+ *             table is built up to it; larger positions are clamped to its last entry)
+ *   window    -1 (causal over cache and chunk) or >= 0 (each new token sees itself plus `window` previous
+ *             keys, cache rows included)
+ *   out       bf16 [total_tokens, n_q_heads, 128];  lse fp32 [n_q_heads, total_tokens] or NULL
+ *   workspace at least mimo_attn_prefill_cached_workspace_size() bytes of device memory (the prepared key
+ *             stream: cache rows and the chunk's rotated keys per sequence)
+ * New token i of sequence b gets exactly the row that mimo_attn_fwd gives token n_b + i of the whole
+ * sequence whose first n_b tokens are the cache; with no cache rows and positions 0 this is mimo_attn_fwd.
+ * The cache is read, never written. */
+mimo_status_t mimo_attn_prefill_cached(const void *q, const void *k, const void *v, const void *k_cache,
+                                       const void *v_cache, const float *sink, const int32_t *cu_seqlens,
+                                       const int32_t *cu_cache, const int32_t *positions, int32_t batch,
+                                       int32_t total_tokens, int32_t total_cache, int32_t max_seqlen,
+                                       int32_t max_position, int32_t window, double rope_base,
+                                       int32_t n_q_heads, int32_t n_kv_heads, void *out, float *lse,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Per-kernel tracing.  While enabled, every entry point records a HIP event on the caller's stream before
  * and after each kernel it launches (the events only mark the stream; nothing is synchronised).  The
  * records accumulate until mimo_attn_trace_clear(); reading one waits for its end event.  Not thread-safe

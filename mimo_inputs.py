@@ -21,6 +21,13 @@ otherwise, ``randn`` in fp32, then rounded to bf16 round-to-nearest-even by ``.t
   sink (SWA), then the cache (K, then V).  The global cache (about 11 GB) is drawn on the device with a
   device generator seeded the same way when ``device`` is a GPU, since the CPU stream would take minutes;
   its first-kind recipe is then ``torch.Generator(device).manual_seed(seed + 1000)``.
+* cached prefill (``make_cached``): new tokens (q, k, v) per sequence plus cache rows standing for the keys
+  just before them (random bf16 K treated as already rotated, and V); sequence b's first new token sits at
+  position prefix_b, and its cache holds the last min(prefix_b, keep) rows (keep None: the whole prefix).
+  Draw order: q, k, v of the new tokens, sink, then the cache (K, then V).  ``chunked_16`` (seed 5): 16
+  sequences, prefixes drawn by ``randint(2048, 8193)``, chunks by ``randint(1024, 2049)``, then the tensors
+  of the global layer (4 KV heads, whole prefix cached, base 1e7, no sink) and of the SWA layer (8 KV heads,
+  the last 128 rows cached, window 128, sink, base 1e4).
 """
 from __future__ import annotations
 
@@ -137,3 +144,32 @@ def decode_global(batch=64, n_kv_heads=4, seed=3, device="cpu", len_lo=8192, len
                 flat[s:e] = torch.randn((e - s,), generator=gd, device=dev, dtype=torch.float32).to(torch.bfloat16)
     return dict(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, cu_cache=cu.to(device),
                 positions=lens.to(device), sink=None, window=-1, rope_base=1e7, n_kv_heads=n_kv_heads)
+
+
+def make_cached(chunk_lengths, prefixes, n_q_heads, n_kv_heads, seed, with_sink, keep=None, device="cpu", g=None):
+    """A prefill chunk over cached prefixes: q, k, v of the new tokens (bf16), sink, cu_seqlens (new tokens),
+    k_cache, v_cache (bf16), cu_cache, positions (int32: the first new token's position = the prefix)."""
+    g = g if g is not None else _gen(seed)
+    d = make_layer(chunk_lengths, n_q_heads, n_kv_heads, None, with_sink, device, g=g)
+    rows = [int(p) if keep is None else min(int(p), keep) for p in prefixes]
+    cuc = cu_from_lengths(rows)
+    Tc = int(cuc[-1])
+    d["k_cache"] = _randn_bf16((Tc, n_kv_heads, DQK), g, device)
+    d["v_cache"] = _randn_bf16((Tc, n_kv_heads, DV), g, device)
+    d["cu_cache"] = cuc.to(device)
+    d["positions"] = torch.as_tensor([int(p) for p in prefixes], dtype=torch.int32).to(device)
+    d["cache_rows"] = rows
+    d["max_position"] = max([int(p) + int(n) for p, n in zip(prefixes, chunk_lengths)] + [1])
+    return d
+
+
+def chunked_16(device="cpu", seed=5):
+    """Both layers of a 16-sequence chunked prefill: dict(glb=..., swa=...)."""
+    g = _gen(seed)
+    prefixes = torch.randint(2048, 8193, (16,), generator=g).tolist()
+    chunks = torch.randint(1024, 2049, (16,), generator=g).tolist()
+    glb = make_cached(chunks, prefixes, HQ, 4, None, False, None, device, g=g)
+    glb.update(window=-1, rope_base=1e7)
+    swa = make_cached(chunks, prefixes, HQ, 8, None, True, 128, device, g=g)
+    swa.update(window=128, rope_base=1e4)
+    return dict(glb=glb, swa=swa)

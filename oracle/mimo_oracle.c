@@ -631,9 +631,10 @@ int oracle_decode_rows(const void *q, const void *k_new, const void *v_new, cons
 }
 
 /* ---------------------------------------------------------------------------------------------
- * Prefill of a chunk of new tokens over a cached prefix (the rollout engine prefills long prompts in
- * chunks against the KV cache: miles docs "MiMo-V2.6-Flash", section 3.2, chunked prefill size; the cache
- * holds rotated K and unscaled V as in decode).  Sequence b has n_b cache rows cu_cache[b] ..
+ * Prefill of a chunk of new tokens over a cached prefix (the serving engine prefills long prompts in
+ * chunks of up to 49152 tokens against its KV cache: SGLang cookbook page "MiMo-V2.6", section 2
+ * "Configuration tips", "Context length and memory"; the cache holds rotated K and unscaled V as in
+ * decode).  Sequence b has n_b cache rows cu_cache[b] ..
  * cu_cache[b+1]-1, the keys at positions positions[b]-n_b .. positions[b]-1 in that order, and new tokens
  * cu_q[b] .. cu_q[b+1]-1 at positions positions[b], positions[b]+1, ...  New token i attends the cache
  * rows and the new tokens 0..i, limited to key positions >= its own position - window when window >= 0,

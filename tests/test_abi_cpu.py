@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     for n in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_fwd_workspace_size",
               "mimo_attn_bwd_workspace_size", "mimo_attn_bwd_workspace_size_fast",
               "mimo_attn_decode_workspace_size", "mimo_attn_status_string", "mimo_attn_last_error",
-              "mimo_attn_release"):
+              "mimo_attn_release", "mimo_attn_prefill_cached", "mimo_attn_prefill_cached_workspace_size"):
         assert n in names
 
 
@@ -142,6 +142,31 @@ def test_decode_rejects_bad_arguments(L):
     assert dec(q=None) == 1
     assert dec(ws=None) == 4
     assert dec(batch=0) == 0
+
+
+def test_prefill_cached_rejects_bad_arguments(L):
+    def pc(**kw):
+        a = dict(batch=2, T=16, Tc=64, max_seqlen=16, max_position=200, window=128, hq=64, hkv=8, ws=FAKE,
+                 wsb=1 << 30, kc=FAKE, cuc=FAKE, pos=FAKE, out=FAKE)
+        a.update(kw)
+        return L.mimo_attn_prefill_cached(FAKE, FAKE, FAKE, a["kc"], FAKE, None, FAKE, a["cuc"], a["pos"], a["batch"],
+                                          a["T"], a["Tc"], a["max_seqlen"], a["max_position"], a["window"], 1e4,
+                                          a["hq"], a["hkv"], a["out"], None, a["ws"], a["wsb"], None)
+    assert pc(hkv=5) == 1
+    assert pc(window=-3) == 1
+    assert pc(Tc=-1) == 1
+    assert pc(cuc=None) == 1
+    assert pc(pos=None) == 1
+    assert pc(kc=None) == 1
+    assert pc(out=None) == 1
+    assert pc(max_position=8) == 1
+    assert pc(ws=None) == 4
+    assert pc(wsb=16) == 4
+    assert pc(T=0) == 0
+    assert pc(T=0, Tc=0, batch=0, max_seqlen=0) == 0
+    need = L.mimo_attn_prefill_cached_workspace_size(16, 64, 8)
+    assert need >= L.mimo_attn_fwd_workspace_size(80, 64, 8, 128)
+    assert L.mimo_attn_prefill_cached_workspace_size(-1, 0, 8) == 0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -69,3 +69,18 @@ def test_traffic_summary_rejects_misaligned_launches(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h")
     with pytest.raises(SystemExit):
         bench.traffic_summary(fetch, write)
+
+
+def test_cached_pairs_counts_visible_keys():
+    """Pairs of a chunked prefill: brute force over key positions (cache rows precede the chunk)."""
+    import bench
+
+    def brute(chunks, rows, window):
+        tot = 0
+        for L, n in zip(chunks, rows):
+            for i in range(L):
+                p = n + i                          # the query's position when the cache starts at 0
+                tot += sum(1 for j in range(n + i + 1) if window < 0 or j >= p - window)
+        return tot
+    for chunks, rows, window in [([3, 2, 0], [4, 0, 9], -1), ([5, 130], [200, 3], 128), ([7], [2], 0)]:
+        assert bench.cached_pairs(chunks, rows, window) == brute(chunks, rows, window)
