@@ -7,10 +7,11 @@ the timed region.  FLOPs are algorithmic: attended (query, key) pairs x 640 (for
 
 The decode step (batch 64, SWA ring of 128 + sink; global cache lengths in [8192, 131072]) is timed in the
 same run and reported as GB/s of cache traffic under "decode"; the prefill forward alone ("prefill") and a
-prefill of 16 chunks over cached prefixes ("prefill_cached") likewise.  None of them is part of the step's
-value.
+prefill of 16 chunks over cached prefixes ("prefill_cached"), the step at the per-GPU shapes of a 4-way head
+split ("tp4_shard_step") and a decode against one 1,048,576-row cache ("decode_1m") likewise.  None of them is
+part of the step's value.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--step-only]
 
 HBM traffic of the kernels (the roofline's "traffic") is taken with two rocprofv3 counter passes over
 `--traffic-probe` (one warm step plus a plain 1 GiB copy that calibrates the counters), then summarised:
@@ -384,6 +385,80 @@ def run_prefill_cached(ga, torch, mi, reps=10):
     return res
 
 
+def run_shards(ga, torch, thd, dout_cpu, steps=5):
+    """The training step at the per-GPU shapes of a 4-way head split of the same 32K THD batch: 16 query heads
+    with 2 KV heads (sliding-window layer) and 1 KV head (global layer), forward and backward of both."""
+    dev = torch.device("cuda", 0)
+    layers = {}
+    for name, hkv in (("swa", 2), ("glb", 1)):
+        d = thd[name]
+        g = {"q": d["q"][:, :16].contiguous().to(dev), "k": d["k"][:, :hkv].contiguous().to(dev),
+             "v": d["v"][:, :hkv].contiguous().to(dev), "cu_seqlens": d["cu_seqlens"].to(dev),
+             "sink": None if d["sink"] is None else d["sink"][:16].contiguous().to(dev),
+             "window": d["window"], "rope_base": d["rope_base"], "max_seqlen": max(d["lengths"])}
+        T = g["q"].shape[0]
+        g["out"] = torch.empty(T, 16, 128, dtype=torch.bfloat16, device=dev)
+        g["lse"] = torch.empty(16, T, dtype=torch.float32, device=dev)
+        g["q_rot"] = torch.empty(T, 16, 192, dtype=torch.bfloat16, device=dev)
+        g["grads"] = (torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"]),
+                      torch.empty(16, dtype=torch.float32, device=dev) if g["sink"] is not None else None)
+        g["ws"] = torch.empty(ga.bwd_workspace_size(T, 16, hkv, g["window"], len(d["lengths"]), g["max_seqlen"]),
+                              dtype=torch.uint8, device=dev)
+        g["pairs"] = pairs_per_head(d["lengths"], d["window"]) * 16
+        layers[name] = g
+    dout = dout_cpu[:, :16].contiguous().to(dev)
+
+    def step():
+        for g in layers.values():
+            ga.fwd(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], g["max_seqlen"], g["window"], g["rope_base"],
+                   out=g["out"], lse=g["lse"], q_rot=g["q_rot"])
+            ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], dout, g["cu_seqlens"], g["max_seqlen"],
+                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"], q_rot=g["q_rot"])
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flop = sum(g["pairs"] for g in layers.values()) * (FWD_FLOP_PER_PAIR + BWD_FLOP_PER_PAIR)
+    res = {"shapes": "16 q heads; 2 kv heads (SWA), 1 kv head (global)", "ms_per_step": round(ms, 3),
+           "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+           "frac_of_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del layers, dout
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode_1m(ga, torch, mi, reps=10):
+    """Decode of one sequence against 1,048,576 cached rows (global layer, 64 q / 4 kv heads)."""
+    n = 1 << 20
+    d = mi.decode_global(batch=1, len_lo=n, len_hi=n, device="cuda")
+    ws = torch.empty(ga.decode_workspace_size(1, n, 64, -1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, 64, 128, dtype=torch.bfloat16, device="cuda")
+    call = lambda: ga.decode(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["cu_cache"],  # noqa
+                             d["positions"], None, n, -1, 1e7, out, ws)
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        call()
+    times = []
+    for _ in range(reps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    byts = n * 4 * (192 + 128) * 2 + 64 * (192 + 128) * 2 + 4 * (192 + 128) * 2
+    del d, ws, out, flush
+    torch.cuda.empty_cache()
+    return {"cache_rows": n, "ms": round(ms, 4), "GB/s": round(byts / ms / 1e6, 1),
+            "hbm_frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -391,6 +466,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the training step (for profiles whose per-kernel averages are the step's)")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--traffic-probe", metavar="DIR", help="run the counter-pass workload (see the module doc)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -489,11 +566,14 @@ def main():
         "frac_of_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "layers": layer_tflops, "kernels": kernels, "roofline": roofline,
     }
-    line["prefill"] = run_prefill(ga, torch, layers)
-    line["prefill_cached"] = run_prefill_cached(ga, torch, mi)
-    if not args.no_decode:
+    if not args.step_only:
+        line["prefill"] = run_prefill(ga, torch, layers)
+        line["prefill_cached"] = run_prefill_cached(ga, torch, mi)
+        line["tp4_shard_step"] = run_shards(ga, torch, thd, dout_cpu)
+    if not args.no_decode and not args.step_only:
         line["decode"] = run_decode(ga, torch, mi)
-    if not args.no_cpu_baseline:
+        line["decode_1m"] = run_decode_1m(ga, torch, mi)
+    if not args.no_cpu_baseline and not args.step_only:
         line["cpu_baseline"] = cpu_baseline(thd, dout_cpu, args.cpu_threads)
     print(json.dumps(line), flush=True)
 

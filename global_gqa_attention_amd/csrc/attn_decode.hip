@@ -231,10 +231,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     }
 }
 
-// One wave per (sequence, query head): merge the splits, the new token and the sink.
-__global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs A)
+// One workgroup of four waves per (sequence, query head): merge the splits, the new token and the sink.
+// Wave w takes splits w, w + 4, ...; the four partial sums are added in wave order (deterministic).
+__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs A)
 {
-    const int lane = threadIdx.x;
+    __shared__ float red_m[4], red_l[4];
+    __shared__ float2 red_o[4][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x / A.hq, h = blockIdx.x % A.hq;
     const int G = A.hq / A.hkv, kvh = h / G;
     const double pos = (double)A.positions[b];
@@ -259,29 +262,48 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs A)
     for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
     const float s_new = dot * A.scale_log2;
 
+    // common reference: the largest of the new score, the sink and every split's max
     const float *ml = A.part_ml + ((size_t)b * A.hq + h) * A.splits * 2;
     const float *po = A.part_o + ((size_t)b * A.hq + h) * A.splits * DVV;
-    float M = s_new;
     const float sk = A.sink ? A.sink[h] * LOG2E : -INFINITY;
-    M = fmaxf(M, sk);
-    for (int s = 0; s < A.splits; ++s) M = fmaxf(M, ml[2 * s]);
-    const float w_new = fast_exp2(s_new - M);
-    float L = w_new + (sk > -INFINITY ? fast_exp2(sk - M) : 0.f);
-    const u16 *vp = A.v_new + ((size_t)b * A.hkv + kvh) * DVV;
-    float o0 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane]));
-    float o1 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane + 1]));
-    for (int s = 0; s < A.splits; ++s) {
+    float M = fmaxf(s_new, sk);
+    for (int s = tid; s < A.splits; s += 256) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    if (lane == 0) red_m[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
+    // this wave's splits: weighted sums of the partial numerators (dims 2 lane, 2 lane + 1) and denominators
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+    for (int s = wave; s < A.splits; s += 4) {
         const float m = ml[2 * s];
-        if (m == -INFINITY) continue;
-        const float wgt = fast_exp2(m - M);
+        const float wgt = m == -INFINITY ? 0.f : fast_exp2(m - M);
         L += wgt * ml[2 * s + 1];
-        o0 += wgt * po[(size_t)s * DVV + 2 * lane];
-        o1 += wgt * po[(size_t)s * DVV + 2 * lane + 1];
+        const float2 x = *(const float2 *)(po + (size_t)s * DVV + 2 * lane);
+        o0 += wgt * x.x;
+        o1 += wgt * x.y;
     }
-    const float inv = VSCALE / L;
+    red_o[wave][lane] = make_float2(o0, o1);
+    if (lane == 0) red_l[wave] = L;
+    __syncthreads();
+    if (wave != 0) return;
+    const float w_new = fast_exp2(s_new - M);
+    const u16 *vp = A.v_new + ((size_t)b * A.hkv + kvh) * DVV;
+    float t0 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane]));
+    float t1 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane + 1]));
+    float Lt = w_new + (sk > -INFINITY ? fast_exp2(sk - M) : 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        Lt += red_l[w];
+        t0 += red_o[w][lane].x;
+        t1 += red_o[w][lane].y;
+    }
+    const float inv = VSCALE / Lt;
     u16 *out = A.out + ((size_t)b * A.hq + h) * DVV + 2 * lane;
-    out[0] = __builtin_bit_cast(u16, f2bf(o0 * inv));
-    out[1] = __builtin_bit_cast(u16, f2bf(o1 * inv));
+    out[0] = __builtin_bit_cast(u16, f2bf(t0 * inv));
+    out[1] = __builtin_bit_cast(u16, f2bf(t1 * inv));
 }
 
 }  // namespace
@@ -290,13 +312,15 @@ bool decode_group_supported(int group) { return group >= 1; }
 
 void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window, int *splits, int *split_len)
 {
-    (void)batch;
     (void)hq;
     (void)hkv;
     int n = max_cache_len;
     if (window >= 0 && window < n) n = window;
-    // at most 32 splits, each a multiple of the chunk and at least 1024 rows
-    int len = (n + 31) / 32;
+    // up to 32 splits per sequence at a batch of 64 and proportionally more for smaller batches (a batch
+    // of one long cache still fills the chip: 1024 splits of 1024 rows at 1M rows), each a multiple of the
+    // chunk and at least 1024 rows
+    const int target = batch >= 64 ? 32 : min(1024, 32 * ((64 + max(batch, 1) - 1) / max(batch, 1)));
+    int len = (n + target - 1) / target;
     len = (len + CH - 1) / CH * CH;
     if (len < 1024) len = 1024;
     int s = (n + len - 1) / len;
@@ -325,7 +349,7 @@ hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     trace_begin("decode_combine", stream);
-    decode_combine_kernel<<<(unsigned)(A.batch * A.hq), 64, 0, stream>>>(A);
+    decode_combine_kernel<<<(unsigned)(A.batch * A.hq), 256, 0, stream>>>(A);
     trace_end(stream);
     return hipGetLastError();
 }
