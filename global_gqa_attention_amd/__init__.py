@@ -48,6 +48,10 @@ def lib():
         L.mimo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
         L.mimo_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mimo_attn_decode.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
+        L.mimo_attn_cache_append.argtypes = [P, P, P, P, i32, i32, i32, f64, P, P, P]
+        L.mimo_attn_decode_paged.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
+        L.mimo_attn_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32,
+                                              i32, P, P, P, sz, P]
         L.mimo_attn_prefill_cached_workspace_size.argtypes = [i32, i32, i32]
         L.mimo_attn_prefill_cached_workspace_size.restype = sz
         L.mimo_attn_prefill_cached.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32,
@@ -63,7 +67,8 @@ def lib():
         L.mimo_attn_trace_count.restype = i32
         L.mimo_attn_trace_read.restype = ctypes.c_int
         L.mimo_attn_trace_clear.restype = None
-        for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_prefill_cached"):
+        for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_prefill_cached",
+                  "mimo_attn_cache_append", "mimo_attn_decode_paged", "mimo_attn_prefill_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.mimo_attn_bwd_workspace_size.restype = sz
         L.mimo_attn_decode_workspace_size.restype = sz
@@ -250,6 +255,85 @@ def prefill_cached(q, k, v, k_cache, v_cache, sink, cu_seqlens, cu_cache, positi
                                         int(max_seqlen), int(max_position), int(window), float(rope_base), hq, hkv,
                                         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(rc, "mimo_attn_prefill_cached")
+    return out, lse
+
+
+def _pool_checks(k_pool, v_pool, hkv):
+    _need(k_pool, "k_pool", torch.bfloat16)
+    _need(v_pool, "v_pool", torch.bfloat16)
+    P = k_pool.shape[0]
+    _need(k_pool, "k_pool", torch.bfloat16, (P, hkv, DQK))
+    _need(v_pool, "v_pool", torch.bfloat16, (P, hkv, DV))
+    return P
+
+
+def cache_append(k, v, positions, slots, k_pool, v_pool, rope_base):
+    """Rotate k (bf16 [n, hkv, 192]) at positions (int32 [n]) and store it with v in pool rows slots (int32 [n])."""
+    _need(k, "k", torch.bfloat16)
+    n, hkv = k.shape[0], k.shape[1]
+    _need(k, "k", torch.bfloat16, (n, hkv, DQK))
+    _need(v, "v", torch.bfloat16, (n, hkv, DV))
+    _need(positions, "positions", torch.int32, (n,))
+    _need(slots, "slots", torch.int32, (n,))
+    P = _pool_checks(k_pool, v_pool, hkv)
+    rc = lib().mimo_attn_cache_append(_ptr(k), _ptr(v), _ptr(positions), _ptr(slots), n, hkv, P, float(rope_base),
+                                      _ptr(k_pool), _ptr(v_pool), _stream(k.device))
+    _check(rc, "mimo_attn_cache_append")
+
+
+def decode_paged(q, k_new, v_new, k_pool, v_pool, page_table, cu_pages, positions, sink, max_cache_len, window,
+                 rope_base, out=None, workspace=None):
+    """Decode over a paged cache (cache row r of sequence b = pool row page_table[cu_pages[b] + r])."""
+    _need(q, "q", torch.bfloat16)
+    B, hq = q.shape[0], q.shape[1]
+    hkv = k_new.shape[1]
+    _need(q, "q", torch.bfloat16, (B, hq, DQK))
+    _need(k_new, "k_new", torch.bfloat16, (B, hkv, DQK))
+    _need(v_new, "v_new", torch.bfloat16, (B, hkv, DV))
+    _pool_checks(k_pool, v_pool, hkv)
+    _need(page_table, "page_table", torch.int32)
+    _need(cu_pages, "cu_pages", torch.int32, (B + 1,))
+    _need(positions, "positions", torch.int32, (B,))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (hq,))
+    if out is None:
+        out = torch.empty((B, hq, DV), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, hq, DV))
+    if workspace is None:
+        workspace = torch.empty((max(decode_workspace_size(B, max_cache_len, hq, window), 1),), dtype=torch.uint8,
+                                device=q.device)
+    rc = lib().mimo_attn_decode_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                      _ptr(cu_pages), _ptr(positions), _ptr(sink), B, int(max_cache_len), int(window),
+                                      float(rope_base), hq, hkv, _ptr(out), _ptr(workspace), workspace.numel(),
+                                      _stream(q.device))
+    _check(rc, "mimo_attn_decode_paged")
+    return out
+
+
+def prefill_paged(q, k, v, k_pool, v_pool, page_table, sink, cu_seqlens, cu_pages, positions, max_seqlen, max_position,
+                  window, rope_base, out=None, lse=None, return_lse=True, workspace=None):
+    """prefill_cached over a paged cache (the multi-token verify step with short chunks)."""
+    T, hq, hkv, batch = _layer_checks(q, k, v, sink, cu_seqlens)
+    _pool_checks(k_pool, v_pool, hkv)
+    _need(page_table, "page_table", torch.int32)
+    _need(cu_pages, "cu_pages", torch.int32, (batch + 1,))
+    _need(positions, "positions", torch.int32, (batch,))
+    npg = page_table.numel()
+    if workspace is None:
+        workspace = torch.empty((max(prefill_cached_workspace_size(T, npg, hkv), 1),), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((T, hq, DV), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (T, hq, DV))
+    if return_lse and lse is None:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (hq, T))
+    rc = lib().mimo_attn_prefill_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                       _ptr(sink), _ptr(cu_seqlens), _ptr(cu_pages), _ptr(positions), batch, T, npg,
+                                       int(max_seqlen), int(max_position), int(window), float(rope_base), hq, hkv,
+                                       _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(rc, "mimo_attn_prefill_paged")
     return out, lse
 
 

@@ -269,13 +269,15 @@ size_t mimo_attn_prefill_cached_workspace_size(int32_t total_tokens, int32_t tot
     return mimo::prep_bytes(total_tokens + total_cache, n_kv_heads);
 }
 
-mimo_status_t mimo_attn_prefill_cached(const void *q, const void *k, const void *v, const void *k_cache,
-                                       const void *v_cache, const float *sink, const int32_t *cu_seqlens,
-                                       const int32_t *cu_cache, const int32_t *positions, int32_t batch,
-                                       int32_t total_tokens, int32_t total_cache, int32_t max_seqlen,
-                                       int32_t max_position, int32_t window, double rope_base,
-                                       int32_t n_q_heads, int32_t n_kv_heads, void *out, float *lse,
-                                       void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+mimo_status_t prefill_over_cache(const void *q, const void *k, const void *v, const void *k_cache, const void *v_cache,
+                                 const int32_t *page_table, const float *sink, const int32_t *cu_seqlens,
+                                 const int32_t *cu_cache, const int32_t *positions, int32_t batch,
+                                 int32_t total_tokens, int32_t total_cache, int32_t max_seqlen, int32_t max_position,
+                                 int32_t window, double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
+                                 float *lse, void *workspace, size_t workspace_bytes, void *stream)
 {
     mimo_status_t s = check_layer(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base,
                                   n_q_heads, n_kv_heads);
@@ -315,12 +317,63 @@ mimo_status_t mimo_attn_prefill_cached(const void *q, const void *k, const void 
     a.C.k_cache = (const uint16_t *)k_cache;
     a.C.v_cache = (const uint16_t *)v_cache;
     a.C.cu_cache = cu_cache;
+    a.C.page_table = page_table;
     a.C.positions = positions;
     a.C.Tc = total_cache;
     a.out = (uint16_t *)out;
     a.lse = lse;
     hipError_t e = mimo::launch_fwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "cached prefill launch");
+    return ok();
+}
+}  // namespace
+
+extern "C" {
+
+mimo_status_t mimo_attn_prefill_cached(const void *q, const void *k, const void *v, const void *k_cache,
+                                       const void *v_cache, const float *sink, const int32_t *cu_seqlens,
+                                       const int32_t *cu_cache, const int32_t *positions, int32_t batch,
+                                       int32_t total_tokens, int32_t total_cache, int32_t max_seqlen,
+                                       int32_t max_position, int32_t window, double rope_base,
+                                       int32_t n_q_heads, int32_t n_kv_heads, void *out, float *lse,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    return prefill_over_cache(q, k, v, k_cache, v_cache, nullptr, sink, cu_seqlens, cu_cache, positions, batch,
+                              total_tokens, total_cache, max_seqlen, max_position, window, rope_base, n_q_heads,
+                              n_kv_heads, out, lse, workspace, workspace_bytes, stream);
+}
+
+mimo_status_t mimo_attn_prefill_paged(const void *q, const void *k, const void *v, const void *k_pool,
+                                      const void *v_pool, const int32_t *page_table, const float *sink,
+                                      const int32_t *cu_seqlens, const int32_t *cu_pages, const int32_t *positions,
+                                      int32_t batch, int32_t total_tokens, int32_t total_pages, int32_t max_seqlen,
+                                      int32_t max_position, int32_t window, double rope_base, int32_t n_q_heads,
+                                      int32_t n_kv_heads, void *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream)
+{
+    if (total_pages > 0 && !page_table) return fail(MIMO_ERR_INVALID_ARG, "page_table is null");
+    return prefill_over_cache(q, k, v, k_pool, v_pool, total_pages > 0 ? page_table : nullptr, sink, cu_seqlens,
+                              cu_pages, positions, batch, total_tokens, total_pages, max_seqlen, max_position, window,
+                              rope_base, n_q_heads, n_kv_heads, out, lse, workspace, workspace_bytes, stream);
+}
+
+mimo_status_t mimo_attn_cache_append(const void *k, const void *v, const int32_t *positions, const int32_t *slots,
+                                     int32_t n_tokens, int32_t n_kv_heads, int32_t pool_rows, double rope_base,
+                                     void *k_pool, void *v_pool, void *stream)
+{
+    if (n_tokens < 0) return fail(MIMO_ERR_INVALID_ARG, "n_tokens must be >= 0 (got %d)", n_tokens);
+    if (n_kv_heads <= 0) return fail(MIMO_ERR_INVALID_ARG, "n_kv_heads must be positive");
+    if (pool_rows < 0) return fail(MIMO_ERR_INVALID_ARG, "pool_rows must be >= 0");
+    if (!(rope_base > 1.0) || !isfinite(rope_base))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_base must be finite and > 1 (got %g)", rope_base);
+    if (n_tokens == 0) return ok();
+    if (!k || !v || !positions || !slots || !k_pool || !v_pool)
+        return fail(MIMO_ERR_INVALID_ARG, "null pointer among k/v/positions/slots/k_pool/v_pool");
+    if (n_kv_heads > 65535) return fail(MIMO_ERR_UNSUPPORTED, "too many KV heads");
+    hipError_t e = mimo::launch_cache_append((const uint16_t *)k, (const uint16_t *)v, positions, slots, n_tokens,
+                                             n_kv_heads, pool_rows, rope_base, (uint16_t *)k_pool,
+                                             (uint16_t *)v_pool, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "cache append launch");
     return ok();
 }
 
@@ -410,11 +463,14 @@ size_t mimo_attn_decode_workspace_size(int32_t batch, int32_t max_cache_len, int
     return mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, window);
 }
 
-mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_new, const void *k_cache,
-                               const void *v_cache, const int32_t *cu_cache, const int32_t *positions,
-                               const float *sink, int32_t batch, int32_t max_cache_len, int32_t window,
-                               double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
-                               void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+mimo_status_t decode_over_cache(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                                const void *v_cache, const int32_t *page_table, const int32_t *cu_cache,
+                                const int32_t *positions, const float *sink, int32_t batch, int32_t max_cache_len,
+                                int32_t window, double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
+                                void *workspace, size_t workspace_bytes, void *stream)
 {
     if (batch < 0) return fail(MIMO_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
     if (max_cache_len < 0) return fail(MIMO_ERR_INVALID_ARG, "max_cache_len must be >= 0");
@@ -439,6 +495,7 @@ mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_n
     a.k_cache = (const uint16_t *)k_cache;
     a.v_cache = (const uint16_t *)v_cache;
     a.cu_cache = cu_cache;
+    a.page_table = page_table;
     a.positions = positions;
     a.sink = sink;
     a.out = (uint16_t *)out;
@@ -456,6 +513,33 @@ mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_n
     hipError_t e = mimo::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
+}
+}  // namespace
+
+extern "C" {
+
+mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                               const void *v_cache, const int32_t *cu_cache, const int32_t *positions,
+                               const float *sink, int32_t batch, int32_t max_cache_len, int32_t window,
+                               double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_over_cache(q, k_new, v_new, k_cache, v_cache, nullptr, cu_cache, positions, sink, batch,
+                             max_cache_len, window, rope_base, n_q_heads, n_kv_heads, out, workspace,
+                             workspace_bytes, stream);
+}
+
+mimo_status_t mimo_attn_decode_paged(const void *q, const void *k_new, const void *v_new, const void *k_pool,
+                                     const void *v_pool, const int32_t *page_table, const int32_t *cu_pages,
+                                     const int32_t *positions, const float *sink, int32_t batch,
+                                     int32_t max_cache_len, int32_t window, double rope_base, int32_t n_q_heads,
+                                     int32_t n_kv_heads, void *out, void *workspace, size_t workspace_bytes,
+                                     void *stream)
+{
+    if (batch > 0 && max_cache_len > 0 && !page_table) return fail(MIMO_ERR_INVALID_ARG, "page_table is null");
+    return decode_over_cache(q, k_new, v_new, k_pool, v_pool, max_cache_len > 0 ? page_table : nullptr, cu_pages,
+                             positions, sink, batch, max_cache_len, window, rope_base, n_q_heads, n_kv_heads, out,
+                             workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -46,6 +46,7 @@ __device__ __forceinline__ const u16 *wave_uniform(const u16 *p)
     return (const u16 *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
 {
     __shared__ __attribute__((aligned(256))) DecTile ring[2];
@@ -100,9 +101,30 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
         voff[j] = (uint32_t)((r * vrow + 8 * swz256t(r, q)) * 2);
     }
     const int klast = ks + (ke - ks - 1) / CH * CH;   // first row of the split's last chunk
+    // paged cache: pool rows of the chunk's cache rows, lane r (mod 32) holding row k + r (clamped to the
+    // split's end); read one chunk ahead of its copy
+    auto table_rows = [&](int k) __attribute__((always_inline)) {
+        k = min(k, klast);
+        return A.page_table[c0 + min(k + c, ke - 1)];
+    };
+    int tv = PAGED ? table_rows(ks) : 0;
     auto issue = [&](int k, DecTile &T) __attribute__((always_inline)) {
         k = __builtin_amdgcn_readfirstlane(min(k, klast));   // past the end: the last chunk again (uniform waits)
-        if (k + CH <= ke) {
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int j = 0; j < CH * DKC / 64; ++j) {
+                const int slot = 64 * j + lane, r = slot / DKC, q = slot % DKC;
+                const int row = __shfl(tv, r, 64);
+                lds_dma16(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
+            }
+#pragma unroll
+            for (int j = 0; j < CH * DVC / 64; ++j) {
+                const int slot = 64 * j + lane, r = slot / DVC, q = slot % DVC;
+                const int row = __shfl(tv, r, 64);
+                lds_dma16(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
+            }
+            tv = table_rows(k + CH);
+        } else if (k + CH <= ke) {
             const u16 *kb = wave_uniform(A.k_cache + ((size_t)(c0 + k) * A.hkv + kvh) * DQK);
             const u16 *vb = wave_uniform(A.v_cache + ((size_t)(c0 + k) * A.hkv + kvh) * DVV);
 #pragma unroll
@@ -344,7 +366,8 @@ hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)
     const long waves = (long)A.batch * A.hkv * ((G + 31) / 32) * A.splits;
     if (waves > 0x7fffffffL || (long)A.batch * A.hq > 0x7fffffffL) return hipErrorInvalidConfiguration;
     trace_begin(A.window >= 0 ? "decode_split_swa" : "decode_split_global", stream);
-    decode_split_kernel<<<(unsigned)waves, 64, 0, stream>>>(A);
+    if (A.page_table) decode_split_kernel<true><<<(unsigned)waves, 64, 0, stream>>>(A);
+    else decode_split_kernel<false><<<(unsigned)waves, 64, 0, stream>>>(A);
     trace_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -124,7 +124,8 @@ __global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, 
         const int j = u - (C.cu_cache[b] + a.cu[b]);
         const int n = C.cu_cache[b + 1] - C.cu_cache[b];
         if (j < n) {
-            const size_t row = (size_t)(C.cu_cache[b] + j) * a.hkv + kvh;
+            const int cr = C.cu_cache[b] + j;
+            const size_t row = (size_t)(C.page_table ? C.page_table[cr] : cr) * a.hkv + kvh;
             ks = C.k_cache + row * DQK;
             vs = C.v_cache + row * DVV;
             pos = -1;

@@ -31,8 +31,9 @@ void prep_carve(void *ws, int T, int hkv, KVPrep *p);
 // lays the cache rows and the new tokens' keys out as one key stream per sequence (sequence b's keys start
 // at cu_cache[b] + cu[b]), so the key index of new token t is t + cu_cache[b+1].
 struct CacheArgs {
-    const uint16_t *k_cache, *v_cache;   // bf16 [Tc,hkv,192] (rotated), [Tc,hkv,128]
+    const uint16_t *k_cache, *v_cache;   // bf16 [Tc,hkv,192] (rotated), [Tc,hkv,128]; paged: the pools
     const int32_t *cu_cache;             // [batch+1], or nullptr: no cache (plain prefill)
+    const int32_t *page_table;           // paged cache: pool row of cache row i is page_table[i], or nullptr
     const int32_t *positions;            // [batch]
     int Tc;                              // cache rows in all
 };
@@ -77,8 +78,9 @@ struct BwdArgs {
 void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A, bool stored_ds, int batch, int max_seqlen);
 
 struct DecodeArgs {
-    const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
+    const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;   // paged: k_cache / v_cache are the pools
     const int32_t *cu_cache, *positions;
+    const int32_t *page_table;     // paged cache: pool row of each cache row (cu_cache indexes it), or nullptr
     const float *sink;
     uint16_t *out;
     float *part_o;                 // workspace [batch, hq, splits, 128]
@@ -98,6 +100,9 @@ hipError_t launch_kv_prep_cached(const LayerArgs &a, const KVPrep &p, const Cach
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_cache_append(const uint16_t *k, const uint16_t *v, const int32_t *positions, const int32_t *slots,
+                               int n, int hkv, int pool_rows, double rope_base, uint16_t *k_pool, uint16_t *v_pool,
+                               hipStream_t stream);
 hipError_t launch_rope_table(float2 *table, int npos, double base, hipStream_t stream);
 hipError_t launch_zero_f32(float *p, int n, hipStream_t stream);   // a fill kernel (no memset nodes)
 

@@ -169,8 +169,9 @@ size_t mimo_attn_prefill_cached_workspace_size(int32_t total_tokens, int32_t tot
  *   out       bf16 [total_tokens, n_q_heads, 128];  lse fp32 [n_q_heads, total_tokens] or NULL
  *   workspace at least mimo_attn_prefill_cached_workspace_size() bytes of device memory (the prepared key
  *             stream: cache rows and the chunk's rotated keys per sequence)
- * New token i of sequence b gets exactly the row that mimo_attn_fwd gives token n_b + i of the whole
- * sequence whose first n_b tokens are the cache; with no cache rows and positions 0 this is mimo_attn_fwd.
+ * With positions[b] = n_b, new token i of sequence b gets the row that mimo_attn_fwd gives token n_b + i of
+ * the whole sequence whose first n_b tokens are the cache; with no cache rows and positions 0 this is
+ * mimo_attn_fwd.
  * The cache is read, never written. */
 mimo_status_t mimo_attn_prefill_cached(const void *q, const void *k, const void *v, const void *k_cache,
                                        const void *v_cache, const float *sink, const int32_t *cu_seqlens,
@@ -179,6 +180,45 @@ mimo_status_t mimo_attn_prefill_cached(const void *q, const void *k, const void 
                                        int32_t max_position, int32_t window, double rope_base,
                                        int32_t n_q_heads, int32_t n_kv_heads, void *out, float *lse,
                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Paged KV cache (page size 1: one token per pool row).  Source: SGLang cookbook page "MiMo-V2.6", section 2
+ * "Configuration tips", "Context length and memory" (page size 1; decode batches up to 64); miles docs
+ * "MiMo-V2.6-Flash" section 3.2 (sliding-window layers keep their own KV pools).
+ *
+ * A pool is k_pool bf16 [pool_rows, n_kv_heads, 192] (keys ALREADY rotated at their own positions) and
+ * v_pool bf16 [pool_rows, n_kv_heads, 128] (unscaled).  A sequence's cache is a list of pool rows: entries
+ * page_table[cu_pages[b]] .. page_table[cu_pages[b+1]-1] (int32, device), in position order.  Every pool row
+ * a table names must lie in [0, pool_rows); nothing on the device checks it. */
+
+/* Write n_tokens new tokens into a pool: token i's key (bf16 [n_tokens, n_kv_heads, 192], un-rotated) is
+ * rotated at positions[i] and stored, with its value (bf16 [n_tokens, n_kv_heads, 128], unscaled), in pool
+ * row slots[i] (int32 device arrays).  The rotated key is bit-identical to the one the forward computes for
+ * the same token and position.  Slots outside [0, pool_rows) are skipped; duplicate slots race. */
+mimo_status_t mimo_attn_cache_append(const void *k, const void *v, const int32_t *positions, const int32_t *slots,
+                                     int32_t n_tokens, int32_t n_kv_heads, int32_t pool_rows, double rope_base,
+                                     void *k_pool, void *v_pool, void *stream);
+
+/* mimo_attn_decode over a paged cache: cache row r of sequence b is pool row page_table[cu_pages[b] + r];
+ * max_cache_len >= every cu_pages[b+1] - cu_pages[b].  Everything else (q, k_new, v_new, positions, sink,
+ * window, out, workspace of mimo_attn_decode_workspace_size()) as mimo_attn_decode. */
+mimo_status_t mimo_attn_decode_paged(const void *q, const void *k_new, const void *v_new, const void *k_pool,
+                                     const void *v_pool, const int32_t *page_table, const int32_t *cu_pages,
+                                     const int32_t *positions, const float *sink, int32_t batch,
+                                     int32_t max_cache_len, int32_t window, double rope_base, int32_t n_q_heads,
+                                     int32_t n_kv_heads, void *out, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* mimo_attn_prefill_cached over a paged cache (total_pages table entries; workspace of
+ * mimo_attn_prefill_cached_workspace_size(total_tokens, total_pages, n_kv_heads)).  With a chunk of a few
+ * tokens per sequence this is the multi-token verify step of speculative decoding: the draft tokens attend
+ * the cache and each other causally. */
+mimo_status_t mimo_attn_prefill_paged(const void *q, const void *k, const void *v, const void *k_pool,
+                                      const void *v_pool, const int32_t *page_table, const float *sink,
+                                      const int32_t *cu_seqlens, const int32_t *cu_pages, const int32_t *positions,
+                                      int32_t batch, int32_t total_tokens, int32_t total_pages, int32_t max_seqlen,
+                                      int32_t max_position, int32_t window, double rope_base, int32_t n_q_heads,
+                                      int32_t n_kv_heads, void *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 /* Per-kernel tracing.  While enabled, every entry point records a HIP event on the caller's stream before
  * and after each kernel it launches (the events only mark the stream; nothing is synchronised).  The

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     for n in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_fwd_workspace_size",
               "mimo_attn_bwd_workspace_size", "mimo_attn_bwd_workspace_size_fast",
               "mimo_attn_decode_workspace_size", "mimo_attn_status_string", "mimo_attn_last_error",
-              "mimo_attn_release", "mimo_attn_prefill_cached", "mimo_attn_prefill_cached_workspace_size"):
+              "mimo_attn_release", "mimo_attn_prefill_cached", "mimo_attn_prefill_cached_workspace_size",
+              "mimo_attn_cache_append", "mimo_attn_decode_paged", "mimo_attn_prefill_paged"):
         assert n in names
 
 
@@ -167,6 +168,40 @@ def test_prefill_cached_rejects_bad_arguments(L):
     need = L.mimo_attn_prefill_cached_workspace_size(16, 64, 8)
     assert need >= L.mimo_attn_fwd_workspace_size(80, 64, 8, 128)
     assert L.mimo_attn_prefill_cached_workspace_size(-1, 0, 8) == 0
+
+
+def test_paged_entry_points_reject_bad_arguments(L):
+    def app(**kw):
+        a = dict(k=FAKE, n=4, hkv=8, pool=100, base=1e4, kp=FAKE)
+        a.update(kw)
+        return L.mimo_attn_cache_append(a["k"], FAKE, FAKE, FAKE, a["n"], a["hkv"], a["pool"], a["base"], a["kp"], FAKE,
+                                        None)
+    assert app(n=-1) == 1
+    assert app(hkv=0) == 1
+    assert app(pool=-1) == 1
+    assert app(base=1.0) == 1
+    assert app(k=None) == 1
+    assert app(kp=None) == 1
+    assert app(n=0) == 0
+
+    def dec(**kw):
+        a = dict(batch=4, hkv=8, table=FAKE, maxlen=128, ws=FAKE)
+        a.update(kw)
+        return L.mimo_attn_decode_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], FAKE, FAKE, None, a["batch"],
+                                        a["maxlen"], 128, 1e4, 64, a["hkv"], FAKE, a["ws"], 1 << 30, None)
+    assert dec(table=None) == 1
+    assert dec(hkv=5) == 1
+    assert dec(ws=None) == 4
+    assert dec(batch=0) == 0
+
+    def pre(**kw):
+        a = dict(table=FAKE, npg=64, T=16, ws=FAKE)
+        a.update(kw)
+        return L.mimo_attn_prefill_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], None, FAKE, FAKE, FAKE, 2, a["T"],
+                                         a["npg"], 16, 200, 128, 1e4, 64, 8, FAKE, None, a["ws"], 1 << 30, None)
+    assert pre(table=None) == 1
+    assert pre(ws=None) == 4
+    assert pre(T=0) == 0
 
 
 def test_binding_refuses_cpu_tensors():
