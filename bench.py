@@ -8,7 +8,8 @@ the timed region.  FLOPs are algorithmic: attended (query, key) pairs x 640 (for
 The decode step (batch 64, SWA ring of 128 + sink; global cache lengths in [8192, 131072]) is timed in the
 same run and reported as GB/s of cache traffic under "decode"; the prefill forward alone ("prefill") and a
 prefill of 16 chunks over cached prefixes ("prefill_cached"), the step at the per-GPU shapes of a 4-way head
-split ("tp4_shard_step") and a decode against one 1,048,576-row cache ("decode_1m") likewise.  None of them is
+split ("tp4_shard_step"), a decode against one 1,048,576-row cache ("decode_1m") and decode plus 8-token verify
+over a paged cache ("paged") likewise.  None of them is
 part of the step's value.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--step-only]
@@ -459,6 +460,58 @@ def run_decode_1m(ga, torch, mi, reps=10):
             "hbm_frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def run_paged(ga, torch, mi, reps=10):
+    """Batch-64 decode and an 8-token verify per sequence over the global-layer decode caches held in a paged
+    pool whose table is a random permutation of the pool rows (every cache row in its own place)."""
+    d = mi.decode_global(device="cuda")
+    cu = d["cu_cache"]
+    lens = (cu[1:] - cu[:-1]).tolist()
+    N = int(d["k_cache"].shape[0])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    table = torch.randperm(N, generator=g, device="cuda").to(torch.int32)
+    ws = torch.empty(ga.decode_workspace_size(64, max(lens), 64, -1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(64, 64, 128, dtype=torch.bfloat16, device="cuda")
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        times = []
+        for _ in range(reps):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]
+
+    ms = timed(lambda: ga.decode_paged(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], table, cu,
+                                       d["positions"], None, max(lens), -1, 1e7, out, ws))
+    byts = N * 4 * 640 + 64 * (64 + 4) * 640
+    res = {"decode_ms": round(ms, 4), "decode_GB/s": round(byts / ms / 1e6, 1),
+           "decode_hbm_frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    # verify: 8 draft tokens per sequence at positions len_b .. len_b + 7 over the same paged caches
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(8)
+    q = torch.randn(64 * 8, 64, 192, generator=gq, device="cuda").to(torch.bfloat16)
+    k = torch.randn(64 * 8, 4, 192, generator=gq, device="cuda").to(torch.bfloat16)
+    v = torch.randn(64 * 8, 4, 128, generator=gq, device="cuda").to(torch.bfloat16)
+    cuq = torch.arange(0, 64 * 8 + 1, 8, dtype=torch.int32, device="cuda")
+    wsv = torch.empty(ga.prefill_cached_workspace_size(64 * 8, N, 4), dtype=torch.uint8, device="cuda")
+    outv = torch.empty(64 * 8, 64, 128, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(64, 64 * 8, dtype=torch.float32, device="cuda")
+    msv = timed(lambda: ga.prefill_paged(q, k, v, d["k_cache"], d["v_cache"], table, None, cuq, cu, d["positions"],
+                                         8, max(lens) + 8, -1, 1e7, out=outv, lse=lse, workspace=wsv))
+    res.update({"verify_tokens_per_sequence": 8, "verify_ms": round(msv, 4),
+                "verify_ms_per_token": round(msv / 8, 4)})
+    del d, table, ws, out, flush, q, k, v, wsv, outv, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -573,6 +626,7 @@ def main():
     if not args.no_decode and not args.step_only:
         line["decode"] = run_decode(ga, torch, mi)
         line["decode_1m"] = run_decode_1m(ga, torch, mi)
+        line["paged"] = run_paged(ga, torch, mi)
     if not args.no_cpu_baseline and not args.step_only:
         line["cpu_baseline"] = cpu_baseline(thd, dout_cpu, args.cpu_threads)
     print(json.dumps(line), flush=True)

@@ -253,12 +253,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     }
 }
 
-// One workgroup of four waves per (sequence, query head): merge the splits, the new token and the sink.
-// Wave w takes splits w, w + 4, ...; the four partial sums are added in wave order (deterministic).
-__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs A)
+// One workgroup of NWV waves per (sequence, query head): merge the splits, the new token and the sink.
+// Wave w takes splits w, w + NWV, ...; the partial sums are added in wave order (deterministic).  Four
+// waves when there are many splits (a small batch over long caches), one otherwise.
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) void decode_combine_kernel(const DecodeArgs A)
 {
-    __shared__ float red_m[4], red_l[4];
-    __shared__ float2 red_o[4][64];
+    __shared__ float red_m[NWV], red_l[NWV];
+    __shared__ float2 red_o[NWV][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x / A.hq, h = blockIdx.x % A.hq;
     const int G = A.hq / A.hkv, kvh = h / G;
@@ -289,17 +291,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs A)
     const float *po = A.part_o + ((size_t)b * A.hq + h) * A.splits * DVV;
     const float sk = A.sink ? A.sink[h] * LOG2E : -INFINITY;
     float M = fmaxf(s_new, sk);
-    for (int s = tid; s < A.splits; s += 256) M = fmaxf(M, ml[2 * s]);
+    for (int s = tid; s < A.splits; s += 64 * NWV) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    if (lane == 0) red_m[wave] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    if (NWV > 1) {
+        if (lane == 0) red_m[wave] = M;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) M = fmaxf(M, red_m[w]);
+    }
 
     // this wave's splits: weighted sums of the partial numerators (dims 2 lane, 2 lane + 1) and denominators
     float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll 4
-    for (int s = wave; s < A.splits; s += 4) {
+    for (int s = wave; s < A.splits; s += NWV) {
         const float m = ml[2 * s];
         const float wgt = m == -INFINITY ? 0.f : fast_exp2(m - M);
         L += wgt * ml[2 * s + 1];
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs A)
     float t1 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane + 1]));
     float Lt = w_new + (sk > -INFINITY ? fast_exp2(sk - M) : 0.f);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWV; ++w) {
         Lt += red_l[w];
         t0 += red_o[w][lane].x;
         t1 += red_o[w][lane].y;
@@ -372,7 +377,8 @@ hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     trace_begin("decode_combine", stream);
-    decode_combine_kernel<<<(unsigned)(A.batch * A.hq), 256, 0, stream>>>(A);
+    if (A.splits > 16) decode_combine_kernel<4><<<(unsigned)(A.batch * A.hq), 256, 0, stream>>>(A);
+    else decode_combine_kernel<1><<<(unsigned)(A.batch * A.hq), 64, 0, stream>>>(A);
     trace_end(stream);
     return hipGetLastError();
 }
