@@ -493,7 +493,8 @@ def run_paged(ga, torch, mi, reps=10):
     byts = N * 4 * 640 + 64 * (64 + 4) * 640
     res = {"decode_ms": round(ms, 4), "decode_GB/s": round(byts / ms / 1e6, 1),
            "decode_hbm_frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    # verify: 8 draft tokens per sequence at positions len_b .. len_b + 7 over the same paged caches
+    # verify: 8 draft tokens per sequence; the last 8 rows of each cache list play the drafts (already
+    # appended), at positions len_b - 8 .. len_b - 1
     gq = torch.Generator(device="cuda")
     gq.manual_seed(8)
     q = torch.randn(64 * 8, 64, 192, generator=gq, device="cuda").to(torch.bfloat16)
@@ -503,11 +504,25 @@ def run_paged(ga, torch, mi, reps=10):
     wsv = torch.empty(ga.prefill_cached_workspace_size(64 * 8, N, 4), dtype=torch.uint8, device="cuda")
     outv = torch.empty(64 * 8, 64, 128, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(64, 64 * 8, dtype=torch.float32, device="cuda")
-    msv = timed(lambda: ga.prefill_paged(q, k, v, d["k_cache"], d["v_cache"], table, None, cuq, cu, d["positions"],
-                                         8, max(lens) + 8, -1, 1e7, out=outv, lse=lse, workspace=wsv))
+    posv = (d["positions"] - 8).contiguous()
+    wsq = torch.empty(ga.verify_workspace_size(64, 8, max(lens), 64, -1), dtype=torch.uint8, device="cuda")
+    msv = timed(lambda: ga.verify_paged(q, d["k_cache"], d["v_cache"], table, cu, posv, None, 8, max(lens), -1, 1e7,
+                                        out=outv, workspace=wsq))
+    byv = N * 4 * 640 + 64 * 8 * 64 * 640
+    # the same verify through the cached-prefill path: the drafts as a chunk over each list without its last
+    # 8 entries (a table of exactly those entries, so cu_before[-1] equals its length)
+    idx = torch.arange(N, device="cuda")
+    seq = torch.bucketize(idx, cu[1:].long(), right=True)
+    keep = idx < (cu[1:].long()[seq] - 8)
+    table_before = table[keep].contiguous()
+    cu_before = (cu - torch.arange(0, 65 * 8, 8, dtype=torch.int32, device="cuda")).contiguous()
+    assert table_before.numel() == int(cu_before[-1])
+    msp = timed(lambda: ga.prefill_paged(q, k, v, d["k_cache"], d["v_cache"], table_before, None, cuq, cu_before,
+                                         posv, 8, max(lens) + 8, -1, 1e7, out=outv, lse=lse, workspace=wsv))
     res.update({"verify_tokens_per_sequence": 8, "verify_ms": round(msv, 4),
-                "verify_ms_per_token": round(msv / 8, 4)})
-    del d, table, ws, out, flush, q, k, v, wsv, outv, lse
+                "verify_ms_per_token": round(msv / 8, 4), "verify_GB/s": round(byv / msv / 1e6, 1),
+                "verify_via_cached_prefill_ms": round(msp, 4)})
+    del d, table, ws, out, flush, q, k, v, wsv, wsq, outv, lse
     torch.cuda.empty_cache()
     return res
 

@@ -52,6 +52,9 @@ def lib():
         L.mimo_attn_decode_paged.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
         L.mimo_attn_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32,
                                               i32, P, P, P, sz, P]
+        L.mimo_attn_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.mimo_attn_verify_workspace_size.restype = sz
+        L.mimo_attn_verify_paged.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, sz, P]
         L.mimo_attn_prefill_cached_workspace_size.argtypes = [i32, i32, i32]
         L.mimo_attn_prefill_cached_workspace_size.restype = sz
         L.mimo_attn_prefill_cached.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32,
@@ -68,7 +71,8 @@ def lib():
         L.mimo_attn_trace_read.restype = ctypes.c_int
         L.mimo_attn_trace_clear.restype = None
         for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_prefill_cached",
-                  "mimo_attn_cache_append", "mimo_attn_decode_paged", "mimo_attn_prefill_paged"):
+                  "mimo_attn_cache_append", "mimo_attn_decode_paged", "mimo_attn_prefill_paged",
+                  "mimo_attn_verify_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.mimo_attn_bwd_workspace_size.restype = sz
         L.mimo_attn_decode_workspace_size.restype = sz
@@ -335,6 +339,42 @@ def prefill_paged(q, k, v, k_pool, v_pool, page_table, sink, cu_seqlens, cu_page
                                        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(rc, "mimo_attn_prefill_paged")
     return out, lse
+
+
+def verify_workspace_size(batch, n_query, max_cache_len, n_q_heads, window) -> int:
+    return int(lib().mimo_attn_verify_workspace_size(int(batch), int(n_query), int(max_cache_len), int(n_q_heads),
+                                                     int(window)))
+
+
+def verify_paged(q, k_pool, v_pool, page_table, cu_pages, positions, sink, n_query, max_cache_len, window, rope_base,
+                 out=None, workspace=None):
+    """Verify n_query draft tokens per sequence (their keys already appended as the last n_query entries of
+    each page-table list).  q: bf16 [batch * n_query, hq, 192].  Returns out bf16 [batch * n_query, hq, 128]."""
+    _need(q, "q", torch.bfloat16)
+    R, hq = q.shape[0], q.shape[1]
+    if n_query < 1 or R % n_query:
+        raise ValueError("q must hold n_query rows per sequence")
+    B = R // n_query
+    hkv = k_pool.shape[1] if k_pool.dim() == 3 else 0
+    _need(q, "q", torch.bfloat16, (R, hq, DQK))
+    _pool_checks(k_pool, v_pool, hkv)
+    _need(page_table, "page_table", torch.int32)
+    _need(cu_pages, "cu_pages", torch.int32, (B + 1,))
+    _need(positions, "positions", torch.int32, (B,))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (hq,))
+    if out is None:
+        out = torch.empty((R, hq, DV), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (R, hq, DV))
+    if workspace is None:
+        workspace = torch.empty((max(verify_workspace_size(B, n_query, max_cache_len, hq, window), 1),),
+                                dtype=torch.uint8, device=q.device)
+    rc = lib().mimo_attn_verify_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(cu_pages),
+                                      _ptr(positions), _ptr(sink), B, int(n_query), int(max_cache_len), int(window),
+                                      float(rope_base), hq, hkv, _ptr(out), _ptr(workspace), workspace.numel(),
+                                      _stream(q.device))
+    _check(rc, "mimo_attn_verify_paged")
+    return out
 
 
 def release():

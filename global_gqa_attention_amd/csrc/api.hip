@@ -466,12 +466,18 @@ size_t mimo_attn_decode_workspace_size(int32_t batch, int32_t max_cache_len, int
 }  // extern "C"
 
 namespace {
+// Decode (nq = 1, k_new/v_new given) or verify (nq draft tokens whose keys are the last nq cache rows,
+// k_new == v_new == nullptr) over a contiguous or paged cache.
 mimo_status_t decode_over_cache(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                                 const void *v_cache, const int32_t *page_table, const int32_t *cu_cache,
-                                const int32_t *positions, const float *sink, int32_t batch, int32_t max_cache_len,
-                                int32_t window, double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
-                                void *workspace, size_t workspace_bytes, void *stream)
+                                const int32_t *positions, const float *sink, int32_t batch, int32_t nq,
+                                int32_t max_cache_len, int32_t window, double rope_base, int32_t n_q_heads,
+                                int32_t n_kv_heads, void *out, void *workspace, size_t workspace_bytes, void *stream)
 {
+    const bool verify = k_new == nullptr;
+    if (nq < 1 || (!verify && nq != 1)) return fail(MIMO_ERR_INVALID_ARG, "query tokens per sequence must be >= 1");
+    if (verify && batch > 0 && max_cache_len < nq)
+        return fail(MIMO_ERR_INVALID_ARG, "max_cache_len (%d) must cover the %d draft rows", max_cache_len, nq);
     if (batch < 0) return fail(MIMO_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
     if (max_cache_len < 0) return fail(MIMO_ERR_INVALID_ARG, "max_cache_len must be >= 0");
     if (window < -1) return fail(MIMO_ERR_INVALID_ARG, "window must be -1 or >= 0 (got %d)", window);
@@ -480,12 +486,14 @@ mimo_status_t decode_over_cache(const void *q, const void *k_new, const void *v_
     if (!(rope_base > 1.0) || !isfinite(rope_base))
         return fail(MIMO_ERR_INVALID_ARG, "rope_base must be finite and > 1 (got %g)", rope_base);
     if (batch == 0) return ok();
-    if (!q || !k_new || !v_new || !cu_cache || !positions || !out)
+    if (!q || (!verify && !v_new) || !cu_cache || !positions || !out)
         return fail(MIMO_ERR_INVALID_ARG, "null pointer among q/k_new/v_new/cu_cache/positions/out");
+    if ((long long)batch * nq * n_q_heads > 0x7fffffffLL) return fail(MIMO_ERR_UNSUPPORTED, "too many query rows");
     if (max_cache_len > 0 && (!k_cache || !v_cache)) return fail(MIMO_ERR_INVALID_ARG, "null cache pointer");
     if (!mimo::decode_group_supported(n_q_heads / n_kv_heads))
         return fail(MIMO_ERR_UNSUPPORTED, "no decode kernel for group size %d", n_q_heads / n_kv_heads);
-    const size_t need = mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, window);
+    const int wplan = verify && window >= 0 ? window + nq : window;   // rows a query can see
+    const size_t need = mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, wplan, nq);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     mimo::DecodeArgs a{};
@@ -500,15 +508,16 @@ mimo_status_t decode_over_cache(const void *q, const void *k_new, const void *v_
     a.sink = sink;
     a.out = (uint16_t *)out;
     a.batch = batch;
+    a.nq = nq;
     a.window = window;
     a.hq = n_q_heads;
     a.hkv = n_kv_heads;
     a.rope_base = rope_base;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kDQK));
-    mimo::decode_split_plan(batch, max_cache_len, n_q_heads, n_kv_heads, window, &a.splits, &a.split_len);
+    mimo::decode_split_plan(batch, max_cache_len, n_q_heads, n_kv_heads, wplan, &a.splits, &a.split_len);
     char *ws = (char *)workspace;
     a.part_o = (float *)ws;
-    size_t off = ((size_t)batch * n_q_heads * a.splits * kDV * sizeof(float) + 255) & ~(size_t)255;
+    size_t off = ((size_t)batch * nq * n_q_heads * a.splits * kDV * sizeof(float) + 255) & ~(size_t)255;
     a.part_ml = (float *)(ws + off);
     hipError_t e = mimo::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -524,7 +533,8 @@ mimo_status_t mimo_attn_decode(const void *q, const void *k_new, const void *v_n
                                double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
                                void *workspace, size_t workspace_bytes, void *stream)
 {
-    return decode_over_cache(q, k_new, v_new, k_cache, v_cache, nullptr, cu_cache, positions, sink, batch,
+    if (batch > 0 && !k_new) return fail(MIMO_ERR_INVALID_ARG, "k_new is null");
+    return decode_over_cache(q, k_new, v_new, k_cache, v_cache, nullptr, cu_cache, positions, sink, batch, 1,
                              max_cache_len, window, rope_base, n_q_heads, n_kv_heads, out, workspace,
                              workspace_bytes, stream);
 }
@@ -537,9 +547,31 @@ mimo_status_t mimo_attn_decode_paged(const void *q, const void *k_new, const voi
                                      void *stream)
 {
     if (batch > 0 && max_cache_len > 0 && !page_table) return fail(MIMO_ERR_INVALID_ARG, "page_table is null");
+    if (batch > 0 && !k_new) return fail(MIMO_ERR_INVALID_ARG, "k_new is null");
     return decode_over_cache(q, k_new, v_new, k_pool, v_pool, max_cache_len > 0 ? page_table : nullptr, cu_pages,
-                             positions, sink, batch, max_cache_len, window, rope_base, n_q_heads, n_kv_heads, out,
+                             positions, sink, batch, 1, max_cache_len, window, rope_base, n_q_heads, n_kv_heads, out,
                              workspace, workspace_bytes, stream);
+}
+
+size_t mimo_attn_verify_workspace_size(int32_t batch, int32_t n_query, int32_t max_cache_len, int32_t n_q_heads,
+                                       int32_t window)
+{
+    if (batch < 0 || n_query < 1 || max_cache_len < 0 || n_q_heads <= 0 || window < -1) return 0;
+    return mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, window >= 0 ? window + n_query : window,
+                                        n_query);
+}
+
+mimo_status_t mimo_attn_verify_paged(const void *q, const void *k_pool, const void *v_pool, const int32_t *page_table,
+                                     const int32_t *cu_pages, const int32_t *positions, const float *sink,
+                                     int32_t batch, int32_t n_query, int32_t max_cache_len, int32_t window,
+                                     double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
+                                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (batch > 0 && !page_table) return fail(MIMO_ERR_INVALID_ARG, "page_table is null");
+    if (batch > 0 && (!k_pool || !v_pool)) return fail(MIMO_ERR_INVALID_ARG, "null pool pointer");
+    return decode_over_cache(q, nullptr, nullptr, k_pool, v_pool, page_table, cu_pages, positions, sink, batch,
+                             n_query, max_cache_len, window, rope_base, n_q_heads, n_kv_heads, out, workspace,
+                             workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -53,7 +53,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     const int lane = threadIdx.x, hh = lane >> 5, c = lane & 31;
     const int grp = lane >> 4, t4 = (lane & 15) >> 2, m4 = lane & 3;
     const int G = A.hq / A.hkv;
-    const int ngrp = (G + 31) / 32;          // the group's query heads in blocks of 32 MFMA columns
+    // query columns of a KV head: (query token, head) pairs, token-major; decode has one query token per
+    // sequence, verify A.nq draft tokens whose keys are already the last A.nq cache rows (no k_new)
+    const bool verify = A.k_new == nullptr;
+    const int NC = G * A.nq;
+    const int ngrp = (NC + 31) / 32;         // the columns in blocks of 32 MFMA columns
     int w = blockIdx.x;
     const int split = w % A.splits;
     w /= A.splits;
@@ -65,14 +69,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
 
     int c0 = __builtin_amdgcn_readfirstlane(A.cu_cache[b]);
     const int c1 = __builtin_amdgcn_readfirstlane(A.cu_cache[b + 1]);
-    if (A.window >= 0 && c1 - c0 > A.window) c0 = c1 - A.window;
+    // rows that some query of the sequence can see: decode the last `window` (the new token comes on top),
+    // verify the last window + nq (the first draft token's window reaches window rows below it)
+    const int keep = verify ? A.window + A.nq : A.window;
+    if (A.window >= 0 && c1 - c0 > keep) c0 = c1 - keep;
     const int n = c1 - c0;
     const int ks = split * A.split_len;
     const int ke = min(n, ks + A.split_len);
-    const int gi = hgrp * 32 + c;            // this lane's head inside the group
-    const bool hvalid = gi < G;
-    const int h = kvh * G + (hvalid ? gi : G - 1);   // spare MFMA columns repeat the group's last head
-    const size_t part = ((size_t)b * A.hq + h) * A.splits + split;
+    const int gi = hgrp * 32 + c;            // this lane's column
+    const bool hvalid = gi < NC;
+    const int gcol = hvalid ? gi : NC - 1;   // spare MFMA columns repeat the last column
+    const int ti = gcol / G;                 // query token of the column
+    const int h = kvh * G + gcol % G;
+    const size_t part = (((size_t)b * A.nq + ti) * A.hq + h) * A.splits + split;
+    // rows this column may see (indices from c0): decode all; verify those up to its own token (row
+    // n - nq + ti) and at most `window` below it
+    int lim = n - 1, lo = 0;
+    if (verify) {
+        lim = n - A.nq + ti;
+        lo = A.window >= 0 ? lim - A.window : min(lim, 0);
+    }
 
     if (ks >= ke) {                          // nothing cached in this split: an empty partial
         if (hvalid) {
@@ -151,10 +167,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
     // rotated query (bf16) as the B operand: column = head, dims 16s + 8hh + t
     bf16x8 qf[12];
     {
-        const u16 *qp = A.q + ((size_t)b * A.hq + h) * DQK + 8 * hh;
+        const u16 *qp = A.q + (((size_t)b * A.nq + ti) * A.hq + h) * DQK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
-        const double pos = (double)A.positions[b];
+        const double pos = (double)A.positions[b] + (double)ti;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float2 cs[8];
@@ -198,18 +214,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int key = k + 8 * (j >> 2) + 4 * hh + (j & 3);
-            const float sv = key < ke ? sacc[j] * A.scale_log2 : -INFINITY;
+            const bool ok = key < ke && (uint32_t)(key - lo) <= (uint32_t)(lim - lo);
+            const float sv = ok ? sacc[j] * A.scale_log2 : -INFINITY;
             sacc[j] = sv;
             mx = fmaxf(mx, sv);
         }
         mx = pair_max(mx);
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        // a verify column may see none of a chunk's keys: keep it at (max -inf, sum 0) without NaNs
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_ref);
         float psum = 0.f;
         bf16x8 pf[2];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float pj = fast_exp2(sacc[j] - m_new);
+            const float pj = fast_exp2(sacc[j] - m_ref);
             psum += pj;
             pf[j >> 3][j & 7] = f2bf(pj);
         }
@@ -262,15 +281,17 @@ __global__ __launch_bounds__(64 * NWV) void decode_combine_kernel(const DecodeAr
     __shared__ float red_m[NWV], red_l[NWV];
     __shared__ float2 red_o[NWV][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x / A.hq, h = blockIdx.x % A.hq;
+    const int row = blockIdx.x / A.hq, h = blockIdx.x % A.hq;   // row = b * nq + query token
+    const int b = row / A.nq;
     const int G = A.hq / A.hkv, kvh = h / G;
     const double pos = (double)A.positions[b];
+    const bool verify = A.k_new == nullptr;   // verify: the queries' own keys are cache rows already
 
-    // score of the new token: rotate q and k_new (dims 3*lane .. 3*lane+2 of 192) in fp32 from fp64 angles
-    const u16 *qp = A.q + ((size_t)b * A.hq + h) * DQK;
-    const u16 *kp = A.k_new + ((size_t)b * A.hkv + kvh) * DQK;
+    // score of the new token (decode): rotate q and k_new in fp32 from fp64 angles
+    const u16 *qp = A.q + ((size_t)row * A.hq + h) * DQK;
+    const u16 *kp = verify ? nullptr : A.k_new + ((size_t)b * A.hkv + kvh) * DQK;
     float dot = 0.f;
-    if (lane < NHALF) {
+    if (!verify && lane < NHALF) {
         double sn, cn;
         sincos(pos * inv_freq(A.rope_base, lane), &sn, &cn);
         const float cf = (float)cn, sf = (float)sn;
@@ -280,15 +301,16 @@ __global__ __launch_bounds__(64 * NWV) void decode_combine_kernel(const DecodeAr
         const float ka = k0 * cf - k1 * sf, kb = k1 * cf + k0 * sf;
         dot = qa * ka + qb * kb;
     }
-    for (int d = 64 + lane; d < DQK; d += 64)
-        dot += bf2f(__builtin_bit_cast(__bf16, qp[d])) * bf2f(__builtin_bit_cast(__bf16, kp[d]));
+    if (!verify)
+        for (int d = 64 + lane; d < DQK; d += 64)
+            dot += bf2f(__builtin_bit_cast(__bf16, qp[d])) * bf2f(__builtin_bit_cast(__bf16, kp[d]));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    const float s_new = dot * A.scale_log2;
+    const float s_new = verify ? -INFINITY : dot * A.scale_log2;
 
     // common reference: the largest of the new score, the sink and every split's max
-    const float *ml = A.part_ml + ((size_t)b * A.hq + h) * A.splits * 2;
-    const float *po = A.part_o + ((size_t)b * A.hq + h) * A.splits * DVV;
+    const float *ml = A.part_ml + ((size_t)row * A.hq + h) * A.splits * 2;
+    const float *po = A.part_o + ((size_t)row * A.hq + h) * A.splits * DVV;
     const float sk = A.sink ? A.sink[h] * LOG2E : -INFINITY;
     float M = fmaxf(s_new, sk);
     for (int s = tid; s < A.splits; s += 64 * NWV) M = fmaxf(M, ml[2 * s]);
@@ -316,10 +338,13 @@ __global__ __launch_bounds__(64 * NWV) void decode_combine_kernel(const DecodeAr
     if (lane == 0) red_l[wave] = L;
     __syncthreads();
     if (wave != 0) return;
-    const float w_new = fast_exp2(s_new - M);
-    const u16 *vp = A.v_new + ((size_t)b * A.hkv + kvh) * DVV;
-    float t0 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane]));
-    float t1 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane + 1]));
+    float t0 = 0.f, t1 = 0.f, w_new = 0.f;
+    if (!verify) {
+        w_new = fast_exp2(s_new - M);
+        const u16 *vp = A.v_new + ((size_t)b * A.hkv + kvh) * DVV;
+        t0 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane]));
+        t1 = w_new * bf2f(__builtin_bit_cast(__bf16, vp[2 * lane + 1]));
+    }
     float Lt = w_new + (sk > -INFINITY ? fast_exp2(sk - M) : 0.f);
 #pragma unroll
     for (int w = 0; w < NWV; ++w) {
@@ -328,7 +353,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_combine_kernel(const DecodeAr
         t1 += red_o[w][lane].y;
     }
     const float inv = VSCALE / Lt;
-    u16 *out = A.out + ((size_t)b * A.hq + h) * DVV + 2 * lane;
+    u16 *out = A.out + ((size_t)row * A.hq + h) * DVV + 2 * lane;
     out[0] = __builtin_bit_cast(u16, f2bf(t0 * inv));
     out[1] = __builtin_bit_cast(u16, f2bf(t1 * inv));
 }
@@ -356,20 +381,20 @@ void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window
     *split_len = len;
 }
 
-size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window)
+size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window, int nq)
 {
     int splits, len;
     decode_split_plan(batch, max_cache_len, hq, 1, window, &splits, &len);
-    const size_t po = ((size_t)batch * hq * splits * DVV * sizeof(float) + 255) & ~(size_t)255;
-    const size_t ml = (size_t)batch * hq * splits * 2 * sizeof(float);
+    const size_t po = ((size_t)batch * nq * hq * splits * DVV * sizeof(float) + 255) & ~(size_t)255;
+    const size_t ml = (size_t)batch * nq * hq * splits * 2 * sizeof(float);
     return po + ml;
 }
 
 hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)
 {
     const int G = A.hq / A.hkv;
-    const long waves = (long)A.batch * A.hkv * ((G + 31) / 32) * A.splits;
-    if (waves > 0x7fffffffL || (long)A.batch * A.hq > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    const long waves = (long)A.batch * A.hkv * ((G * A.nq + 31) / 32) * A.splits;
+    if (waves > 0x7fffffffL || (long)A.batch * A.nq * A.hq > 0x7fffffffL) return hipErrorInvalidConfiguration;
     trace_begin(A.window >= 0 ? "decode_split_swa" : "decode_split_global", stream);
     if (A.page_table) decode_split_kernel<true><<<(unsigned)waves, 64, 0, stream>>>(A);
     else decode_split_kernel<false><<<(unsigned)waves, 64, 0, stream>>>(A);
@@ -377,8 +402,9 @@ hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     trace_begin("decode_combine", stream);
-    if (A.splits > 16) decode_combine_kernel<4><<<(unsigned)(A.batch * A.hq), 256, 0, stream>>>(A);
-    else decode_combine_kernel<1><<<(unsigned)(A.batch * A.hq), 64, 0, stream>>>(A);
+    const unsigned rows = (unsigned)((long)A.batch * A.nq * A.hq);
+    if (A.splits > 16) decode_combine_kernel<4><<<rows, 256, 0, stream>>>(A);
+    else decode_combine_kernel<1><<<rows, 64, 0, stream>>>(A);
     trace_end(stream);
     return hipGetLastError();
 }

@@ -106,8 +106,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     // ---- key range: tiles start on a 16-key boundary (the V^T chunk order is per 16 keys); keys of a
     // previous sequence that this brings in are masked
     const int klo = WIN ? max(kseq, t0 + kofs - a.window) : kseq;
-    const int kstart = klo & ~15;
-    const int khi = t_last + kofs;
+    const int kstart = max(klo, 0) & ~15;
+    // the prepared key stream has T_pad rows and every tile read must stay inside it (binds only when the
+    // index arrays disagree with the sizes given)
+    const int khi = min(t_last + kofs, A.P.T_pad - BN - 1);
     const int nkt = (khi - kstart + BN) / BN;
 
     // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = NT j + tid of each array): the

@@ -118,36 +118,41 @@ __global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, 
     const int kvh = blockIdx.y;
     const int t0 = blockIdx.x * PT;
     const int Tk = a.T + C.Tc;
-    // source rows of key u: (K row, V row, rotation position or -1 for a cache row)
+    // source rows of key u: (K row, V row, rotation position or -1 for a cache row).  Returns false when the
+    // index arrays do not account for key u (their totals disagree with T and Tc): the key is then zero-filled
+    // instead of read from outside the tensors.
     auto source = [&](int u, const u16 *&ks, const u16 *&vs, int &pos) {
         const int b = seq_of_keys(a.cu, C.cu_cache, a.batch, u);
         const int j = u - (C.cu_cache[b] + a.cu[b]);
         const int n = C.cu_cache[b + 1] - C.cu_cache[b];
         if (j < n) {
             const int cr = C.cu_cache[b] + j;
+            if (cr < 0 || cr >= C.Tc) return false;
             const size_t row = (size_t)(C.page_table ? C.page_table[cr] : cr) * a.hkv + kvh;
             ks = C.k_cache + row * DQK;
             vs = C.v_cache + row * DVV;
             pos = -1;
         } else {
-            const size_t row = (size_t)(a.cu[b] + j - n) * a.hkv + kvh;
+            const int t = a.cu[b] + j - n;
+            if (t < 0 || t >= a.T) return false;
+            const size_t row = (size_t)t * a.hkv + kvh;
             ks = a.k + row * DQK;
             vs = a.v + row * DVV;
-            pos = C.positions[b] + j - n;
+            pos = max(C.positions[b] + j - n, 0);
         }
+        return true;
     };
 
     // ---- K: key t0 + tid/4, chunk group tid%4 (chunks cg, cg+4 rotated for new tokens; 8+cg+4i copied)
     {
         const int u = t0 + (tid >> 2), cg = tid & 3;
         u16 *dst = p.kr + ((size_t)u * a.hkv + kvh) * DQK;
-        if (u < Tk) {
-            const u16 *src, *vs;
-            int pos;
-            source(u, src, vs, pos);
+        const u16 *src = nullptr, *vs = nullptr;
+        int pos = 0;
+        if (u < Tk && source(u, src, vs, pos)) {
             bf16x8 x0 = ld16(src + 8 * cg), x1 = ld16(src + 8 * (cg + 4));
             if (pos >= 0) {
-                const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;
+                const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;   // pos >= 0 here
                 float2 c8[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) c8[i] = cs[i];
@@ -171,12 +176,12 @@ __global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, 
         const int u = t0 + r;
         const u16 *ks = nullptr, *vs = nullptr;
         int pos = 0;
-        if (u < Tk) source(u, ks, vs, pos);
+        const bool have = u < Tk && source(u, ks, vs, pos);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ch = cg + 4 * i;
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (u < Tk) x = ldu4(vs + 8 * ch);
+            if (have) x = ldu4(vs + 8 * ch);
             *(uint4 *)(sV + r * (DVV + 8) + 8 * ch) = x;
         }
     }

@@ -86,6 +86,8 @@ struct DecodeArgs {
     float *part_o;                 // workspace [batch, hq, splits, 128]
     float *part_ml;                // workspace [batch, hq, splits, 2] (max in log2 units, sum)
     int batch, window, hq, hkv, splits, split_len;
+    int nq;                        // query tokens per sequence: 1 (decode, k_new given) or the draft count
+                                   // (verify, k_new == nullptr: the drafts' keys are the last nq cache rows)
     double rope_base;
     float scale_log2;
 };
@@ -114,7 +116,7 @@ bool decode_group_supported(int group);
 size_t fwd_workspace_bytes(int T, int hq, int hkv, int window);
 size_t bwd_workspace_bytes(int T, int hq, int hkv, int window);
 size_t bwd_workspace_bytes_ds(int T, int hq, int hkv, int window, int batch, int max_seqlen);   // 0: not available
-size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window);
+size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window, int nq = 1);
 void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window, int *splits, int *split_len);
 
 }  // namespace mimo

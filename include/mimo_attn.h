@@ -208,10 +208,31 @@ mimo_status_t mimo_attn_decode_paged(const void *q, const void *k_new, const voi
                                      int32_t n_kv_heads, void *out, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/* Bytes of device workspace mimo_attn_verify_paged needs (0 for invalid sizes). */
+size_t mimo_attn_verify_workspace_size(int32_t batch, int32_t n_query, int32_t max_cache_len, int32_t n_q_heads,
+                                       int32_t window);
+
+/* The verify step of speculative decoding over a paged cache: each sequence has n_query draft tokens at
+ * positions positions[b] .. positions[b] + n_query - 1 whose keys and values were already appended
+ * (mimo_attn_cache_append) as the LAST n_query entries of its page-table list.  Draft token i sees the
+ * table entries up to its own (entry n_b - n_query + i) and, when window >= 0, at most `window` entries
+ * below it; the sink is in the denominator.  Source: SGLang cookbook page "MiMo-V2.6", section 2
+ * "Configuration tips" (speculative decoding with DFlash, decode batches up to 64).
+ *   q     bf16 [batch * n_query, n_q_heads, 192] un-rotated, sequence-major (row b * n_query + i)
+ *   out   bf16 [batch * n_query, n_q_heads, 128]
+ *   max_cache_len >= every list length (drafts included); workspace of mimo_attn_verify_workspace_size().
+ * The cache is read once per KV head and split, as in decode.  n_query = 1 gives the decode of a token
+ * whose key is already in the cache. */
+mimo_status_t mimo_attn_verify_paged(const void *q, const void *k_pool, const void *v_pool, const int32_t *page_table,
+                                     const int32_t *cu_pages, const int32_t *positions, const float *sink,
+                                     int32_t batch, int32_t n_query, int32_t max_cache_len, int32_t window,
+                                     double rope_base, int32_t n_q_heads, int32_t n_kv_heads, void *out,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* mimo_attn_prefill_cached over a paged cache (total_pages table entries; workspace of
- * mimo_attn_prefill_cached_workspace_size(total_tokens, total_pages, n_kv_heads)).  With a chunk of a few
- * tokens per sequence this is the multi-token verify step of speculative decoding: the draft tokens attend
- * the cache and each other causally. */
+ * mimo_attn_prefill_cached_workspace_size(total_tokens, total_pages, n_kv_heads)).  It copies the cache
+ * rows into the workspace first: for a few tokens per sequence mimo_attn_verify_paged reads the cache
+ * once instead. */
 mimo_status_t mimo_attn_prefill_paged(const void *q, const void *k, const void *v, const void *k_pool,
                                       const void *v_pool, const int32_t *page_table, const float *sink,
                                       const int32_t *cu_seqlens, const int32_t *cu_pages, const int32_t *positions,

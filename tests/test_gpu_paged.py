@@ -184,3 +184,69 @@ def test_serving_loop_matches_whole_prefill(hkv, window, sink, base):
         compare(f"decode step {s}", out.cpu(), ro[rows])
         for b in range(2):
             append(b, [p[b]])
+
+
+@pytest.mark.parametrize("prior,hkv,window,sink,base,nq", [
+    ([5000, 0, 300, 128, 1020, 2047], 4, -1, False, 1e7, 8),
+    ([5000, 0, 300, 128, 1020, 2047], 8, 128, True, 1e4, 8),
+    ([40, 3, 1020], 2, 5, True, 1e4, 8),
+    ([700, 1, 0], 4, -1, True, 1e7, 3),
+])
+def test_verify_paged(prior, hkv, window, sink, base, nq):
+    """nq draft tokens per sequence appended to a paged cache, then verified: against the oracle's prefill of
+    the drafts over the prior rows (including a split that some drafts cannot see at all)."""
+    ga = _gpu()
+    hq = 64
+    d = mi.make_cached([nq] * len(prior), prior, hq, hkv, 47, sink)
+    print(f"case verify prior={prior} hkv={hkv} window={window} nq={nq}", flush=True)
+    dev = "cuda"
+    B = len(prior)
+    Tc = d["k_cache"].shape[0]
+    P = Tc + B * nq + 100
+    g = torch.Generator().manual_seed(48)
+    kp = torch.randn(P, hkv, 192, generator=g).to(torch.bfloat16).to(dev)
+    vp = torch.randn(P, hkv, 128, generator=g).to(torch.bfloat16).to(dev)
+    perm = torch.randperm(P, generator=g).to(torch.int32)
+    cache_slots, draft_slots = perm[:Tc], perm[Tc:Tc + B * nq]
+    kp[cache_slots.long()] = d["k_cache"].to(dev)
+    vp[cache_slots.long()] = d["v_cache"].to(dev)
+    pos = d["positions"]
+    draft_pos = torch.cat([pos[b] + torch.arange(nq, dtype=torch.int32) for b in range(B)])
+    ga.cache_append(d["k"].to(dev), d["v"].to(dev), draft_pos.to(dev), draft_slots.to(dev), kp, vp, base)
+    cc = d["cu_cache"].tolist()
+    table = torch.cat([torch.cat([cache_slots[cc[b]:cc[b + 1]], draft_slots[b * nq:(b + 1) * nq]]) for b in range(B)])
+    cup = mi.cu_from_lengths([cc[b + 1] - cc[b] + nq for b in range(B)])
+    maxlen = max(int(cup[b + 1] - cup[b]) for b in range(B))
+    s = None if d["sink"] is None else d["sink"].to(dev)
+    out = ga.verify_paged(d["q"].to(dev), kp, vp, table.to(dev), cup.to(dev), pos.to(dev), s, nq, maxlen, window, base)
+    torch.cuda.synchronize()
+    ro, _ = oracle.prefill_cached_rows(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["cu_seqlens"],
+                                       d["cu_cache"], d["positions"], d["sink"], window, base)
+    compare("out", out.cpu(), ro.reshape(B * nq, hq, -1))
+
+
+def test_verify_one_token_is_decode():
+    """A one-token verify (the token's key appended first) gives decode's result within the tolerance."""
+    ga = _gpu()
+    g = torch.Generator().manual_seed(49)
+    lens, hq, hkv = [300, 1, 2000], 64, 4
+    B = len(lens)
+    r = lambda *sh: torch.randn(*sh, generator=g).to(torch.bfloat16)  # noqa: E731
+    cu = mi.cu_from_lengths(lens)
+    q, kn, vn = r(B, hq, 192), r(B, hkv, 192), r(B, hkv, 128)
+    kc, vc = r(int(cu[-1]), hkv, 192), r(int(cu[-1]), hkv, 128)
+    pos = torch.tensor(lens, dtype=torch.int32)
+    dev = "cuda"
+    o_dec = ga.decode(q.to(dev), kn.to(dev), vn.to(dev), kc.to(dev), vc.to(dev), cu.to(dev), pos.to(dev), None,
+                      max(lens), -1, 1e7)
+    Tc = int(cu[-1])
+    kp = torch.cat([kc, torch.zeros(B, hkv, 192, dtype=torch.bfloat16)]).to(dev)
+    vp = torch.cat([vc, torch.zeros(B, hkv, 128, dtype=torch.bfloat16)]).to(dev)
+    slots = torch.arange(Tc, Tc + B, dtype=torch.int32)
+    ga.cache_append(kn.to(dev), vn.to(dev), pos.to(dev), slots.to(dev), kp, vp, 1e7)
+    cl = cu.tolist()
+    table = torch.cat([torch.cat([torch.arange(cl[b], cl[b + 1], dtype=torch.int32), slots[b:b + 1]]) for b in range(B)])
+    cup = mi.cu_from_lengths([n + 1 for n in lens])
+    o_ver = ga.verify_paged(q.to(dev), kp, vp, table.to(dev), cup.to(dev), pos.to(dev), None, 1, max(lens) + 1, -1, 1e7)
+    torch.cuda.synchronize()
+    compare("verify vs decode", o_ver.cpu(), o_dec.cpu().double(), max_abs=1e-2, mean_abs=1e-3)
