@@ -17,6 +17,13 @@
 // keeps more bytes in flight than deeper rings with fewer workgroups.  Each split writes an unnormalised
 // partial (o, running max, running sum); the combine kernel merges the splits with the sink and the new
 // token (whose rotation is computed there in double precision).
+//
+// The same kernels serve two more forms.  Paged cache (page size 1: SGLang cookbook page "MiMo-V2.6",
+// section 2): cache row r of sequence b is pool row page_table[cu_cache[b] + r]; each lane of the first 32
+// holds the pool row of one row of the next chunk, read one chunk ahead, and the copies take per-lane
+// addresses.  Verify (speculative decoding's draft tokens, same page): nq query tokens per sequence whose
+// keys are already the last nq cache rows (no k_new); the MFMA columns are (token, head) pairs, and each
+// column sees the rows up to its own token and at most `window` below it.
 #include "device_common.hpp"
 #include "internal.hpp"
 
