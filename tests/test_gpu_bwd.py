@@ -142,6 +142,58 @@ def test_bwd_thd_32k_swa_sampled():
 
 
 @pytest.mark.parametrize("path", ["fast", "least"])
+def test_bwd_thd_32k_global_sampled(path):
+    """Global layer of the 32768-token THD batch, the launch the benchmark times, checked on sampled rows.
+
+    The oracle's forward over all 2.1 M (token, head) rows is too slow for a test, and none is needed: dq of
+    row i depends on the forward outputs of row i only (through D_i and LSE_i), and dk/dv of key j on those
+    of the queries that see j, which under causal attention are the tokens from j to the end of its
+    sequence.  The oracle computes O and LSE exactly on every row the sampled gradients depend on; every
+    other row gets O = 0 and LSE = 1e4, which make its probabilities and D exactly zero, so it adds nothing
+    to any gradient (and no inf or NaN) whatever its true value."""
+    ga = _gpu()
+    d = mi.thd_32k()["glb"]
+    dO = mi.dout_like(32768, 4)
+    T, hq, hkv = d["q"].shape[0], d["q"].shape[1], d["k"].shape[1]
+    G = hq // hkv
+    starts = np.concatenate([[0], np.cumsum(d["lengths"])])
+    rng = np.random.default_rng(7)
+    # sampled dq rows: first and last token of every sequence, and random rows
+    qtok = [int(starts[b]) for b in range(len(d["lengths"]))] + [int(starts[b + 1]) - 1 for b in range(len(d["lengths"]))]
+    qrows = np.array(sorted(set(t * hq + int(rng.integers(0, hq)) for t in qtok)
+                            | set(rng.integers(0, T * hq, 160).tolist())), dtype=np.int64)
+    # sampled key rows: 1, 2, 33 and 100 tokens before the end of every sequence (ragged against the tiles)
+    ktok = sorted(set(int(starts[b + 1]) - m for b in range(len(d["lengths"])) for m in (1, 2, 33, 100)
+                      if int(starts[b + 1]) - m >= int(starts[b])))
+    krows = np.array([t * hkv + int(rng.integers(0, hkv)) for t in ktok], dtype=np.int64)
+    need = set(qrows.tolist())
+    seq_of = np.searchsorted(starts, np.arange(T), side="right") - 1
+    for kr in krows.tolist():
+        t, g = kr // hkv, kr % hkv
+        e = int(starts[seq_of[t] + 1])
+        need.update(i * hq + g * G + h for i in range(t, e) for h in range(G))
+    need = np.array(sorted(need), dtype=np.int64)
+    print(f"case thd_32k glb bwd path={path}: {len(need)} oracle forward rows, {len(qrows)} dq rows, "
+          f"{len(krows)} dk/dv rows", flush=True)
+    o, l = oracle.prefill_rows(d["q"], d["k"], d["v"], d["sink"], d["cu_seqlens"], d["window"], d["rope_base"],
+                               rows=need)
+    O = torch.zeros(T * hq, 128, dtype=torch.bfloat16)
+    O[torch.from_numpy(need)] = torch.from_numpy(o).to(torch.bfloat16)
+    O = O.reshape(T, hq, 128)
+    L = torch.full((T * hq,), 1e4, dtype=torch.float32)
+    L[torch.from_numpy(need)] = torch.from_numpy(l).to(torch.float32)
+    L = L.reshape(T, hq).T.contiguous()
+    dq, dk, dv, _ = _run_bwd(ga, d, O, L, dO, path)
+    rq = oracle.bwd_dq_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"], d["rope_base"],
+                            qrows, out_given=O)
+    compare("dq (sampled)", dq.reshape(-1, 192)[qrows], rq, bf16_halfulp=True)
+    rk, rv = oracle.bwd_dkv_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"],
+                                 d["rope_base"], krows, out_given=O)
+    compare("dk (sampled)", dk.reshape(-1, 192)[krows], rk, bf16_halfulp=True)
+    compare("dv (sampled)", dv.reshape(-1, 128)[krows], rv, bf16_halfulp=True)
+
+
+@pytest.mark.parametrize("path", ["fast", "least"])
 def test_bwd_global_small_batch_sampled(path):
     """Global layer on a 2 x 2048 batch (the oracle's full forward stays fast): sampled rows."""
     ga = _gpu()
