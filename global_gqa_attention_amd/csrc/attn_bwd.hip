@@ -951,12 +951,16 @@ __global__ __launch_bounds__(64 * NH, 1) void bwd_dq_ds_kernel(const BwdArgs A)
     }
     wait_vmcnt<0>();
 
-    // ---- epilogue: dq = R^T dQ^T / sqrt(192) for this lane's query
+    // ---- epilogue: dq = R^T dQ^T / sqrt(192) for this lane's query.  The tile leaves through the idle ring:
+    // every wave puts its head's 32 rows there (row c NH + wave, 16-byte chunks XOR-swizzled by query within
+    // groups of eight), then each store instruction writes whole runs of the NH heads of a query.
     const int qt = q0 + c;
-    if (qt >= seq_start && qt < seq_end) {
-        const float2 *qcs = a.rope + (size_t)min(qt - seq_start, a.rope_len - 1) * NHALF;
-        rope_back(dq[0], dq[1], qcs, hh);
-        u16 *dqp = A.dq + ((size_t)qt * a.hq + h) * DQK + 4 * hh;
+    const float2 *qcs = a.rope + (size_t)min(max(qt - seq_start, 0), a.rope_len - 1) * NHALF;
+    rope_back(dq[0], dq[1], qcs, hh);
+    __syncthreads();                        // every wave is done reading the ring
+    uint4 *stg = (uint4 *)ring;
+    {
+        u16 *row = (u16 *)(stg + (c * NH + wave) * KCH) + 4 * hh;
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
 #pragma unroll
@@ -964,9 +968,19 @@ __global__ __launch_bounds__(64 * NH, 1) void bwd_dq_ds_kernel(const BwdArgs A)
                 bf16x4 w;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) w[t] = f2bf(dq[i][4 * jj + t] * RSQRT_DQK);
-                *(uint2 *)(dqp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                const int k = 4 * i + jj;
+                *(uint2 *)(row + 8 * ((k & ~7) | ((k & 7) ^ (c & 7)))) = __builtin_bit_cast(uint2, w);
             }
         }
+    }
+    __syncthreads();
+    const int h0 = kvh * G + hg * NH;
+#pragma unroll
+    for (int j = 0; j < 32 * KCH / 64; ++j) {
+        const int g = 64 * NH * j + tid, R = g / KCH, k = g % KCH, qc = R / NH, w = R % NH;
+        const uint4 x = stg[R * KCH + ((k & ~7) | ((k & 7) ^ (qc & 7)))];
+        if (q0 + qc >= seq_start && q0 + qc < seq_end)
+            st16u(A.dq + ((size_t)(q0 + qc) * a.hq + h0 + w) * DQK + 8 * k, x);
     }
 }
 

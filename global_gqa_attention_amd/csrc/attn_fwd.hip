@@ -55,7 +55,8 @@ __device__ __forceinline__ int vpos(int d, int q) { return BN == 64 ? swz128(d, 
 // that three workgroups fit on a CU (OCC): these short work items wait mostly on HBM (Q and the first
 // tiles), and more resident workgroups keep more loads in flight.  Their q (48 KB) passes through the same
 // LDS first: a lane that loads its own row touches 32 rows per load instruction, while the copy into LDS
-// reads whole runs of rows per instruction; the rotated q for the backward leaves the same way.
+// reads whole runs of rows per instruction; the rotated q for the backward leaves the same way.  Both
+// forms write O through LDS in the same manner once the key loop is done.
 template <int NW, int GP, bool SINK, bool WIN, int BN, int KA, int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
 {
@@ -361,11 +362,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     }
     wait_vmcnt<0>();                        // no load may still target this workgroup's LDS at exit
 
-    // ---- epilogue: out = 0.707 * O / l, LSE = ln(l) + max
+    // ---- epilogue: out = 0.707 * O / l, LSE = ln(l) + max.  O leaves through the idle K/V ring: each lane
+    // puts its row there (16-byte chunks XOR-swizzled by row), then every store instruction writes whole
+    // runs of rows instead of touching 32 rows.
     const float l_tot = pair_sum(l_run);
-    if (qvalid) {
-        const float inv = VSCALE / l_tot;
-        u16 *op = A.out + ((size_t)qt * a.hq + qh) * DVV + 4 * hh;
+    const float inv = VSCALE / l_tot;
+    if (qvalid && A.lse && hh == 0) A.lse[(size_t)qh * a.T + qt] = (m_run + __log2f(l_tot)) * LN2;
+    __builtin_amdgcn_s_barrier();           // every wave is done reading the ring
+    {
+        // the lane index again from mbcnt: cheaper to recompute here than to keep across the key loop
+        const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int lc = ln & 31, lh = ln >> 5;
+        u16 *orow = (u16 *)lds + (size_t)(wave * 32 + lc) * DVV + 4 * lh;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -373,10 +381,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
                 bf16x4 w;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) w[t] = f2bf(o[i][4 * jj + t] * inv);
-                *(uint2 *)(op + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                *(uint2 *)(orow + 8 * ((4 * i + jj) ^ (lc & 15))) = __builtin_bit_cast(uint2, w);
             }
         }
-        if (A.lse && hh == 0) A.lse[(size_t)qh * a.T + qt] = (m_run + __log2f(l_tot)) * LN2;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own rows, read by its lanes
+        const uint4 *ws = lds + wave * 32 * (DVV / 8);
+        u16 *obase = A.out + ((size_t)t0 * a.hq + h0) * DVV;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int g = 64 * j + ln, rw = g >> 4, p = g & 15, r = wave * 32 + rw;
+            const uint4 x = ws[16 * rw + (p ^ (rw & 15))];
+            if (t0 + r / GP < seq_end) st16u(obase + (uint32_t)(((r / GP) * a.hq + r % GP) * DVV + 8 * p), x);
+        }
     }
 }
 
