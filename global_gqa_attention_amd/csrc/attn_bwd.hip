@@ -98,27 +98,34 @@ __device__ __forceinline__ void rope_back(f32x16 &x0, f32x16 &x1, const float2 *
 // ------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A)
 {
+    // a block owns 16 tokens x 16 heads: per token the 16 heads' dO and O rows are one contiguous run (a
+    // 16-lane group per row), and D and LSE*log2(e) of a head are written as 16 consecutive values
+    __shared__ float sd[16][17];
     const int tid = threadIdx.x, g = tid >> 4, sub = tid & 15;
-    const long rows = (long)A.T_pad * A.L.hq;
-    const long r0 = (long)blockIdx.x * 64;
-    for (long r = r0 + g; r < rows && r < r0 + 64; r += 16) {
-        const int t = (int)(r / A.L.hq), h = (int)(r % A.L.hq);
-        float s = 0.f, l2 = 0.f;
-        if (t < A.L.T) {
+    const int t0 = blockIdx.x * 16, h = blockIdx.y * 16 + g;
+    const int T = A.L.T, hq = A.L.hq;
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+        const int t = t0 + it;
+        float s = 0.f;
+        if (t < T && h < hq) {
+            const size_t r = (size_t)t * hq + h;
             const bf16x8 x = ld16(A.dout + r * DVV + 8 * sub);
             const bf16x8 y = ld16(A.out + r * DVV + 8 * sub);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s += bf2f(x[e]) * bf2f(y[e]);
-            l2 = A.lse[(size_t)h * A.L.T + t] * LOG2E;
         }
         s += __shfl_xor(s, 8, 16);
         s += __shfl_xor(s, 4, 16);
         s += __shfl_xor(s, 2, 16);
         s += __shfl_xor(s, 1, 16);
-        if (sub == 0) {
-            A.delta[(size_t)h * A.T_pad + t] = s;
-            A.lse2[(size_t)h * A.T_pad + t] = l2;
-        }
+        if (sub == 0) sd[g][it] = s;
+    }
+    __syncthreads();
+    if (h < hq) {
+        const int t = t0 + sub;
+        A.delta[(size_t)h * A.T_pad + t] = sd[g][sub];
+        A.lse2[(size_t)h * A.T_pad + t] = t < T ? A.lse[(size_t)h * T + t] * LOG2E : 0.f;
     }
 }
 
@@ -483,6 +490,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             stage(st + 2, ring[2], ring[0]);
         }
         wait_vmcnt<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();       // the epilogue's barrier (the gradient waves reuse the LDS)
     } else {
         // ================= gradient waves (one step behind): dV^T += dO^T P and dK^T += Q'^T dS, with the
         // transposed operands read from the step's row tiles and P, dS from the score wave of these keys
@@ -534,25 +543,62 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             stage(st + 2, ring[1], ring[0]);
         }
         wait_vmcnt<0>();
-        // ---- epilogue: dv = 0.707 dV^T, dk = R^T dK^T / sqrt(192) (fp32 partials with several head splits)
+        // ---- epilogue: dv = 0.707 dV^T, dk = R^T dK^T / sqrt(192) (fp32 partials with several head splits).
+        // The rows leave through LDS (this wave's 12 KB of the ring for dk, 8 KB of the hand-over buffers for
+        // dv, once every wave is past its last read of them): the lanes put their rows in (16-byte chunks
+        // XOR-swizzled by row), then each store instruction writes whole rows.
         const float2 *cs = a.rope + (size_t)min(kjl - seq_start, a.rope_len - 1) * NHALF;
         rope_back(dk[0], dk[1], cs, hh);
-        if (kvalid && A.splits > 1) {
-            float *pp = A.dkv_part + (((size_t)split * A.T_pad + kj) * a.hkv + kvh) * (DQK + DVV) + 4 * hh;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        uint4 *kst = (uint4 *)ring + kq * 32 * QCH;
+        uint4 *vst = &pbuf[0][0][0] + kq * 32 * OCH;
+        if (A.splits > 1) {
+            // fp32 rows of 48 (dk) + 32 (dv) chunks: two rounds of 16 keys
 #pragma unroll
-            for (int i = 0; i < 6; ++i)
+            for (int rd = 0; rd < 2; ++rd) {
+                if ((c >> 4) == rd) {
+                    const int r = c & 15;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    *(float4 *)(pp + 32 * i + 8 * jj) = make_float4(dk[i][4 * jj] * RSQRT_DQK, dk[i][4 * jj + 1] * RSQRT_DQK,
-                                                                    dk[i][4 * jj + 2] * RSQRT_DQK, dk[i][4 * jj + 3] * RSQRT_DQK);
+                    for (int i = 0; i < 6; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const int k = 8 * i + 2 * jj + hh;
+                            kst[48 * r + ((k & ~15) | ((k & 15) ^ r))] =
+                                __builtin_bit_cast(uint4, make_float4(dk[i][4 * jj] * RSQRT_DQK, dk[i][4 * jj + 1] * RSQRT_DQK,
+                                                                      dk[i][4 * jj + 2] * RSQRT_DQK, dk[i][4 * jj + 3] * RSQRT_DQK));
+                        }
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    *(float4 *)(pp + DQK + 32 * i + 8 * jj) = make_float4(dv[i][4 * jj] * VSCALE, dv[i][4 * jj + 1] * VSCALE,
-                                                                          dv[i][4 * jj + 2] * VSCALE, dv[i][4 * jj + 3] * VSCALE);
-        } else if (kvalid) {
-            u16 *dkp = A.dk + ((size_t)kj * a.hkv + kvh) * DQK + 4 * hh;
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const int k = 8 * i + 2 * jj + hh;
+                            vst[32 * r + ((k & ~15) | ((k & 15) ^ r))] =
+                                __builtin_bit_cast(uint4, make_float4(dv[i][4 * jj] * VSCALE, dv[i][4 * jj + 1] * VSCALE,
+                                                                      dv[i][4 * jj + 2] * VSCALE, dv[i][4 * jj + 3] * VSCALE));
+                        }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own rows, read by its lanes
+#pragma unroll
+                for (int j = 0; j < 12; ++j) {
+                    const int g = 64 * j + lane, r = g / 48, p = g % 48, k = (p & ~15) | ((p & 15) ^ r);
+                    const int key = kw0 + 16 * rd + r;
+                    const uint4 x = kst[g];
+                    if (key <= kb_last)
+                        *(uint4 *)(A.dkv_part + (((size_t)split * A.T_pad + key) * a.hkv + kvh) * (DQK + DVV) + 4 * k) = x;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int g = 64 * j + lane, r = g >> 5, p = g & 31, k = (p & ~15) | ((p & 15) ^ r);
+                    const int key = kw0 + 16 * rd + r;
+                    const uint4 x = vst[g];
+                    if (key <= kb_last)
+                        *(uint4 *)(A.dkv_part + (((size_t)split * A.T_pad + key) * a.hkv + kvh) * (DQK + DVV) + DQK + 4 * k) = x;
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next round's writes
+            }
+        } else {
+            // bf16 rows of 24 (dk) + 16 (dv) chunks
 #pragma unroll
             for (int i = 0; i < 6; ++i) {
 #pragma unroll
@@ -560,10 +606,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
                     bf16x4 w;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) w[t] = f2bf(dk[i][4 * jj + t] * RSQRT_DQK);
-                    *(uint2 *)(dkp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                    const int k = 4 * i + jj;
+                    *(uint2 *)((u16 *)(kst + QCH * c + ((k & ~7) | ((k & 7) ^ (c & 7)))) + 4 * hh) = __builtin_bit_cast(uint2, w);
                 }
             }
-            u16 *dvp = A.dv + ((size_t)kj * a.hkv + kvh) * DVV + 4 * hh;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -571,12 +617,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
                     bf16x4 w;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) w[t] = f2bf(dv[i][4 * jj + t] * VSCALE);
-                    *(uint2 *)(dvp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                    const int k = 4 * i + jj;
+                    *(uint2 *)((u16 *)(vst + OCH * c + (k ^ (c & 15))) + 4 * hh) = __builtin_bit_cast(uint2, w);
                 }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < 12; ++j) {
+                const int g = 64 * j + lane, r = g / QCH, p = g % QCH, k = (p & ~7) | ((p & 7) ^ (r & 7));
+                const uint4 x = kst[g];
+                if (kw0 + r <= kb_last) st16u(A.dk + ((size_t)(kw0 + r) * a.hkv + kvh) * DQK + 8 * k, x);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = 64 * j + lane, r = g >> 4, p = g & 15, k = p ^ (r & 15);
+                const uint4 x = vst[g];
+                if (kw0 + r <= kb_last) st16u(A.dv + ((size_t)(kw0 + r) * a.hkv + kvh) * DVV + 8 * k, x);
             }
         }
     }
 }
+
 
 // sum of the head-split partials, in split order (deterministic): one thread per 8 of the 320 values
 __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(const BwdArgs A)
@@ -1096,11 +1157,10 @@ void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A, bool stored_ds, int
 hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
 {
     const LayerArgs &a = A.L;
-    const long rows = (long)A.T_pad * a.hq;
-    const long pre_blocks = (rows + 63) / 64;
-    if (pre_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    const dim3 pre_grid((unsigned)(A.T_pad / 16), (unsigned)((a.hq + 15) / 16));   // T_pad is a multiple of 16
+    if (pre_grid.y > 65535) return hipErrorInvalidConfiguration;
     trace_begin(a.window >= 0 ? "bwd_pre_swa" : "bwd_pre_global", stream);
-    bwd_pre_kernel<<<(unsigned)pre_blocks, 256, 0, stream>>>(A);
+    bwd_pre_kernel<<<pre_grid, 256, 0, stream>>>(A);
     trace_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
