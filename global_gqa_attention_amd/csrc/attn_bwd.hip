@@ -132,23 +132,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A)
 // ------------------------------------------------------------------------------------------------------
 // 2. dsink_h = -sum_t exp(sink_h - LSE_t) D_t, fixed order
 // ------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dsink_kernel(const BwdArgs A)
+__global__ __launch_bounds__(1024) void bwd_dsink_kernel(const BwdArgs A)
 {
-    __shared__ float red[256];
+    // one workgroup per head: each thread sums a fixed stride of tokens, then the wave sums (shuffle tree)
+    // and the 16 wave totals in wave order
+    __shared__ float red[16];
     const int h = blockIdx.x, tid = threadIdx.x;
     const float sk = A.L.sink[h];
     float acc = 0.f;
     if (sk > -INFINITY) {
         const float *lse = A.lse + (size_t)h * A.L.T, *dl = A.delta + (size_t)h * A.T_pad;
-        for (int t = tid; t < A.L.T; t += 256) acc -= expf(sk - lse[t]) * dl[t];
+#pragma unroll 4
+        for (int t = tid; t < A.L.T; t += 1024) acc -= expf(sk - lse[t]) * dl[t];
     }
-    red[tid] = acc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if ((tid & 63) == 0) red[tid >> 6] = acc;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] += red[tid + s];
-        __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) s += red[w];
+        A.dsink[h] = s;
     }
-    if (tid == 0) A.dsink[h] = red[0];
 }
 
 __global__ void zero_kernel(float *p, int n)
@@ -870,9 +876,16 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
     }
     wait_vmcnt<0>();
 
-    if (qvalid) {
-        rope_back(dq[0], dq[1], qcs, hh);
-        u16 *dqp = A.dq + ((size_t)qt * a.hq + qh) * DQK + 4 * hh;
+    // ---- epilogue: dq = R^T dQ^T / sqrt(192).  The rows leave through the idle ring (12 KB per wave, two
+    // waves per tile buffer; 16-byte chunks XOR-swizzled by row): the lanes put their rows in, then each
+    // store instruction writes whole runs of rows (the GP heads of a token are contiguous)
+    rope_back(dq[0], dq[1], qcs, hh);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();           // every wave is done reading the ring
+    static_assert(NW <= 4 && sizeof(DqTile) >= 2 * 32 * KCH * sizeof(uint4), "two waves' rows per tile buffer");
+    uint4 *stg = (uint4 *)(wave < 2 ? &t0s : &t1s) + (wave & 1) * 32 * KCH;
+    {
+        u16 *row = (u16 *)(stg + c * KCH) + 4 * hh;
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
 #pragma unroll
@@ -880,9 +893,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
                 bf16x4 w;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) w[t] = f2bf(dq[i][4 * jj + t] * RSQRT_DQK);
-                *(uint2 *)(dqp + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+                const int k = 4 * i + jj;
+                *(uint2 *)(row + 8 * ((k & ~7) | ((k & 7) ^ (c & 7)))) = __builtin_bit_cast(uint2, w);
             }
         }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own rows, read by its lanes
+#pragma unroll
+    for (int j = 0; j < 12; ++j) {
+        const int g = 64 * j + lane, rw = g / KCH, p = g % KCH, k = (p & ~7) | ((p & 7) ^ (rw & 7));
+        const int r = wave * 32 + rw, tok = t0 + r / GP;
+        const uint4 x = stg[g];
+        if (tok < seq_end) st16u(A.dq + ((size_t)tok * a.hq + h0 + r % GP) * DQK + 8 * k, x);
     }
 }
 
@@ -1166,7 +1188,7 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     if (e != hipSuccess) return e;
     if (A.dsink) {
         trace_begin(a.window >= 0 ? "bwd_dsink_swa" : "bwd_dsink_global", stream);
-        bwd_dsink_kernel<<<a.hq, 256, 0, stream>>>(A);
+        bwd_dsink_kernel<<<a.hq, 1024, 0, stream>>>(A);
         trace_end(stream);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
