@@ -53,10 +53,10 @@ __device__ __forceinline__ int vpos(int d, int q) { return BN == 64 ? swz128(d, 
 // waves, 64-key tiles in a 3-stage ring (120 KB), one workgroup per CU, all 12 K operands of a block read
 // up front (KA = 12).  Sliding-window layers: 4 waves, 32-key tiles double-buffered (40 KB) and KA = 4 so
 // that three workgroups fit on a CU (OCC): these short work items wait mostly on HBM (Q and the first
-// tiles), and more resident workgroups keep more loads in flight.  Their q (48 KB) passes through the same
-// LDS first: a lane that loads its own row touches 32 rows per load instruction, while the copy into LDS
-// reads whole runs of rows per instruction; the rotated q for the backward leaves the same way.  Both
-// forms write O through LDS in the same manner once the key loop is done.
+// tiles), and more resident workgroups keep more loads in flight.  In both forms q passes through LDS first
+// (48 KB at the start of the pool, or 96 KB behind the first tile's buffer, 136 KB in all): a lane that
+// loads its own row touches 32 rows per load instruction, while the copy into LDS reads whole runs of rows
+// per instruction; the rotated q for the backward and, after the key loop, O leave the same way.
 template <int NW, int GP, bool SINK, bool WIN, int BN, int KA, int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
 {
@@ -68,8 +68,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     const LayerArgs &a = A.L;
     constexpr int NBUF = NW == 8 ? 3 : 2;      // LDS stages (3 x 40 KB for one 8-wave workgroup per CU)
     constexpr int KS = BN * KCH, VS = DVV * VCH;                 // 16-byte chunks of a K and a V^T tile
-    constexpr int QS = WIN ? BM * KCH : 0;                       // the workgroup's q rows (sliding window)
-    constexpr int POOL = NBUF * (KS + VS) > QS ? NBUF * (KS + VS) : QS;
+    // the workgroup's q rows pass through LDS first: sliding window from the start of the pool (the first
+    // tile is issued after them), causal behind the first tile's buffer (the first tile is in flight meanwhile)
+    constexpr int QOFF = WIN ? 0 : KS + VS, QEND = QOFF + BM * KCH;
+    constexpr int POOL = NBUF * (KS + VS) > QEND ? NBUF * (KS + VS) : QEND;
     __shared__ __attribute__((aligned(16))) uint4 lds[POOL];
     uint4 *const sK0 = lds, *const sV0 = lds + KS, *const sK1 = lds + KS + VS, *const sV1 = lds + 2 * KS + VS;
     uint4 *const sK2 = lds + 2 * (KS + VS), *const sV2 = lds + 3 * KS + 2 * VS;   // NBUF == 3 only
@@ -151,63 +153,46 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         const int qtl = qvalid ? qt : t_last;
         const float2 *cs = a.rope + (size_t)min(max(qtl + pofs, 0), a.rope_len - 1) * NHALF + 8 * hh;
         float2 c0[8], c1[8];
-        if constexpr (WIN) {
-            // the wave's 32 rows (768 16-byte chunks, GP-row runs contiguous in memory) are copied into
-            // LDS by whole runs, chunk slot g by instruction g / 64, swizzled like a K tile; each lane then
-            // reads its own row and rotates it.  The rotated q for the backward leaves the same way: the
-            // rotated chunks go back into their slots and each instruction stores whole runs.  The first
-            // K/V tile is issued into the same LDS once every wave is done with its q.
-            const u16 *qbase = a.q + ((size_t)t0 * a.hq + h0) * DQK;
-            uint4 *qs = lds + 32 * KCH * wave;
+        // the wave's 32 rows (768 16-byte chunks, GP-row runs contiguous in memory) are copied into LDS by
+        // whole runs, chunk slot g by instruction g / 64, swizzled like a K tile; each lane then reads its
+        // own row and rotates it.  The rotated q for the backward leaves the same way: the rotated chunks go
+        // back into their slots and each instruction stores whole runs.  The next K/V tile is issued into
+        // this LDS once every wave is done with its q (sliding window: the first tile; causal: the second,
+        // the first being in flight meanwhile in its own buffer).
+        const u16 *qbase = a.q + ((size_t)t0 * a.hq + h0) * DQK;
+        uint4 *qs = lds + QOFF + 32 * KCH * wave;
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            const int g = 64 * i + lane, rw = g / KCH, rr = wave * 32 + rw;
+            const int tk = min(rr / GP, t_last - t0);
+            lds_dma16(qbase, (uint32_t)(((tk * a.hq + rr % GP) * DQK + 8 * kpos(rw, g % KCH)) * 2), qs + 64 * i);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            c0[t] = cs[t];
+            c1[t] = cs[16 + t];
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int s = 0; s < 12; ++s) qf[s] = __builtin_bit_cast(bf16x8, qs[KCH * c + kpos(c, 2 * s + hh)]);
+        rope_pair(qf[0], qf[2], c0);
+        rope_pair(qf[1], qf[3], c1);
+        if (A.q_rot) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qs[KCH * c + kpos(c, 2 * s + hh)] = __builtin_bit_cast(uint4, qf[s]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own slots, read by its lanes
 #pragma unroll
             for (int i = 0; i < 12; ++i) {
                 const int g = 64 * i + lane, rw = g / KCH, rr = wave * 32 + rw;
-                const int tk = min(rr / GP, t_last - t0);
-                lds_dma16(qbase, (uint32_t)(((tk * a.hq + rr % GP) * DQK + 8 * kpos(rw, g % KCH)) * 2), qs + 64 * i);
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                c0[t] = cs[t];
-                c1[t] = cs[16 + t];
-            }
-            wait_vmcnt<0>();
-#pragma unroll
-            for (int s = 0; s < 12; ++s) qf[s] = __builtin_bit_cast(bf16x8, qs[KCH * c + kpos(c, 2 * s + hh)]);
-            rope_pair(qf[0], qf[2], c0);
-            rope_pair(qf[1], qf[3], c1);
-            if (A.q_rot) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) qs[KCH * c + kpos(c, 2 * s + hh)] = __builtin_bit_cast(uint4, qf[s]);
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own slots, read by its lanes
-#pragma unroll
-                for (int i = 0; i < 12; ++i) {
-                    const int g = 64 * i + lane, rw = g / KCH, rr = wave * 32 + rw;
-                    const int tok = t0 + rr / GP;
-                    const uint4 x = qs[g];
-                    if (tok < seq_end)
-                        st16u(A.q_rot + ((size_t)tok * a.hq + h0 + rr % GP) * DQK + 8 * kpos(rw, g % KCH), x);
-                }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            issue_tile(kstart, sK0, sV0);
-        } else {
-            const u16 *qp = a.q + ((size_t)qtl * a.hq + qh) * DQK + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                c0[t] = cs[t];
-                c1[t] = cs[16 + t];
-            }
-            rope_pair(qf[0], qf[2], c0);
-            rope_pair(qf[1], qf[3], c1);
-            if (A.q_rot && qvalid) {   // the rotated q for the backward: this lane's 12 chunks of its row
-                u16 *qo = A.q_rot + ((size_t)qt * a.hq + qh) * DQK + 8 * hh;
-#pragma unroll
-                for (int s = 0; s < 12; ++s) st16(qo + 16 * s, qf[s]);
+                const int tok = t0 + rr / GP;
+                const uint4 x = qs[g];
+                if (tok < seq_end)
+                    st16u(A.q_rot + ((size_t)tok * a.hq + h0 + rr % GP) * DQK + 8 * kpos(rw, g % KCH), x);
             }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if constexpr (WIN) issue_tile(kstart, sK0, sV0);
     }
 
     // this wave's rows sit at key indices [wt0, wt1]; 32-key blocks outside [wklo, wkhi] are skipped
