@@ -263,6 +263,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const LayerArgs &a = A.L;
     __shared__ __attribute__((aligned(16))) DkdvTile ring[3];          // tiles of steps st-1, st, st+1
     __shared__ __attribute__((aligned(16))) uint4 pbuf[2][4][256];     // P and dS (bf16) of a step: 4 planes x 64 lanes
+    __shared__ __attribute__((aligned(16))) uint4 kstage[4 * 32 * QCH]; // the score waves' k' rows, at the start
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -387,12 +388,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         // dS (bf16) go to the gradient wave of the same keys through LDS, dS also to the stored-dS blocks
         bf16x8 kf[12], vf[8];
         {
-            const u16 *kp = A.W.kr + ((size_t)kjl * a.hkv + kvh) * DQK + 8 * hh;
+            // the wave's 32 k' and v rows are copied into LDS by whole rows (chunk slot g by instruction
+            // g / 64; k' into its staging array, v into the hand-over buffers, which no wave writes before
+            // the first stage's barrier), then each lane reads its own row: a lane that loads its own row
+            // touches 32 rows per load instruction
+            uint4 *ks = kstage + 32 * QCH * kq;
+            uint4 *vs = &pbuf[0][0][0] + 32 * OCH * kq;
+            const u16 *kbase = A.W.kr + ((size_t)kb0 * a.hkv + kvh) * DQK;
+            const u16 *vbase = a.v + ((size_t)kb0 * a.hkv + kvh) * DVV;
 #pragma unroll
-            for (int s = 0; s < 12; ++s) kf[s] = ld16(kp + 16 * s);
-            const u16 *vp = a.v + ((size_t)kjl * a.hkv + kvh) * DVV + 8 * hh;
+            for (int i = 0; i < 12; ++i) {
+                const int g = 64 * i + lane, rw = g / QCH, row = min(kw0 + rw, kb_last) - kb0;
+                lds_dma16(kbase, (uint32_t)((row * a.hkv * DQK + 8 * swz384(rw, g % QCH)) * 2), ks + 64 * i);
+            }
 #pragma unroll
-            for (int s = 0; s < 8; ++s) vf[s] = ld16(vp + 16 * s);
+            for (int i = 0; i < 8; ++i) {
+                const int g = 64 * i + lane, rw = g / OCH, row = min(kw0 + rw, kb_last) - kb0;
+                lds_dma16(vbase, (uint32_t)((row * a.hkv * DVV + 8 * swz256(rw, g % OCH)) * 2), vs + 64 * i);
+            }
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int s = 0; s < 12; ++s) kf[s] = __builtin_bit_cast(bf16x8, ks[QCH * c + swz384(c, 2 * s + hh)]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) vf[s] = __builtin_bit_cast(bf16x8, vs[OCH * c + swz256(c, 2 * s + hh)]);
         }
         // operand k: q' rows (S, k < 12), then dO rows (dP, k - 12)
         auto load_op = [&](int k, const DkdvTile &T) -> bf16x8 {
