@@ -53,12 +53,23 @@ def pairs_per_head(lengths, window):
     return tot
 
 
-def kernel_source_hash():
+def code_only(text):
+    """C++ source with comments and whitespace removed (string literals kept as they are)."""
+    import re
+
+    pat = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
+    text = pat.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return re.sub(r"\s+", "", text)
+
+
+def kernel_source_hash(csrc=None):
+    """Hash of the kernel sources' code (comments and whitespace do not count): the traffic counters in
+    profiles/traffic.json stand only for the code they were taken on."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "global_gqa_attention_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "global_gqa_attention_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(f.encode() + b"\0" + code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

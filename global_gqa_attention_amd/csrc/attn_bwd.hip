@@ -11,8 +11,9 @@
 //
 // Kernels, all on the caller's stream, no atomics (every output is written by exactly one workgroup and
 // dsink is summed in a fixed order, so results are bitwise repeatable):
-//   1. bwd_pre:   D and LSE * log2(e) for every (head, token), zero-padded to T_pad.
-//   2. bwd_dsink: one workgroup per head, fixed-order tree sum (only when a sink is given).
+//   1. bwd_pre:   D and LSE * log2(e) for every (head, token), zero-padded to T_pad; a block owns 16 tokens
+//                 x 16 heads, so each head's 16 values are written together.
+//   2. bwd_dsink: one 1024-thread workgroup per head, fixed-order tree sum (only when a sink is given).
 //   3. row_prep:  DMA-ready copies in the workspace: q' (rotated) row-major, k' (rotated) row-major and
 //                 transposed (the transposed copy keeps each 16-token group's 4-token chunks in the order
 //                 (0, 2, 1, 3), the order in which the score registers hold tokens).
@@ -26,7 +27,10 @@
 //   5. bwd_dq:    either from the stored dS blocks (5b: dQ^T += K'^T dS^T, no recomputation), or
 //                 query-major like the forward: S^T = K'Q'^T, P^T, dP^T = V dO^T, dS^T, then
 //                 dQ^T += K'^T dS^T with k' (both layouts) and v streamed HBM -> LDS.
-// dq and dk leave through the transposed rotation in their epilogues.
+// dq and dk leave through the transposed rotation in their epilogues.  Rows that a lane owns (the dK/dV score
+// waves' k' and v at the start; dq, dk, dv and the fp32 partials at the end) move between HBM and the lanes
+// through LDS that is idle at that moment, so that each memory instruction covers whole rows instead of one
+// 16-byte piece of each of 32 rows.
 #include <type_traits>
 
 #include "device_common.hpp"
