@@ -84,3 +84,22 @@ def test_cached_pairs_counts_visible_keys():
         return tot
     for chunks, rows, window in [([3, 2, 0], [4, 0, 9], -1), ([5, 130], [200, 3], 128), ([7], [2], 0)]:
         assert bench.cached_pairs(chunks, rows, window) == brute(chunks, rows, window)
+
+
+def test_kernel_hash_ignores_comments_only(tmp_path):
+    """The traffic counters are tied to the kernels' code: a comment or whitespace edit keeps the hash, a code
+    edit (even inside a line that also holds a comment, or in a string) changes it."""
+    d = tmp_path / "csrc"
+    d.mkdir()
+    src = 'int f(int a) { // add one\n  return a + 1; /* done */ }\nconst char *s = "x // y";\n'
+    (d / "k.hip").write_text(src)
+    h0 = bench.kernel_source_hash(str(d))
+    (d / "k.hip").write_text(src.replace("// add one", "// adds one to a").replace("  return", "\treturn"))
+    assert bench.kernel_source_hash(str(d)) == h0
+    (d / "k.hip").write_text(src.replace("a + 1", "a + 2"))
+    assert bench.kernel_source_hash(str(d)) != h0
+    (d / "k.hip").write_text(src.replace('"x // y"', '"x // z"'))
+    assert bench.kernel_source_hash(str(d)) != h0
+    (d / "notes.txt").write_text("not a source")
+    (d / "k.hip").write_text(src)
+    assert bench.kernel_source_hash(str(d)) == h0
