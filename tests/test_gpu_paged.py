@@ -191,6 +191,7 @@ def test_serving_loop_matches_whole_prefill(hkv, window, sink, base):
     ([5000, 0, 300, 128, 1020, 2047], 8, 128, True, 1e4, 8),
     ([40, 3, 1020], 2, 5, True, 1e4, 8),
     ([700, 1, 0], 4, -1, True, 1e7, 3),
+    ([3000, 77, 0, 513], 4, 128, True, 1e4, 6),    # 96 columns: three column blocks and an idle wave
 ])
 def test_verify_paged(prior, hkv, window, sink, base, nq):
     """nq draft tokens per sequence appended to a paged cache, then verified: against the oracle's prefill of
