@@ -12,9 +12,11 @@
 // up to split_len rows) and walks it in 32-row chunks.  Each chunk's K and V rows are copied HBM -> LDS by
 // direct-to-LDS loads whose 64 lanes cover whole rows (coalesced: the rows of one KV head are 1.5 KB
 // apart in the cache); S^T = K q^T takes K rows from LDS as MFMA A operands (the G query heads of the
-// group are the MFMA columns) and O^T = V^T P^T reads V transposed.  The chunk after the current one is
-// in flight while the current one is computed; two 20 KB buffers let four workgroups share a CU, which
-// keeps more bytes in flight than deeper rings with fewer workgroups.  Each split writes an unnormalised
+// group are the MFMA columns) and O^T = V^T P^T reads V transposed.  One 20 KB buffer per workgroup and
+// at most 256 registers per wave (K operands read four ahead of their MFMAs, V operands just before
+// theirs) let eight workgroups share a CU, two waves per SIMD: a wave's next chunk is copied while the
+// other wave on its SIMD computes, which kept more bytes in flight than two buffers at four workgroups per
+// CU or deeper rings with fewer.  Each split writes an unnormalised
 // partial (o, running max, running sum); the combine kernel merges the splits with the sink and the new
 // token (whose rotation is computed there in double precision).
 //
@@ -35,9 +37,9 @@ constexpr int CH = 32;            // cache rows per chunk
 
 __device__ __forceinline__ double inv_freq(double base, int d) { return pow(base, -(double)d / (double)NHALF); }
 
-// LDS ring of a decode wave: chunk of CH cache rows of one KV head, K rows (chunk q of row r at
+// LDS buffer of a decode wave: chunk of CH cache rows of one KV head, K rows (chunk q of row r at
 // swz384(r, q): conflict-free 16-row operand reads) and V rows (chunk q at swz256t(r, q): conflict-free
-// transposed reads).  Two buffers: the next chunk is in flight while one is computed.
+// transposed reads).
 constexpr int DKC = DQK / 8;      // 16-byte chunks per K row (24)
 constexpr int DVC = DVV / 8;      // per V row (16)
 struct DecTile {
@@ -55,9 +57,9 @@ __device__ __forceinline__ const u16 *wave_uniform(const u16 *p)
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
 {
-    __shared__ __attribute__((aligned(256))) DecTile ring[2];
+    __shared__ __attribute__((aligned(256))) DecTile ring[1];   // one buffer (see the loop)
     const int lane = threadIdx.x, hh = lane >> 5, c = lane & 31;
     const int grp = lane >> 4, t4 = (lane & 15) >> 2, m4 = lane & 3;
     const int G = A.hq / A.hkv;
@@ -209,15 +211,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
         return (const char *)T.v + R * (DVC * 16) + 16 * swz256t(R, q) + 8 * (m4 & 1);
     };
     auto chunk = [&](int k, const DecTile &T) __attribute__((always_inline)) {
-        bf16x8 kop[12];
+        constexpr int KR = 4;             // K operands read ahead of their MFMA (a ring: fewer registers)
+        auto kread = [&](int s) __attribute__((always_inline)) {
+            return ld16((const u16 *)T.k + (c * DKC + swz384(c, 2 * s + hh)) * 8);
+        };
+        bf16x8 kop[KR];
 #pragma unroll
-        for (int s = 0; s < 12; ++s) kop[s] = ld16((const u16 *)T.k + (c * DKC + swz384(c, 2 * s + hh)) * 8);
+        for (int s = 0; s < KR; ++s) kop[s] = kread(s);
         f32x16 sacc = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 12; ++s) sacc = mfma32(kop[s], qf[s], sacc);
-        bf16x8 vop[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) vop[m] = tr_pair(vtr(T, m & 1, 0, m >> 1), vtr(T, m & 1, 1, m >> 1));
+        for (int s = 0; s < 12; ++s) {
+            sacc = mfma32(kop[s % KR], qf[s], sacc);
+            if (s + KR < 12) kop[s % KR] = kread(s + KR);
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -244,23 +250,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs A)
         m_run = m_new;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const bf16x8 v0 = tr_pair(vtr(T, 0, 0, i), vtr(T, 0, 1, i));
+            const bf16x8 v1 = tr_pair(vtr(T, 1, 0, i), vtr(T, 1, 1, i));
             o[i] *= alpha;
-            o[i] = mfma32(vop[2 * i], pf[0], o[i]);
-            o[i] = mfma32(vop[2 * i + 1], pf[1], o[i]);
+            o[i] = mfma32(v0, pf[0], o[i]);
+            o[i] = mfma32(v1, pf[1], o[i]);
         }
     };
 
-    // ---- two-buffer ring: wait for chunk k (the only loads in flight), load chunk k + CH into the buffer
-    // computed in the previous step (its LDS reads have completed: their results were consumed), then
-    // compute chunk k; unrolled by two so each step names its buffers
-    for (int k = ks; k < ke; k += 2 * CH) {
+    // ---- one buffer: wait for chunk k (the only loads in flight), compute it, wait until every LDS read of
+    // the buffer has returned, then copy chunk k + CH into it (the other wave on the SIMD computes meanwhile)
+    for (int k = ks; k < ke; k += CH) {
         wait_vmcnt<0>();
-        issue(k + CH, ring[1]);
         chunk(k, ring[0]);
-        if (k + CH >= ke) break;
-        wait_vmcnt<0>();
-        issue(k + 2 * CH, ring[0]);
-        chunk(k + CH, ring[1]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every read of the buffer has returned
+        if (k + CH < ke) issue(k + CH, ring[0]);
     }
     wait_vmcnt<0>();                        // no load may still target this workgroup's LDS at exit
 
