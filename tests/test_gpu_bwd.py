@@ -2,7 +2,8 @@
 
 The backward is given the forward outputs; both sides receive the same O (the oracle's forward rounded to
 bf16) and LSE (rounded to fp32), so D = rowsum(dO * O) uses the same O on both sides.  dq/dk/dv: max-abs
-2e-2 (widened by a bf16 half-ulp of |ref| where |ref| >= 8), mean-abs 2e-3; dsink: 1e-2 relative per head.
+2e-2 on the unrounded value plus the bf16 rounding of it (parity.grad_bound), mean-abs 2e-3; dsink: 1e-2
+relative per head.  Elements beyond the strict 2e-2 are counted per compare and summarised at session end.
 Both backward paths run: "fast" (a workspace that keeps the dS blocks, which the dQ kernel reads back) and
 "least" (the least workspace: dQ recomputes S and dP).
 """
@@ -68,9 +69,9 @@ def test_bwd_small_full(lengths, hq, hkv, window, base, sink, path):
     dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO, path)
     rq, rk, rv, rs = oracle.prefill_bwd(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], window, base,
                                         out_given=O)
-    compare("dq", dq, rq, bf16_halfulp=True)
-    compare("dk", dk, rk, bf16_halfulp=True)
-    compare("dv", dv, rv, bf16_halfulp=True)
+    compare("dq", dq, rq, grad=True)
+    compare("dk", dk, rk, grad=True)
+    compare("dv", dv, rv, grad=True)
     if sink:
         compare_rel("dsink", ds, rs)
     else:
@@ -114,7 +115,7 @@ def _sampled_bwd(ga, d, dO, nq, nk, heads, seed, path="fast"):
     qrows = rng.integers(0, T * hq, nq)
     rq = oracle.bwd_dq_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"], d["rope_base"],
                             qrows, out_given=O)
-    compare("dq (sampled)", dq.reshape(-1, 192)[qrows], rq, bf16_halfulp=True)
+    compare("dq (sampled)", dq.reshape(-1, 192)[qrows], rq, grad=True)
     toks = []
     for b in range(len(d["lengths"])):
         if d["lengths"][b]:
@@ -124,8 +125,8 @@ def _sampled_bwd(ga, d, dO, nq, nk, heads, seed, path="fast"):
     krows = toks * hkv + rng.integers(0, hkv, len(toks))
     rk, rv = oracle.bwd_dkv_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"],
                                  d["rope_base"], krows, out_given=O)
-    compare("dk (sampled)", dk.reshape(-1, 192)[krows], rk, bf16_halfulp=True)
-    compare("dv (sampled)", dv.reshape(-1, 128)[krows], rv, bf16_halfulp=True)
+    compare("dk (sampled)", dk.reshape(-1, 192)[krows], rk, grad=True)
+    compare("dv (sampled)", dv.reshape(-1, 128)[krows], rv, grad=True)
     if d["sink"] is not None:
         rs = oracle.bwd_dsink_heads(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"],
                                     d["rope_base"], heads, out_given=O)
@@ -186,11 +187,11 @@ def test_bwd_thd_32k_global_sampled(path):
     dq, dk, dv, _ = _run_bwd(ga, d, O, L, dO, path)
     rq = oracle.bwd_dq_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"], d["rope_base"],
                             qrows, out_given=O)
-    compare("dq (sampled)", dq.reshape(-1, 192)[qrows], rq, bf16_halfulp=True)
+    compare("dq (sampled)", dq.reshape(-1, 192)[qrows], rq, grad=True)
     rk, rv = oracle.bwd_dkv_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"],
                                  d["rope_base"], krows, out_given=O)
-    compare("dk (sampled)", dk.reshape(-1, 192)[krows], rk, bf16_halfulp=True)
-    compare("dv (sampled)", dv.reshape(-1, 128)[krows], rv, bf16_halfulp=True)
+    compare("dk (sampled)", dk.reshape(-1, 192)[krows], rk, grad=True)
+    compare("dv (sampled)", dv.reshape(-1, 128)[krows], rv, grad=True)
 
 
 @pytest.mark.parametrize("path", ["fast", "least"])
@@ -242,8 +243,8 @@ def test_bwd_many_sequences(window, hkv, sink, path):
     dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO, path)
     rq, rk, rv, rs = oracle.prefill_bwd(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], window, 1e4,
                                         out_given=O)
-    compare("dq", dq, rq, bf16_halfulp=True)
-    compare("dk", dk, rk, bf16_halfulp=True)
-    compare("dv", dv, rv, bf16_halfulp=True)
+    compare("dq", dq, rq, grad=True)
+    compare("dk", dk, rk, grad=True)
+    compare("dv", dv, rv, grad=True)
     if sink:
         compare_rel("dsink", ds, rs)
