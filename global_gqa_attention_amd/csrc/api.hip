@@ -124,6 +124,7 @@ mimo_status_t check_layer(const void *q, const void *k, const void *v, const int
     if (T > 0 && (!q || !k || !v || !cu)) return fail(MIMO_ERR_INVALID_ARG, "null input pointer");
     if (batch > 0 && !cu) return fail(MIMO_ERR_INVALID_ARG, "cu_seqlens is null");
     if ((long long)T * hq * kDQK > (1LL << 40)) return fail(MIMO_ERR_UNSUPPORTED, "tensor too large");
+    if (hq > 4096) return fail(MIMO_ERR_UNSUPPORTED, "n_q_heads above 4096 (got %d)", hq);
     return MIMO_OK;
 }
 
@@ -227,6 +228,8 @@ mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const f
     if (total_tokens > 0 && !out) return fail(MIMO_ERR_INVALID_ARG, "out is null");
     if (!mimo::fwd_group_supported(n_q_heads / n_kv_heads))
         return fail(MIMO_ERR_UNSUPPORTED, "no forward kernel for group size %d", n_q_heads / n_kv_heads);
+    if (!mimo::fwd_stream_fits(total_tokens))
+        return fail(MIMO_ERR_UNSUPPORTED, "total_tokens %d: the key stream passes the 32-bit copy offsets", total_tokens);
     if (total_tokens == 0) return ok();
     const size_t need = mimo::fwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
     if (!workspace || workspace_bytes < need)
@@ -258,14 +261,14 @@ mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const f
 size_t mimo_attn_fwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
                                     int32_t window)
 {
-    if (total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
+    if (total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || !mimo::fwd_stream_fits(total_tokens)) return 0;
     return mimo::fwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
 }
 
 size_t mimo_attn_prefill_cached_workspace_size(int32_t total_tokens, int32_t total_cache, int32_t n_kv_heads)
 {
     if (total_tokens < 0 || total_cache < 0 || n_kv_heads <= 0) return 0;
-    if ((long long)total_tokens + total_cache > 0x7fffff00LL) return 0;
+    if (!mimo::fwd_stream_fits((long long)total_tokens + total_cache)) return 0;
     return mimo::prep_bytes(total_tokens + total_cache, n_kv_heads);
 }
 
@@ -283,8 +286,9 @@ mimo_status_t prefill_over_cache(const void *q, const void *k, const void *v, co
                                   n_q_heads, n_kv_heads);
     if (s != MIMO_OK) return s;
     if (total_cache < 0) return fail(MIMO_ERR_INVALID_ARG, "total_cache must be >= 0 (got %d)", total_cache);
-    if ((long long)total_tokens + total_cache > 0x7fffff00LL)
-        return fail(MIMO_ERR_UNSUPPORTED, "total_tokens + total_cache too large");
+    if (!mimo::fwd_stream_fits((long long)total_tokens + total_cache))
+        return fail(MIMO_ERR_UNSUPPORTED, "total_tokens + total_cache = %lld: the key stream passes the 32-bit copy "
+                    "offsets", (long long)total_tokens + total_cache);
     if (max_position < max_seqlen)
         return fail(MIMO_ERR_INVALID_ARG, "max_position (%d) must be >= max_seqlen (%d)", max_position, max_seqlen);
     if (batch > 0 && (!cu_cache || !positions)) return fail(MIMO_ERR_INVALID_ARG, "cu_cache or positions is null");
@@ -380,7 +384,7 @@ mimo_status_t mimo_attn_cache_append(const void *k, const void *v, const int32_t
 size_t mimo_attn_bwd_workspace_size(int32_t total_tokens, int32_t n_q_heads, int32_t n_kv_heads,
                                     int32_t window)
 {
-    if (total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
+    if (total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || !mimo::bwd_stream_fits(total_tokens)) return 0;
     return mimo::bwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
 }
 
@@ -388,6 +392,7 @@ size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, in
                                          int32_t n_q_heads, int32_t n_kv_heads, int32_t window)
 {
     if (total_tokens < 0 || batch < 0 || max_seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
+    if (!mimo::bwd_stream_fits(total_tokens)) return 0;
     const size_t ds = mimo::bwd_workspace_bytes_ds(total_tokens, n_q_heads, n_kv_heads, window, batch, max_seqlen);
     return ds ? ds : mimo::bwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
 }
@@ -408,6 +413,8 @@ mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const f
         return fail(MIMO_ERR_INVALID_ARG, "null pointer among out/lse/dout/dq/dk/dv");
     if (!mimo::bwd_group_supported(n_q_heads / n_kv_heads))
         return fail(MIMO_ERR_UNSUPPORTED, "no backward kernel for group size %d", n_q_heads / n_kv_heads);
+    if (!mimo::bwd_stream_fits(total_tokens))
+        return fail(MIMO_ERR_UNSUPPORTED, "total_tokens %d: the key stream passes the 32-bit copy offsets", total_tokens);
     const size_t need = mimo::bwd_workspace_bytes(total_tokens, n_q_heads, n_kv_heads, window);
     if (total_tokens > 0 && (!workspace || workspace_bytes < need))
         return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);

@@ -110,12 +110,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
 
     // ---- key range: tiles start on a 16-key boundary (the V^T chunk order is per 16 keys); keys of a
     // previous sequence that this brings in are masked
+    // The prepared key stream has T_pad rows (a multiple of 16) and every tile read must stay inside it: the
+    // first tile starts at most at T_pad - BN, the last ends at most at row T_pad - 1, and a range that
+    // holds no tile gives no key step at all (these bounds bind only when the cache index arrays claim more
+    // rows than the sizes given; the rows are then wrong, but nothing outside the workspace is read).
     const int klo = WIN ? max(kseq, t0 + kofs - a.window) : kseq;
-    const int kstart = max(klo, 0) & ~15;
-    // the prepared key stream has T_pad rows and every tile read must stay inside it (binds only when the
-    // index arrays disagree with the sizes given)
+    const int kstart = min(max(klo, 0) & ~15, A.P.T_pad - BN);
     const int khi = min(t_last + kofs, A.P.T_pad - BN - 1);
-    const int nkt = (khi - kstart + BN) / BN;
+    const int nkt = max((khi - kstart + BN) / BN, 0);
 
     // ---- direct HBM -> LDS loads of one K tile and one V^T tile (slot s = NT j + tid of each array): the
     // per-lane byte offsets are fixed, the tile start is a wave-uniform base
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         }
     };
 
-    const int klast = kstart + (nkt - 1) * BN;
+    const int klast = kstart + max(nkt - 1, 0) * BN;   // first row of the last tile (kstart when there is none)
     if constexpr (NBUF == 3) {
         // ---- three-stage ring, unrolled by three so each step names its buffers.  Every step issues
         // exactly one tile (the last valid tile again once the range is exhausted), so the loads in flight
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     // puts its row there (16-byte chunks XOR-swizzled by row), then every store instruction writes whole
     // runs of rows instead of touching 32 rows.
     const float l_tot = pair_sum(l_run);
-    const float inv = VSCALE / l_tot;
+    const float inv = l_tot > 0.f ? VSCALE / l_tot : 0.f;   // no visible key and no sink: zero output
     if (qvalid && A.lse && hh == 0) A.lse[(size_t)qh * a.T + qt] = (m_run + __log2f(l_tot)) * LN2;
     __builtin_amdgcn_s_barrier();           // every wave is done reading the ring
     {

@@ -22,6 +22,18 @@ struct KVPrep {
     int T_pad;                     // tokens rounded up to 16, plus 64 zero-filled
 };
 inline int prep_tpad(int T) { return (T + 15) / 16 * 16 + 64; }
+// The direct-to-LDS copies address a tile with a 64-bit wave-uniform base plus a 32-bit per-lane byte offset.
+// Transposed copies (dim-major, T_pad tokens per row) put the dim index into that offset: 128 rows of V^T in
+// the forward, 192 rows of k'^T in the backward.  Key streams whose offsets would pass 2^32 are refused on
+// the host.
+inline bool fwd_stream_fits(long long rows)
+{
+    return rows >= 0 && rows <= 0x7fffff00LL && (long long)prep_tpad((int)rows) * 128 * 2 <= 0xffffffffLL;
+}
+inline bool bwd_stream_fits(long long rows)
+{
+    return rows >= 0 && rows <= 0x7fffff00LL && (long long)prep_tpad((int)rows) * 192 * 2 <= 0xffffffffLL;
+}
 size_t prep_bytes(int T, int hkv);
 void prep_carve(void *ws, int T, int hkv, KVPrep *p);
 

@@ -215,3 +215,82 @@ def test_binding_refuses_cpu_tensors():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ga.MimoAttnError):
         ga.fwd(q, k, v, None, cu, 4, 128, 1e4)
+
+
+def test_key_stream_offset_limits(L):
+    """Key streams whose transposed copies would need 32-bit copy offsets past 2^32 are refused: the forward
+    and cached prefill up to T_pad * 256 bytes per V^T row block, the backward up to T_pad * 384."""
+    fwd_max, bwd_max = 16_777_136, 11_184_736          # largest token counts whose padded stream fits
+    assert L.mimo_attn_fwd_workspace_size(fwd_max, 1, 1, -1) > 0
+    assert L.mimo_attn_fwd_workspace_size(fwd_max + 1, 1, 1, -1) == 0
+    assert L.mimo_attn_prefill_cached_workspace_size(fwd_max - 1000, 1000, 1) > 0
+    assert L.mimo_attn_prefill_cached_workspace_size(fwd_max - 1000, 1001, 1) == 0
+    assert L.mimo_attn_bwd_workspace_size(bwd_max, 1, 1, -1) > 0
+    assert L.mimo_attn_bwd_workspace_size(bwd_max + 1, 1, 1, -1) == 0
+    assert L.mimo_attn_bwd_workspace_size_fast(bwd_max + 1, 1, bwd_max + 1, 4, 1, -1) == 0
+    assert fwd(L, T=fwd_max + 1, max_seqlen=fwd_max + 1, hq=1, hkv=1) == 2
+    assert b"32-bit" in L.mimo_attn_last_error()
+    assert L.mimo_attn_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1, bwd_max + 1, bwd_max + 1, -1,
+                           1e4, 1, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 62, None) == 2
+    assert L.mimo_attn_prefill_cached(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 16, fwd_max, 16,
+                                      fwd_max + 16, -1, 1e4, 1, 1, FAKE, None, FAKE, 1 << 62, None) == 2
+    assert fwd(L, hq=8192, hkv=8) == 2                  # head counts beyond the copy offsets' range
+
+
+def _fwd_tile_starts(t0, t_last, kofs, kseq, window, T_pad, BN):
+    """Every key-tile start the forward kernel issues for one work item, restated from its integer formulas:
+    the first tile at kstart, then in each step the tile one (two-stage ring) or two (three-stage ring)
+    ahead, clamped to the last tile klast."""
+    klo = max(kseq, t0 + kofs - window) if window >= 0 else kseq
+    kstart = min(max(klo, 0) & ~15, T_pad - BN)
+    khi = min(t_last + kofs, T_pad - BN - 1)
+    num = khi - kstart + BN
+    nkt = max(int(num / BN), 0)                          # C division truncates toward zero
+    klast = kstart + max(nkt - 1, 0) * BN
+    starts = [kstart]
+    if window < 0:                                       # causal: three-stage ring
+        starts.append(min(kstart + BN, klast))
+        for it in range(nkt):
+            starts.append(min(kstart + (it + 2) * BN, klast))
+    else:                                                # sliding window: two-stage ring
+        for it in range(0, nkt, 2):
+            k0 = kstart + it * BN
+            starts += [min(k0 + BN, klast), min(k0 + 2 * BN, klast)]
+    computed = [kstart + it * BN for it in range(nkt)]
+    return starts, computed, khi
+
+
+@pytest.mark.parametrize("window,BN,TT", [(-1, 64, 32), (128, 32, 16), (3, 32, 16)])
+def test_fwd_key_tiles_stay_inside_the_prepared_stream(window, BN, TT):
+    """Cached prefill with cache index arrays that agree with the sizes, claim more rows than given (the key
+    offsets run past the stream) or fewer: every tile the forward issues lies inside the T_pad rows of the
+    prepared stream, and with agreeing arrays every key a query sees is computed."""
+    import numpy as np
+
+    rng = np.random.default_rng(11)
+    for trial in range(400):
+        batch = int(rng.integers(1, 6))
+        lens = rng.integers(0, 300, batch)
+        ncache = rng.integers(0, 400, batch)
+        T, Tc = int(lens.sum()), int(ncache.sum())
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        cuc = np.concatenate([[0], np.cumsum(ncache)])
+        mode = trial % 3
+        if mode == 1:                                    # over-stated: more cache rows than Tc
+            cuc = cuc + rng.integers(0, 5000) * np.arange(batch + 1)
+        elif mode == 2:                                  # under-stated
+            cuc = cuc // 2
+        T_pad = (T + Tc + 15) // 16 * 16 + 64
+        for b in range(batch):
+            s, e = int(cu[b]), int(cu[b + 1])
+            kofs, kseq = int(cuc[b + 1]), int(cuc[b]) + s
+            for t0 in range(s, e, TT):
+                t_last = min(t0 + TT - 1, e - 1)
+                starts, computed, khi = _fwd_tile_starts(t0, t_last, kofs, kseq, window, T_pad, BN)
+                for k in starts:
+                    assert 0 <= k and k + BN <= T_pad, (trial, mode, k, T_pad)
+                if mode == 0:
+                    need_lo = max(kseq, t0 + kofs - window) if window >= 0 else kseq
+                    need_hi = t_last + kofs
+                    assert computed and computed[0] <= need_lo and computed[-1] + BN - 1 >= need_hi
+

@@ -251,3 +251,65 @@ def test_verify_one_token_is_decode():
     o_ver = ga.verify_paged(q.to(dev), kp, vp, table.to(dev), cup.to(dev), pos.to(dev), None, 1, max(lens) + 1, -1, 1e7)
     torch.cuda.synchronize()
     compare("verify vs decode", o_ver.cpu(), o_dec.cpu().double(), max_abs=1e-2, mean_abs=1e-3)
+
+
+def _guarded(x, fill, rows=64):
+    """x on the GPU inside one larger allocation with `rows` guard rows of `fill` before and after it:
+    (the whole buffer, the view holding x)."""
+    buf = torch.full((rows + x.shape[0] + rows, *x.shape[1:]), fill, dtype=x.dtype, device="cuda")
+    buf[rows:rows + x.shape[0]] = x.to("cuda")
+    return buf, buf[rows:rows + x.shape[0]]
+
+
+@pytest.mark.parametrize("hkv,window,sink,base", [(4, -1, False, 1e7), (8, 128, True, 1e4)])
+def test_prefill_paged_index_arrays_disagree_with_sizes(hkv, window, sink, base):
+    """Regression test of the guards for index arrays that do not match the sizes given.  Inputs, pools and
+    the table sit inside larger allocations whose guard rows hold NaN (a read past any of them would make the
+    outputs non-finite) and the output inside one whose guard rows hold a sentinel (a write past it would
+    change them).  (a) A table with more entries than cu_pages covers: the extra entries belong to no sequence,
+    so the output equals, bit for bit, the call with the exact table, and the oracle.  (b) cu_pages claiming
+    2000 more cache rows for the second sequence than the table holds (the later sequences' keys then start
+    past the prepared stream): keys the arrays do not account for are zero-filled and the key range is clamped
+    to the stream, so the rows of that call are finite (not checked against the oracle: they are not
+    defined), the guard rows of the output are untouched, and the first sequence, whose entries are exact,
+    keeps the exact call's rows bit for bit."""
+    ga = _gpu()
+    prefixes, chunks = [300, 5, 64, 0], [40, 7, 129, 33]
+    d = mi.make_cached(chunks, prefixes, 64, hkv, 46, sink, 128 if window >= 0 else None)
+    kp, vp, table = _scatter(d["k_cache"], d["v_cache"], 300, 47)
+    g = torch.Generator().manual_seed(48)
+    extra = torch.randint(0, kp.shape[0], (50,), generator=g).to(torch.int32)
+    nan = float("nan")
+    _, q = _guarded(d["q"], nan)
+    _, k = _guarded(d["k"], nan)
+    _, v = _guarded(d["v"], nan)
+    _, kpg = _guarded(kp, nan)
+    _, vpg = _guarded(vp, nan)
+    T = d["q"].shape[0]
+    dev = "cuda"
+    t = lambda x: None if x is None else x.to(dev)  # noqa: E731
+    print(f"case index arrays vs sizes hkv={hkv} window={window}", flush=True)
+
+    def run(tab, cu_pages):
+        obuf, out = _guarded(torch.zeros(T, 64, 128, dtype=torch.bfloat16), 7.0)
+        o, lse = ga.prefill_paged(q, k, v, kpg, vpg, tab, t(d["sink"]), t(d["cu_seqlens"]), cu_pages,
+                                  t(d["positions"]), max(chunks), d["max_position"] + 4000, window, base, out=out)
+        torch.cuda.synchronize()
+        g_ = obuf.cpu().float()
+        assert (g_[:64] == 7.0).all() and (g_[64 + T:] == 7.0).all(), "output guard rows changed"
+        return o.cpu(), lse.cpu()
+
+    o_exact, l_exact = run(t(table), t(d["cu_cache"]))
+    _, tab_long = _guarded(torch.cat([table, extra]).reshape(-1, 1), 0)
+    o_long, l_long = run(tab_long.reshape(-1), t(d["cu_cache"]))
+    assert torch.equal(o_long.view(torch.int16), o_exact.view(torch.int16)) and torch.equal(l_long, l_exact)
+    ro, rl = oracle.prefill_cached_rows(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["cu_seqlens"],
+                                        d["cu_cache"], d["positions"], d["sink"], window, base)
+    compare("out (longer table)", o_long, ro.reshape(T, 64, -1))
+
+    over = d["cu_cache"].clone()
+    over[2:] += 2000
+    o_over, l_over = run(t(table), t(over))
+    assert torch.isfinite(o_over.float()).all() and not torch.isnan(l_over).any()
+    n0 = chunks[0]
+    assert torch.equal(o_over[:n0].view(torch.int16), o_exact[:n0].view(torch.int16))
