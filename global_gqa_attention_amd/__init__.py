@@ -52,6 +52,7 @@ def lib():
         L.mimo_attn_decode_paged.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P, sz, P]
         L.mimo_attn_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32,
                                               i32, P, P, P, sz, P]
+        L.mimo_attn_decode_paged_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, f64, i32, i32, P, P]
         L.mimo_attn_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         L.mimo_attn_verify_workspace_size.restype = sz
         L.mimo_attn_verify_paged.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, P, sz, P]
@@ -72,7 +73,7 @@ def lib():
         L.mimo_attn_trace_clear.restype = None
         for f in ("mimo_attn_fwd", "mimo_attn_bwd", "mimo_attn_decode", "mimo_attn_prefill_cached",
                   "mimo_attn_cache_append", "mimo_attn_decode_paged", "mimo_attn_prefill_paged",
-                  "mimo_attn_verify_paged"):
+                  "mimo_attn_verify_paged", "mimo_attn_decode_paged_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.mimo_attn_bwd_workspace_size.restype = sz
         L.mimo_attn_decode_workspace_size.restype = sz
@@ -311,6 +312,31 @@ def decode_paged(q, k_new, v_new, k_pool, v_pool, page_table, cu_pages, position
                                       float(rope_base), hq, hkv, _ptr(out), _ptr(workspace), workspace.numel(),
                                       _stream(q.device))
     _check(rc, "mimo_attn_decode_paged")
+    return out
+
+
+def decode_paged_noalloc(q, k_new, v_new, k_pool, v_pool, page_table, cu_pages, positions, sink, max_cache_len,
+                         window, rope_base, out):
+    """decode_paged with no workspace (the library's per-device scratch array holds the split partials): for
+    callers that cannot allocate.  `out` (bf16 [batch, hq, 128]) must be given; nothing is allocated here."""
+    _need(q, "q", torch.bfloat16)
+    B, hq = q.shape[0], q.shape[1]
+    hkv = k_new.shape[1]
+    _need(q, "q", torch.bfloat16, (B, hq, DQK))
+    _need(k_new, "k_new", torch.bfloat16, (B, hkv, DQK))
+    _need(v_new, "v_new", torch.bfloat16, (B, hkv, DV))
+    _pool_checks(k_pool, v_pool, hkv)
+    _need(page_table, "page_table", torch.int32)
+    _need(cu_pages, "cu_pages", torch.int32, (B + 1,))
+    _need(positions, "positions", torch.int32, (B,))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (hq,))
+    _need(out, "out", torch.bfloat16, (B, hq, DV))
+    rc = lib().mimo_attn_decode_paged_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                              _ptr(page_table), _ptr(cu_pages), _ptr(positions), _ptr(sink), B,
+                                              int(max_cache_len), int(window), float(rope_base), hq, hkv, _ptr(out),
+                                              _stream(q.device))
+    _check(rc, "mimo_attn_decode_paged_noalloc")
     return out
 
 

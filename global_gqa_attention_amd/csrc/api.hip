@@ -88,6 +88,7 @@ struct TraceRec {
     hipEvent_t start, stop;
 };
 bool g_trace_on = false;
+thread_local bool g_trace_off_here = false;   // set while an entry point that must not allocate runs
 std::vector<TraceRec> g_trace;
 std::vector<hipEvent_t> g_event_pool;
 const char *g_trace_pending = nullptr;
@@ -133,7 +134,7 @@ mimo_status_t check_layer(const void *q, const void *k, const void *v, const int
 namespace mimo {
 void trace_begin(const char *name, hipStream_t stream)
 {
-    if (!g_trace_on) return;
+    if (!g_trace_on || g_trace_off_here) return;
     g_trace_start = pool_event();
     g_trace_pending = name;
     if (g_trace_start) (void)hipEventRecord(g_trace_start, stream);
@@ -141,7 +142,7 @@ void trace_begin(const char *name, hipStream_t stream)
 
 void trace_end(hipStream_t stream)
 {
-    if (!g_trace_on || !g_trace_start) return;
+    if (!g_trace_on || g_trace_off_here || !g_trace_start) return;
     hipEvent_t stop = pool_event();
     if (!stop) return;
     (void)hipEventRecord(stop, stream);
@@ -472,14 +473,43 @@ size_t mimo_attn_decode_workspace_size(int32_t batch, int32_t max_cache_len, int
 
 }  // extern "C"
 
+// ---- scratch for callers that cannot allocate (mimo_attn_decode_paged_noalloc): the split-KV partials live
+// in this array, one copy per device for the life of the process.  Host code never passes the array's own
+// name to a kernel (on the host it stands for nothing on the device); each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_addr;
+
+mimo_status_t scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_addr.find(dev);
+    if (it == g_scratch_addr.end()) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MIMO_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+        it = g_scratch_addr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return MIMO_OK;
+}
+
 // Decode (nq = 1, k_new/v_new given) or verify (nq draft tokens whose keys are the last nq cache rows,
 // k_new == v_new == nullptr) over a contiguous or paged cache.
 mimo_status_t decode_over_cache(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                                 const void *v_cache, const int32_t *page_table, const int32_t *cu_cache,
                                 const int32_t *positions, const float *sink, int32_t batch, int32_t nq,
                                 int32_t max_cache_len, int32_t window, double rope_base, int32_t n_q_heads,
-                                int32_t n_kv_heads, void *out, void *workspace, size_t workspace_bytes, void *stream)
+                                int32_t n_kv_heads, void *out, void *workspace, size_t workspace_bytes, void *stream,
+                                bool use_scratch = false)
 {
     const bool verify = k_new == nullptr;
     if (nq < 1 || (!verify && nq != 1)) return fail(MIMO_ERR_INVALID_ARG, "query tokens per sequence must be >= 1");
@@ -500,9 +530,23 @@ mimo_status_t decode_over_cache(const void *q, const void *k_new, const void *v_
     if (!mimo::decode_group_supported(n_q_heads / n_kv_heads))
         return fail(MIMO_ERR_UNSUPPORTED, "no decode kernel for group size %d", n_q_heads / n_kv_heads);
     const int wplan = verify && window >= 0 ? window + nq : window;   // rows a query can see
-    const size_t need = mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, wplan, nq);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    int splits = 0, split_len = 0;
+    if (use_scratch) {
+        // the scratch array instead of a workspace: fewer, longer splits when the usual plan's partials do
+        // not fit in it
+        if (!mimo::decode_split_plan_capped(batch, max_cache_len, n_q_heads, wplan, nq, kScratchBytes, &splits,
+                                            &split_len))
+            return fail(MIMO_ERR_UNSUPPORTED, "batch %d x %d query heads: the split partials need more than the "
+                        "%zu-byte scratch array", batch, n_q_heads, kScratchBytes);
+        mimo_status_t st = scratch_address(&workspace);
+        if (st != MIMO_OK) return st;
+        workspace_bytes = kScratchBytes;
+    } else {
+        const size_t need = mimo::decode_workspace_bytes(batch, max_cache_len, n_q_heads, wplan, nq);
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return fail(MIMO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+        mimo::decode_split_plan(batch, max_cache_len, n_q_heads, n_kv_heads, wplan, &splits, &split_len);
+    }
     mimo::DecodeArgs a{};
     a.q = (const uint16_t *)q;
     a.k_new = (const uint16_t *)k_new;
@@ -521,7 +565,8 @@ mimo_status_t decode_over_cache(const void *q, const void *k_new, const void *v_
     a.hkv = n_kv_heads;
     a.rope_base = rope_base;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kDQK));
-    mimo::decode_split_plan(batch, max_cache_len, n_q_heads, n_kv_heads, wplan, &a.splits, &a.split_len);
+    a.splits = splits;
+    a.split_len = split_len;
     char *ws = (char *)workspace;
     a.part_o = (float *)ws;
     size_t off = ((size_t)batch * nq * n_q_heads * a.splits * kDV * sizeof(float) + 255) & ~(size_t)255;
@@ -558,6 +603,22 @@ mimo_status_t mimo_attn_decode_paged(const void *q, const void *k_new, const voi
     return decode_over_cache(q, k_new, v_new, k_pool, v_pool, max_cache_len > 0 ? page_table : nullptr, cu_pages,
                              positions, sink, batch, 1, max_cache_len, window, rope_base, n_q_heads, n_kv_heads, out,
                              workspace, workspace_bytes, stream);
+}
+
+mimo_status_t mimo_attn_decode_paged_noalloc(const void *q, const void *k_new, const void *v_new, const void *k_pool,
+                                             const void *v_pool, const int32_t *page_table, const int32_t *cu_pages,
+                                             const int32_t *positions, const float *sink, int32_t batch,
+                                             int32_t max_cache_len, int32_t window, double rope_base,
+                                             int32_t n_q_heads, int32_t n_kv_heads, void *out, void *stream)
+{
+    if (batch > 0 && max_cache_len > 0 && !page_table) return fail(MIMO_ERR_INVALID_ARG, "page_table is null");
+    if (batch > 0 && !k_new) return fail(MIMO_ERR_INVALID_ARG, "k_new is null");
+    g_trace_off_here = true;   // tracing would create HIP events
+    const mimo_status_t s = decode_over_cache(q, k_new, v_new, k_pool, v_pool, max_cache_len > 0 ? page_table : nullptr,
+                                              cu_pages, positions, sink, batch, 1, max_cache_len, window, rope_base,
+                                              n_q_heads, n_kv_heads, out, nullptr, 0, stream, true);
+    g_trace_off_here = false;
+    return s;
 }
 
 size_t mimo_attn_verify_workspace_size(int32_t batch, int32_t n_query, int32_t max_cache_len, int32_t n_q_heads,

@@ -633,13 +633,37 @@ void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window
     *split_len = len;
 }
 
+static size_t partials_bytes(int batch, int nq, int hq, int splits)
+{
+    const size_t po = ((size_t)batch * nq * hq * splits * DVV * sizeof(float) + 255) & ~(size_t)255;
+    const size_t ml = (size_t)batch * nq * hq * splits * 2 * sizeof(float);
+    return po + ml;
+}
+
 size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window, int nq)
 {
     int splits, len;
     decode_split_plan(batch, max_cache_len, hq, 1, window, &splits, &len);
-    const size_t po = ((size_t)batch * nq * hq * splits * DVV * sizeof(float) + 255) & ~(size_t)255;
-    const size_t ml = (size_t)batch * nq * hq * splits * 2 * sizeof(float);
-    return po + ml;
+    return partials_bytes(batch, nq, hq, splits);
+}
+
+bool decode_split_plan_capped(int batch, int max_cache_len, int hq, int window, int nq, size_t cap, int *splits,
+                              int *split_len)
+{
+    decode_split_plan(batch, max_cache_len, hq, 1, window, splits, split_len);
+    if (partials_bytes(batch, nq, hq, *splits) <= cap) return true;
+    if (partials_bytes(batch, nq, hq, 1) > cap) return false;
+    // the most splits that fit, then chunk-aligned lengths that cover the visible rows with at most that many
+    const size_t per = (size_t)batch * nq * hq * (DVV + 2) * sizeof(float);
+    const int smax = (int)((cap - 255) / per);
+    int n = max_cache_len;
+    if (window >= 0 && window < n) n = window;
+    int len = (n + smax - 1) / smax;
+    len = (len + CH - 1) / CH * CH;
+    if (len < *split_len) len = *split_len;
+    *split_len = len;
+    *splits = n > 0 ? (n + len - 1) / len : 1;
+    return partials_bytes(batch, nq, hq, *splits) <= cap;
 }
 
 hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)

@@ -130,5 +130,9 @@ size_t bwd_workspace_bytes(int T, int hq, int hkv, int window);
 size_t bwd_workspace_bytes_ds(int T, int hq, int hkv, int window, int batch, int max_seqlen);   // 0: not available
 size_t decode_workspace_bytes(int batch, int max_cache_len, int hq, int window, int nq = 1);
 void decode_split_plan(int batch, int max_cache_len, int hq, int hkv, int window, int *splits, int *split_len);
+// The same plan with at most as many splits as let the partials fit in cap bytes (laid out as
+// decode_workspace_bytes lays them out); false when even one split does not fit.
+bool decode_split_plan_capped(int batch, int max_cache_len, int hq, int window, int nq, size_t cap, int *splits,
+                              int *split_len);
 
 }  // namespace mimo

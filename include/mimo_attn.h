@@ -208,6 +208,24 @@ mimo_status_t mimo_attn_decode_paged(const void *q, const void *k_new, const voi
                                      int32_t n_kv_heads, void *out, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/* mimo_attn_decode_paged for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments and result as mimo_attn_decode_paged
+ * minus the workspace: the split-KV partials live in a 64 MiB array that the library keeps on each device
+ * it runs on until the process ends (its address is looked up once per device, on the first call there).
+ * The call allocates nothing, creates no HIP events (kernel tracing skips it) and only launches kernels.
+ *   - When the usual split plan's partials (batch * n_q_heads * splits * 520 bytes) exceed 64 MiB, the call
+ *     uses fewer, longer splits, so its fp32 summation order (not its result beyond rounding) can differ
+ *     from mimo_attn_decode_paged's; batch * n_q_heads above 129055 (one split no longer fits) returns
+ *     MIMO_ERR_UNSUPPORTED.
+ *   - Every call on a device shares that device's array, and calls keep nothing in it that a later call
+ *     needs: calls that overlap in time on one device (other streams, other threads) race and give wrong
+ *     results; calls in one stream order are safe. */
+mimo_status_t mimo_attn_decode_paged_noalloc(const void *q, const void *k_new, const void *v_new, const void *k_pool,
+                                             const void *v_pool, const int32_t *page_table, const int32_t *cu_pages,
+                                             const int32_t *positions, const float *sink, int32_t batch,
+                                             int32_t max_cache_len, int32_t window, double rope_base,
+                                             int32_t n_q_heads, int32_t n_kv_heads, void *out, void *stream);
+
 /* Bytes of device workspace mimo_attn_verify_paged needs (0 for invalid sizes). */
 size_t mimo_attn_verify_workspace_size(int32_t batch, int32_t n_query, int32_t max_cache_len, int32_t n_q_heads,
                                        int32_t window);

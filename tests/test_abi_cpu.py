@@ -294,3 +294,14 @@ def test_fwd_key_tiles_stay_inside_the_prepared_stream(window, BN, TT):
                     need_hi = t_last + kofs
                     assert computed and computed[0] <= need_lo and computed[-1] + BN - 1 >= need_hi
 
+
+def test_decode_paged_noalloc_rejects_partials_beyond_its_scratch(L):
+    """One split's partials of batch x n_q_heads rows (520 bytes each) must fit the 64 MiB scratch array:
+    129055 rows do, 4096 x 64 do not (rejected on the host, nothing launched)."""
+    rc = L.mimo_attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4096, 128, -1, 1e7,
+                                          64, 4, FAKE, None)
+    assert rc == 2 and b"scratch" in L.mimo_attn_last_error()
+    assert L.mimo_attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 4, 128, -1, 1e7,
+                                            64, 4, FAKE, None) == 1          # no page table
+    assert L.mimo_attn_decode_paged_noalloc(None, None, None, None, None, None, None, None, None, 0, 0, -1, 1e7,
+                                            64, 4, None, None) == 0          # empty batch: nothing to do
