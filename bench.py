@@ -89,14 +89,41 @@ def measured_traffic(kernel):
     return None if rec is None else rec.get("bytes_per_launch")
 
 
+def cpu_info():
+    """Host CPUs as the OS reports them and the CPU model name (from /proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cpus": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline(thd, dout, nthreads):
-    """The fp64 oracle on a bounded sample of the same workload (about 25 s on 16 host threads): the first two
-    sequences of the batch for both layers, forward and backward, all 64 heads."""
+    """The fp64 oracle, as it stands, on bounded samples of the workloads (about 20-30 s on 16 host threads),
+    each reported in GFLOP/s with the same algorithmic FLOP count as the GPU lines.  `value` is the sample of
+    the benchmarked step (the first two sequences of the 32K batch, both layers, forward and backward, all 64
+    heads); the other configurations are timed beside it:
+      swa_512     one 512-token sliding-window layer, forward and backward, every row
+      global_2x4096  the 2 x 4096 global forward on the last 256 tokens of each sequence (its costliest rows)
+      decode_swa  the batch-64 ring-cache decode step, every (sequence, head) row
+      decode_global  the global decode step on 2 sequences drawn by the same recipe (seed 3, batch 2)."""
+    import numpy as np
     import torch
 
     import mimo_inputs as mi
     import oracle
 
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    configs = {}
     flops, secs, parts = 0.0, 0.0, []
     for name, d, n_tok, lens in (
         ("swa", thd["swa"], sum(thd["swa"]["lengths"][:2]), thd["swa"]["lengths"][:2]),
@@ -105,18 +132,56 @@ def cpu_baseline(thd, dout, nthreads):
         q, k, v = d["q"][:n_tok], d["k"][:n_tok], d["v"][:n_tok]
         cu = mi.cu_from_lengths(lens)
         dO = dout[:n_tok]
-        t0 = time.perf_counter()
-        o, _ = oracle.prefill(q, k, v, d["sink"], cu, d["window"], d["rope_base"], nthreads=nthreads)
-        og = torch.from_numpy(o).to(torch.bfloat16)
-        oracle.prefill_bwd(q, k, v, d["sink"], dO, cu, d["window"], d["rope_base"], out_given=og,
-                           nthreads=nthreads)
-        dt = time.perf_counter() - t0
-        p = pairs_per_head(lens, d["window"]) * q.shape[1]
-        flops += p * (FWD_FLOP_PER_PAIR + BWD_FLOP_PER_PAIR)
+
+        def fb():
+            o, _ = oracle.prefill(q, k, v, d["sink"], cu, d["window"], d["rope_base"], nthreads=nthreads)
+            og = torch.from_numpy(o).to(torch.bfloat16)
+            oracle.prefill_bwd(q, k, v, d["sink"], dO, cu, d["window"], d["rope_base"], out_given=og,
+                               nthreads=nthreads)
+        dt = timed(fb)
+        f = pairs_per_head(lens, d["window"]) * q.shape[1] * (FWD_FLOP_PER_PAIR + BWD_FLOP_PER_PAIR)
+        flops += f
         secs += dt
         parts.append(f"{name}: {n_tok} tokens x 64 heads fwd+bwd in {dt:.1f}s")
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
-            "sample": "; ".join(parts) + " (fp64 C oracle, algorithmic FLOPs as the GPU line)"}
+        configs[f"thd_32k_{name}_fwd_bwd_2seq"] = {"s": round(dt, 2), "GFLOP/s": round(f / dt / 1e9, 2)}
+
+    d = mi.swa_512()
+    dO = mi.dout_like(512, 4)
+    holder = {}
+    dt_f = timed(lambda: holder.setdefault("o", oracle.prefill(d["q"], d["k"], d["v"], d["sink"], d["cu_seqlens"],
+                                                                128, 1e4, nthreads=nthreads)))
+    og = torch.from_numpy(holder["o"][0]).to(torch.bfloat16)
+    dt_b = timed(lambda: oracle.prefill_bwd(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], 128, 1e4,
+                                            out_given=og, nthreads=nthreads))
+    p = pairs_per_head([512], 128) * 64
+    configs["swa_512"] = {"fwd_s": round(dt_f, 3), "fwd_GFLOP/s": round(p * FWD_FLOP_PER_PAIR / dt_f / 1e9, 2),
+                          "bwd_s": round(dt_b, 3), "bwd_GFLOP/s": round(p * BWD_FLOP_PER_PAIR / dt_b / 1e9, 2)}
+
+    d = mi.global_2x4096()
+    rows = np.concatenate([np.arange(t * 64, (t + 1) * 64) for s0 in (0, 4096) for t in range(s0 + 3840, s0 + 4096)])
+    dt = timed(lambda: oracle.prefill_rows(d["q"], d["k"], d["v"], None, d["cu_seqlens"], -1, 1e7, rows=rows,
+                                           nthreads=nthreads))
+    p = 2 * sum(i + 1 for i in range(3840, 4096)) * 64
+    configs["global_2x4096_fwd_last256"] = {"s": round(dt, 2), "GFLOP/s": round(p * FWD_FLOP_PER_PAIR / dt / 1e9, 2)}
+
+    d = mi.decode_swa()
+    dt = timed(lambda: oracle.decode_rows(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["cu_cache"],
+                                          d["positions"], d["sink"], d["window"], d["rope_base"], nthreads=nthreads))
+    p = 64 * 64 * 129
+    configs["decode_swa"] = {"s": round(dt, 3), "GFLOP/s": round(p * FWD_FLOP_PER_PAIR / dt / 1e9, 2)}
+    d = mi.decode_global(batch=2)
+    cuc = d["cu_cache"]
+    rows_c = int(cuc[-1])
+    dt = timed(lambda: oracle.decode_rows(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], cuc,
+                                          d["positions"], None, -1, 1e7, nthreads=nthreads))
+    p = (rows_c + 2) * 64
+    configs["decode_global_2seq"] = {"s": round(dt, 3), "cache_rows": rows_c,
+                                     "GFLOP/s": round(p * FWD_FLOP_PER_PAIR / dt / 1e9, 2),
+                                     "GB/s": round(rows_c * 4 * 640 / dt / 1e9, 2)}
+    out = {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+           "sample": "; ".join(parts) + " (fp64 C oracle, algorithmic FLOPs as the GPU line)", "configs": configs}
+    out.update(cpu_info())
+    return out
 
 
 def run_decode(ga, torch, mi, reps=20):
@@ -147,10 +212,10 @@ def run_decode(ga, torch, mi, reps=20):
         rows = sum(min(n, d["window"]) if d["window"] >= 0 else n for n in lens)
         cache_bytes = rows * hkv * (192 + 128) * 2
         io_bytes = 64 * 64 * (192 + 128) * 2 + 64 * hkv * (192 + 128) * 2
-        keys = rows * (64 // hkv) + 64 * 64
+        pairs = rows * 64 + 64 * 64      # every cached row is seen by all 64 query heads; plus the new token
         res[name] = {"ms": round(ms, 4), "GB/s": round((cache_bytes + io_bytes) / ms / 1e6, 1),
                      "hbm_frac": round((cache_bytes + io_bytes) / ms / 1e6 / HBM_PEAK_GBS, 4),
-                     "TFLOP/s": round(keys * FWD_FLOP_PER_PAIR / ms / 1e9, 2), "cache_rows": rows}
+                     "TFLOP/s": round(pairs * FWD_FLOP_PER_PAIR / ms / 1e9, 2), "cache_rows": rows}
         del d, flush
         torch.cuda.empty_cache()
     return res
