@@ -244,6 +244,8 @@ def setup_layers(ga, torch, mi, dev):
         g["pairs"] = pairs_per_head(d["lengths"], d["window"]) * hq
         layers[name] = g
     dout = dout_cpu.to(dev)
+    for g in layers.values():
+        g["dout"] = dout
 
     def step():
         for g in layers.values():
@@ -356,20 +358,82 @@ def traffic_summary(fetch_dir, write_dir):
     print(f"wrote {path}")
 
 
-def stats_summary(csv_path, title, command):
-    """Prints a rocprofv3 kernel_stats.csv as a short text table (kernel, calls, average/min/max us, share)."""
-    import csv
+def _short_kernel(n):
     import re
 
-    def short(n):
-        m = re.search(r"mimo::\(anonymous namespace\)::(\w+)(<[^>(]*>)?", n)
-        return m.group(1) + (m.group(2) or "") if m else n.split("(")[0][-70:]
+    m = re.search(r"mimo::\(anonymous namespace\)::(\w+)(<[^>(]*>)?", n)
+    return m.group(1) + (m.group(2) or "") if m else n.split("(")[0][-70:]
 
-    print(f"# {title}\n# command: {command}\n# source: rocprofv3 --kernel-trace --stats (kernel_stats.csv)\n")
-    print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
-    for r in csv.DictReader(open(csv_path)):
-        print(f"{short(r['Name'])[:64]:64s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.1f} "
-              f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
+
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise SystemExit(f"no *{suffix} under {d}")
+
+
+def stats_summary(trace_dir, title, command, timed):
+    """Prints a rocprofv3 kernel trace (kernel_trace.csv under trace_dir) as a short text table: per kernel the
+    launches, the average over all of them, the average over the last `timed` launches (the timed steps of a
+    bench run; warm-up launches come first), and min / max, in microseconds."""
+    import csv
+
+    per = {}
+    for r in csv.DictReader(open(_find_csv(trace_dir, "kernel_trace.csv"))):
+        per.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) -
+                                                     int(r["Start_Timestamp"])))
+    timed = int(timed)
+    total = sum(d for v in per.values() for _, d in v)
+    print(f"# {title}\n# command: {command}\n# source: rocprofv3 --kernel-trace (kernel_trace.csv); avg_timed_us = "
+          f"average of each kernel's last {timed} launches (the timed steps)\n")
+    print(f"{'kernel':56s} {'calls':>6s} {'avg_us':>9s} {'avg_timed_us':>12s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        v.sort()
+        ds = [d for _, d in v]
+        last = ds[-timed:] if len(ds) >= timed else ds
+        print(f"{_short_kernel(name)[:56]:56s} {len(ds):6d} {sum(ds) / len(ds) / 1e3:9.1f} "
+              f"{sum(last) / len(last) / 1e3:12.1f} {min(ds) / 1e3:9.1f} {max(ds) / 1e3:9.1f} "
+              f"{100.0 * sum(ds) / total:6.2f}")
+
+
+def mfma_summary(pmc_dir, title, command):
+    """Per library kernel of the traced step of --traffic-probe (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace): bf16 MFMA flops executed (MOPS x 512), MFMA-busy
+    share of the SIMD cycles (busy / (GRBM_GUI_ACTIVE x 1024 SIMDs)), the clock implied by GRBM_GUI_ACTIVE over
+    the kernel's traced duration, and the executed MFMA rate.  Prints a text table."""
+    import csv
+
+    order = json.load(open(os.path.join(pmc_dir, "traffic_order.json")))["launches"]
+    vals = {}
+    for r in csv.DictReader(open(_find_csv(pmc_dir, "counter_collection.csv"))):
+        key = int(r["Dispatch_Id"])
+        rec = vals.setdefault(key, {"name": r["Kernel_Name"]})
+        c, v = r["Counter_Name"], float(r["Counter_Value"])
+        rec[c] = max(rec.get(c, 0.0), v) if c == "GRBM_GUI_ACTIVE" else rec.get(c, 0.0) + v
+    dur = {}
+    for r in csv.DictReader(open(_find_csv(pmc_dir, "kernel_trace.csv"))):
+        dur[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    lib = [k for k in sorted(vals) if "mimo::" in vals[k]["name"]]
+    if len(lib) < len(order):
+        raise SystemExit(f"{len(lib)} library dispatches with counters, expected at least {len(order)}")
+    print(f"# {title}\n# command: {command}\n# MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; busy = "
+          f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); clock = GRBM_GUI_ACTIVE / traced duration; "
+          f"durations are those of the counter run (kernels serialised)\n")
+    print(f"{'launch':24s} {'kernel':34s} {'us':>9s} {'MFMA_TFLOP':>11s} {'TFLOP/s':>9s} {'mfma_busy%':>10s} {'GHz':>6s}")
+    for name, k in zip(order, lib[-len(order):]):
+        rec = vals[k]
+        want = next(kn for pfx, kn in TRACE_TO_KERNEL if name.startswith(pfx))
+        if want not in rec["name"]:
+            raise SystemExit(f"launch {name} lines up with dispatch {rec['name']}")
+        us = dur.get(k, 0) / 1e3
+        flop = rec.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        gui = rec.get("GRBM_GUI_ACTIVE", 0.0)
+        busy = 100.0 * rec.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * 1024) if gui else 0.0
+        ghz = gui / (us * 1e3) if us else 0.0
+        rate = flop / (us * 1e-6) / 1e12 if us else 0.0
+        print(f"{name:24s} {_short_kernel(rec['name'])[:34]:34s} {us:9.1f} {flop / 1e12:11.4f} {rate:9.1f} "
+              f"{busy:10.1f} {ghz:6.2f}")
 
 
 def run_prefill(ga, torch, layers, reps=10):
@@ -405,6 +469,37 @@ def run_prefill(ga, torch, layers, reps=10):
                       "attn_fwd_TFLOP/s": round(flop / (attn * 1e-3) / 1e12, 1),
                       "attn_fwd_GB/s": round(hbm / (attn * 1e-3) / 1e9, 1),
                       "attn_fwd_hbm_frac": round(hbm / (attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
+
+
+def run_bwd_paths(ga, torch, layers, reps=10):
+    """Backward of each layer with the stored-dS workspace (the step's) and with the least workspace (the dQ
+    kernel recomputes S and dP): median of `reps` traced calls, sum of the backward's kernels."""
+    res = {}
+    for lname, g in layers.items():
+        T, hq, hkv = g["q"].shape[0], g["q"].shape[1], g["k"].shape[1]
+        least = torch.empty(ga.bwd_workspace_size(T, hq, hkv, g["window"]), dtype=torch.uint8, device=g["q"].device)
+        rec = {}
+        for path, ws in (("stored_dS", g["ws"]), ("least", least)):
+            call = lambda: ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], g["dout"], g["cu_seqlens"],  # noqa
+                                  g["max_seqlen"], g["window"], g["rope_base"], workspace=ws, grads=g["grads"],
+                                  q_rot=g["q_rot"])
+            for _ in range(2):
+                call()
+            torch.cuda.synchronize()
+            ga.trace_read(clear=True)
+            ga.trace_enable(True)
+            totals = []
+            for _ in range(reps):
+                call()
+                torch.cuda.synchronize()
+                totals.append(sum(ms for _, ms in ga.trace_read(clear=True)))
+            ga.trace_enable(False)
+            rec[f"{path}_ms"] = round(sorted(totals)[len(totals) // 2], 4)
+            rec[f"{path}_workspace_GB"] = round(ws.numel() / 1e9, 3)
+        res[lname] = rec
+        del least
+    torch.cuda.empty_cache()
     return res
 
 
@@ -616,11 +711,17 @@ def main():
     ap.add_argument("--traffic-probe", metavar="DIR", help="run the counter-pass workload (see the module doc)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two counter passes")
-    ap.add_argument("--stats-summary", nargs=3, metavar=("CSV", "TITLE", "COMMAND"),
-                    help="print a rocprofv3 kernel_stats.csv as a text table")
+    ap.add_argument("--stats-summary", nargs=4, metavar=("TRACE_DIR", "TITLE", "COMMAND", "TIMED"),
+                    help="print a rocprofv3 kernel trace as a text table (TIMED: launches per kernel in the timed "
+                         "steps)")
+    ap.add_argument("--mfma-summary", nargs=3, metavar=("PMC_DIR", "TITLE", "COMMAND"),
+                    help="print the MFMA counters of a --traffic-probe counter run per kernel of the step")
     args = ap.parse_args()
     if args.stats_summary:
         stats_summary(*args.stats_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(*args.mfma_summary)
         return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
@@ -712,6 +813,7 @@ def main():
     }
     if not args.step_only:
         line["prefill"] = run_prefill(ga, torch, layers)
+        line["bwd_paths"] = run_bwd_paths(ga, torch, layers)
         line["prefill_cached"] = run_prefill_cached(ga, torch, mi)
         line["tp4_shard_step"] = run_shards(ga, torch, thd, dout_cpu)
     if not args.no_decode and not args.step_only:

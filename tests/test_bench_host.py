@@ -103,3 +103,44 @@ def test_kernel_hash_ignores_comments_only(tmp_path):
     (d / "notes.txt").write_text("not a source")
     (d / "k.hip").write_text(src)
     assert bench.kernel_source_hash(str(d)) == h0
+
+
+def _write_trace(d, rows):
+    """kernel_trace.csv with (dispatch id, kernel name, start ns, duration ns) rows."""
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "p_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i, name, t0, dt in rows:
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Start_Timestamp": t0, "End_Timestamp": t0 + dt})
+
+
+def test_stats_summary_averages_the_timed_launches(tmp_path, capsys):
+    k = "void mimo::(anonymous namespace)::bwd_dkdv_kernel<false>(mimo::BwdArgs)"
+    # one cold warm-up launch of 9 us, then three timed launches of 6 us
+    _write_trace(str(tmp_path), [(1, k, 0, 9000), (2, k, 20000, 6000), (3, k, 40000, 6000), (4, k, 60000, 6000)])
+    bench.stats_summary(str(tmp_path), "t", "c", "3")
+    line = [l for l in capsys.readouterr().out.splitlines() if l.startswith("bwd_dkdv_kernel")][0].split()
+    assert line[1] == "4" and float(line[2]) == 6.8 and float(line[3]) == 6.0
+
+
+def test_mfma_summary_rates_and_clock(tmp_path, capsys):
+    d = str(tmp_path)
+    k = "void mimo::(anonymous namespace)::bwd_dkdv_kernel<false>(mimo::BwdArgs)"
+    with open(os.path.join(d, "traffic_order.json"), "w") as f:
+        json.dump({"launches": ["bwd_dkdv_global"]}, f)
+    with open(os.path.join(d, "p_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        # 2e12 flop executed (MOPS x 512) over two instances; 1700 cycles in a 1 us kernel; busy 50% of 1024 SIMDs
+        for part in (0.5, 0.5):
+            w.writerow({"Dispatch_Id": 7, "Kernel_Name": k, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                        "Counter_Value": part * 2e12 / 512})
+            w.writerow({"Dispatch_Id": 7, "Kernel_Name": k, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
+                        "Counter_Value": part * 0.5 * 1700 * 1024})
+            w.writerow({"Dispatch_Id": 7, "Kernel_Name": k, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 1700})
+    _write_trace(d, [(7, k, 0, 1000)])
+    bench.mfma_summary(d, "t", "c")
+    line = [l for l in capsys.readouterr().out.splitlines() if l.startswith("bwd_dkdv_global")][0].split()
+    assert float(line[3]) == 2.0 and float(line[4]) == 2e12 / 1e-6 / 1e12 and float(line[5]) == 50.0
+    assert float(line[6]) == 1.7

@@ -99,9 +99,11 @@ def test_bwd_deterministic_and_paths_agree(window, sink):
     assert float(diff.max()) <= 2e-2 and float(diff.mean()) <= 1e-4, (float(diff.max()), float(diff.mean()))
 
 
-def _sampled_bwd(ga, d, dO, nq, nk, heads, seed, path="fast"):
+def _sampled_bwd(ga, d, dO, nq, nk, heads, seed, path="fast", check_forward=False):
     """Full-size backward: the oracle computes the forward rows it needs, and then sampled dq rows, dk/dv rows
-    near the ends of sequences (few queries see them under causal attention), and dsink for a few heads."""
+    near the ends of sequences (few queries see them under causal attention), and dsink for a few heads.
+    check_forward: the oracle's forward is computed on every row anyway, so the GPU forward of the same
+    batch is compared with it on every row too."""
     rng = np.random.default_rng(seed)
     T, hq, hkv = d["q"].shape[0], d["q"].shape[1], d["k"].shape[1]
     starts = np.concatenate([[0], np.cumsum(d["lengths"])])
@@ -111,6 +113,15 @@ def _sampled_bwd(ga, d, dO, nq, nk, heads, seed, path="fast"):
     o, l = oracle.prefill_rows(d["q"], d["k"], d["v"], d["sink"], d["cu_seqlens"], d["window"], d["rope_base"])
     O[:] = torch.from_numpy(o.reshape(T, hq, 128)).to(torch.bfloat16)
     L[:] = torch.from_numpy(l.reshape(T, hq).T.copy()).to(torch.float32)
+    if check_forward:
+        dev = "cuda"
+        sink = None if d["sink"] is None else d["sink"].to(dev)
+        go, gl = ga.fwd(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), sink, d["cu_seqlens"].to(dev),
+                        max(d["lengths"]), d["window"], d["rope_base"])
+        torch.cuda.synchronize()
+        compare("fwd out (every row)", go.cpu().reshape(-1, 128), o)
+        compare("fwd lse (every row)", gl.cpu().T.reshape(-1), l)
+        del go, gl
     dq, dk, dv, ds = _run_bwd(ga, d, O, L, dO, path)
     qrows = rng.integers(0, T * hq, nq)
     rq = oracle.bwd_dq_rows(d["q"], d["k"], d["v"], d["sink"], dO, d["cu_seqlens"], d["window"], d["rope_base"],
@@ -134,12 +145,13 @@ def _sampled_bwd(ga, d, dO, nq, nk, heads, seed, path="fast"):
 
 
 def test_bwd_thd_32k_swa_sampled():
-    """SWA layer of the 32768-token THD batch with dO ~ N(0,1) seed 4: sampled rows, 4 full dsink heads."""
+    """SWA layer of the 32768-token THD batch with dO ~ N(0,1) seed 4: the forward on every row, the backward
+    on sampled rows, 4 full dsink heads."""
     ga = _gpu()
     d = mi.thd_32k()["swa"]
     dO = mi.dout_like(32768, 4)
-    print("case thd_32k swa bwd", flush=True)
-    _sampled_bwd(ga, d, dO, 400, 60, [0, 17, 40, 63], 3)
+    print("case thd_32k swa fwd (every row) + bwd", flush=True)
+    _sampled_bwd(ga, d, dO, 400, 60, [0, 17, 40, 63], 3, check_forward=True)
 
 
 @pytest.mark.parametrize("path", ["fast", "least"])

@@ -62,7 +62,7 @@ def test_decode_ragged_full(lens, hkv, window, sink):
 
 def test_decode_global_full_size_sampled():
     """Batch 64, cached lengths in [8192, 131072], 4 KV heads, base 1e7, seed 3 (cache drawn on the device):
-    sampled (sequence, head) rows against the oracle on the copied cache segments."""
+    all 64 heads of 8 sequences against the oracle on the copied cache segments."""
     ga = _gpu()
     d = mi.decode_global(device="cuda")
     cu = d["cu_cache"].cpu()
@@ -72,10 +72,11 @@ def test_decode_global_full_size_sampled():
     torch.cuda.synchronize()
     out = out.cpu()
     rng = np.random.default_rng(5)
-    bs = sorted(set([int(np.argmax(lens)), int(np.argmin(lens))] + rng.integers(0, 64, 2).tolist()))
-    for b in bs:
+    bs = [int(np.argmax(lens)), int(np.argmin(lens))]
+    bs = sorted(set(bs + [int(b) for b in rng.permutation(64) if int(b) not in bs][:6]))
+    heads = np.arange(64)
+    for b in bs:          # eight sequences (the longest and shortest among them), every query head
         s, e = int(cu[b]), int(cu[b + 1])
-        heads = rng.integers(0, 64, 6)
         kc = d["k_cache"][s:e].cpu()
         vc = d["v_cache"][s:e].cpu()
         ref, _ = oracle.decode_rows(d["q"][b:b + 1].cpu(), d["k_new"][b:b + 1].cpu(), d["v_new"][b:b + 1].cpu(),

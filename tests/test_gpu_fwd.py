@@ -97,16 +97,16 @@ def _sample_rows(lengths, hq, n, seed):
     return toks * hq + heads
 
 
-def test_fwd_global_2x4096_sampled():
-    """Global layer, 2 x 4096 tokens, 64/4 heads, base 1e7, seed 1: sampled rows against the oracle."""
+def test_fwd_global_2x4096_full():
+    """Global layer, 2 x 4096 tokens, 64/4 heads, base 1e7, seed 1: every output row against the oracle (about
+    690 GFLOP of fp64 work on the host)."""
     ga = _gpu()
     d = mi.global_2x4096()
-    print("case global_2x4096", flush=True)
+    print("case global_2x4096 (every row)", flush=True)
     out, lse = _run_fwd(ga, d)
-    rows = _sample_rows(d["lengths"], 64, 600, 1)
-    ro, rl = oracle.prefill_rows(d["q"], d["k"], d["v"], None, d["cu_seqlens"], -1, 1e7, rows)
-    compare("out", out.reshape(-1, 128)[rows], ro)
-    compare("lse", lse.T.reshape(-1)[rows], rl)
+    ro, rl = oracle.prefill(d["q"], d["k"], d["v"], None, d["cu_seqlens"], -1, 1e7)
+    compare("out", out, ro)
+    compare("lse", lse, rl)
 
 
 def test_fwd_thd_32k_sampled():
