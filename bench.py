@@ -399,10 +399,20 @@ def stats_summary(trace_dir, title, command, timed):
 
 def mfma_summary(pmc_dir, title, command):
     """Per library kernel of the traced step of --traffic-probe (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
-    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace): bf16 MFMA flops executed (MOPS x 512), MFMA-busy
-    share of the SIMD cycles (busy / (GRBM_GUI_ACTIVE x 1024 SIMDs)), the clock implied by GRBM_GUI_ACTIVE over
-    the kernel's traced duration, and the executed MFMA rate.  Prints a text table."""
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace): bf16 MFMA flops executed (MOPS x 512), the
+    MFMA-busy share of the SIMD cycles, the clock implied by GRBM_GUI_ACTIVE over the kernel's traced duration,
+    and the executed MFMA rate.  rocprofv3 reports GRBM_GUI_ACTIVE summed over the XCDs (Num_Xcc in the agent
+    file), so one XCD's busy cycles are that sum / Num_Xcc; busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs).
+    Prints a text table."""
     import csv
+
+    nxcc, nsimd = 8, 1024
+    try:
+        for a in csv.DictReader(open(_find_csv(pmc_dir, "agent_info.csv"))):
+            if a.get("Name", "").startswith("gfx"):
+                nxcc, nsimd = int(a["Num_Xcc"]), int(a["Simd_Count"])
+    except (SystemExit, KeyError, ValueError):
+        pass
 
     order = json.load(open(os.path.join(pmc_dir, "traffic_order.json")))["launches"]
     vals = {}
@@ -417,9 +427,9 @@ def mfma_summary(pmc_dir, title, command):
     lib = [k for k in sorted(vals) if "mimo::" in vals[k]["name"]]
     if len(lib) < len(order):
         raise SystemExit(f"{len(lib)} library dispatches with counters, expected at least {len(order)}")
-    print(f"# {title}\n# command: {command}\n# MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; busy = "
-          f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); clock = GRBM_GUI_ACTIVE / traced duration; "
-          f"durations are those of the counter run (kernels serialised)\n")
+    print(f"# {title}\n# command: {command}\n# MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; cycles = "
+          f"GRBM_GUI_ACTIVE / {nxcc} XCDs; busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {nsimd} SIMDs); clock = cycles / "
+          f"traced duration; durations are those of the counter run (kernels serialised)\n")
     print(f"{'launch':24s} {'kernel':34s} {'us':>9s} {'MFMA_TFLOP':>11s} {'TFLOP/s':>9s} {'mfma_busy%':>10s} {'GHz':>6s}")
     for name, k in zip(order, lib[-len(order):]):
         rec = vals[k]
@@ -428,8 +438,8 @@ def mfma_summary(pmc_dir, title, command):
             raise SystemExit(f"launch {name} lines up with dispatch {rec['name']}")
         us = dur.get(k, 0) / 1e3
         flop = rec.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
-        gui = rec.get("GRBM_GUI_ACTIVE", 0.0)
-        busy = 100.0 * rec.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * 1024) if gui else 0.0
+        gui = rec.get("GRBM_GUI_ACTIVE", 0.0) / nxcc
+        busy = 100.0 * rec.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * nsimd) if gui else 0.0
         ghz = gui / (us * 1e3) if us else 0.0
         rate = flop / (us * 1e-6) / 1e12 if us else 0.0
         print(f"{name:24s} {_short_kernel(rec['name'])[:34]:34s} {us:9.1f} {flop / 1e12:11.4f} {rate:9.1f} "

@@ -1222,7 +1222,8 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     trace_begin(a.window >= 0 ? "bwd_prep_k_swa" : "bwd_prep_k_global", stream);
-    e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.W.krt, a, A.T_pad, stream);
+    // the transposed k' copy serves only the dQ kernel that recomputes S and dP (least workspace)
+    e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.ds ? nullptr : A.W.krt, a, A.T_pad, stream);
     trace_end(stream);
     if (e != hipSuccess) return e;
 

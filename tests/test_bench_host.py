@@ -132,13 +132,14 @@ def test_mfma_summary_rates_and_clock(tmp_path, capsys):
     with open(os.path.join(d, "p_counter_collection.csv"), "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
         w.writeheader()
-        # 2e12 flop executed (MOPS x 512) over two instances; 1700 cycles in a 1 us kernel; busy 50% of 1024 SIMDs
+        # 2e12 flop executed (MOPS x 512) over two instances; 1700 cycles in a 1 us kernel (the counter sums the
+        # 8 XCDs); busy 50% of 1024 SIMDs
         for part in (0.5, 0.5):
             w.writerow({"Dispatch_Id": 7, "Kernel_Name": k, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_BF16",
                         "Counter_Value": part * 2e12 / 512})
             w.writerow({"Dispatch_Id": 7, "Kernel_Name": k, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
                         "Counter_Value": part * 0.5 * 1700 * 1024})
-            w.writerow({"Dispatch_Id": 7, "Kernel_Name": k, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 1700})
+            w.writerow({"Dispatch_Id": 7, "Kernel_Name": k, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 1700 * 8})
     _write_trace(d, [(7, k, 0, 1000)])
     bench.mfma_summary(d, "t", "c")
     line = [l for l in capsys.readouterr().out.splitlines() if l.startswith("bwd_dkdv_global")][0].split()
