@@ -15,8 +15,8 @@
 //     s_barriers.  The 16-byte chunks of each LDS row are XOR-swizzled by row (the per-lane source
 //     addresses are permuted), so every MFMA operand read is free of bank conflicts.
 //   * Each wave owns 32 query rows; a workgroup of NW waves owns 32 NW rows: TT = 32 NW / GP consecutive
-//     tokens x GP query heads of one KV group, so all GP heads reuse every K/V tile.  Causal layers use 8
-//     waves (two per SIMD, one K/V stream for 256 rows), sliding-window layers 4 waves (a short key span:
+//     tokens x GP query heads of one KV group, so all GP heads reuse every K/V tile.  Causal layers use 12
+//     waves (three per SIMD, one K/V stream for 384 rows), sliding-window layers 4 waves (a short key span:
 //     the tile's tokens plus 128 keys back).  32-key blocks that no row of a wave can see are skipped.
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: the query is the MFMA column, so each lane owns a query
 //     (lanes l and l ^ 32 split its keys); row max and row sum need one permlane32 swap, and the rescale of
@@ -49,14 +49,18 @@ __device__ __forceinline__ int kpos(int r, int q) { return swz384(r, q); }
 template <int BN>
 __device__ __forceinline__ int vpos(int d, int q) { return BN == 64 ? swz128(d, q) : swz64(d, q); }
 
-// NW waves per workgroup (32 query rows each) share one stream of BN-key K/V tiles.  Causal layers: 8
-// waves, 64-key tiles in a 3-stage ring (120 KB), one workgroup per CU, all 12 K operands of a block read
-// up front (KA = 12).  Sliding-window layers: 4 waves, 32-key tiles double-buffered (40 KB) and KA = 4 so
-// that three workgroups fit on a CU (OCC): these short work items wait mostly on HBM (Q and the first
-// tiles), and more resident workgroups keep more loads in flight.  In both forms q passes through LDS first
-// (48 KB at the start of the pool, or 96 KB behind the first tile's buffer, 136 KB in all): a lane that
+// NW waves per workgroup (32 query rows each) share one stream of BN-key K/V tiles.  Causal layers: 12
+// waves, one workgroup per CU, so three waves share each SIMD and one's softmax and LDS waits overlap the
+// others' MFMAs; that leaves 168 registers per wave: K operands are read four at a time (KA = 4) and the
+// tiles hold 32 keys in a 3-stage ring (60 KB: 64-key tiles would put ring buffers beyond the 64 KB reach of
+// an LDS instruction's offset field, which costs address registers this wave cannot spare).  Sliding-window
+// layers: 4 waves, 32-key tiles double-buffered (40 KB) and KA = 4 so that three workgroups fit on a CU (OCC):
+// these short work items wait mostly on HBM (Q and the first tiles), and more resident workgroups keep more
+// loads in flight.  Sliding-window q passes through LDS first (48 KB at the start of the pool): a lane that
 // loads its own row touches 32 rows per load instruction, while the copy into LDS reads whole runs of rows
-// per instruction; the rotated q for the backward and, after the key loop, O leave the same way.
+// per instruction; the rotated q for the backward leaves the same way.  The 12-wave causal form has no room
+// to stage its 144 KB of q and loads each lane's row directly (once per work item).  After the key loop, O
+// leaves through LDS in both forms.
 template <int NW, int GP, bool SINK, bool WIN, int BN, int KA, int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
 {
@@ -64,14 +68,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     constexpr int NT = 64 * NW;                // threads per workgroup
     constexpr int BM = 32 * NW;                // query rows per workgroup
     constexpr int KLOADS = BN * KCH / NT;      // global_load_lds per thread per K tile
-    constexpr int VLOADS = DVV * VCH / NT;     // ... per V^T tile
+    constexpr int VLOADS = DVV * VCH / NT;     // ... per V^T tile (every thread)
+    constexpr int VEXTRA = DVV * VCH - VLOADS * NT;   // V^T chunks left over: one more for threads below this
+    static_assert(KLOADS * NT == BN * KCH && VEXTRA % 64 == 0, "tile split");
+    constexpr bool QREG = NW > 8;              // q straight into registers (no room to stage 12 waves' rows)
     const LayerArgs &a = A.L;
-    constexpr int NBUF = NW == 8 ? 3 : 2;      // LDS stages (3 x 40 KB for one 8-wave workgroup per CU)
+    constexpr int NBUF = NW >= 8 ? 3 : 2;      // LDS stages: three where one workgroup owns the CU
     constexpr int KS = BN * KCH, VS = DVV * VCH;                 // 16-byte chunks of a K and a V^T tile
     // the workgroup's q rows pass through LDS first: sliding window from the start of the pool (the first
     // tile is issued after them), causal behind the first tile's buffer (the first tile is in flight meanwhile)
-    constexpr int QOFF = WIN ? 0 : KS + VS, QEND = QOFF + BM * KCH;
-    constexpr int POOL = NBUF * (KS + VS) > QEND ? NBUF * (KS + VS) : QEND;
+    constexpr int QOFF = WIN ? 0 : KS + VS, QEND = QREG ? 0 : QOFF + BM * KCH;
+    constexpr int OSTAGE = BM * DVV / 8;                          // the epilogue's O rows (16-byte chunks)
+    constexpr int POOL0 = NBUF * (KS + VS) > QEND ? NBUF * (KS + VS) : QEND;
+    constexpr int POOL = POOL0 > OSTAGE ? POOL0 : OSTAGE;
     __shared__ __attribute__((aligned(16))) uint4 lds[POOL];
     uint4 *const sK0 = lds, *const sV0 = lds + KS, *const sK1 = lds + KS + VS, *const sV1 = lds + 2 * KS + VS;
     uint4 *const sK2 = lds + 2 * (KS + VS), *const sV2 = lds + 3 * KS + 2 * VS;   // NBUF == 3 only
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     const u16 *kr_base = A.P.kr + (size_t)kvh * DQK;
     const size_t kr_row = (size_t)a.hkv * DQK;
     const u16 *vt_base = A.P.vt + (size_t)kvh * DVV * A.P.T_pad;
-    uint32_t koff[KLOADS], voff[VLOADS];
+    uint32_t koff[KLOADS], voff[VLOADS > 0 ? VLOADS : 1];
 #pragma unroll
     for (int j = 0; j < KLOADS; ++j) {
         const int slot = NT * j + tid, r = slot / KCH, p = slot % KCH;
@@ -135,6 +144,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         const int slot = NT * j + tid, d = slot / VCH, p = slot % VCH;
         voff[j] = (uint32_t)(((size_t)d * A.P.T_pad + 8 * vpos<BN>(d, p)) * 2);
     }
+    uint32_t vextra = 0;
+    if constexpr (VEXTRA > 0) {
+        const int slot = NT * VLOADS + min(tid, VEXTRA - 1), d = slot / VCH, p = slot % VCH;
+        vextra = (uint32_t)(((size_t)d * A.P.T_pad + 8 * vpos<BN>(d, p)) * 2);
+    }
     auto issue_tile = [&](int k0, uint4 *sk, uint4 *sv) {
         const u16 *kb = kr_base + (size_t)k0 * kr_row;
         const u16 *vb = vt_base + k0;
@@ -142,6 +156,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         for (int j = 0; j < KLOADS; ++j) lds_dma16(kb, koff[j], sk + NT * j + 64 * wave);
 #pragma unroll
         for (int j = 0; j < VLOADS; ++j) lds_dma16(vb, voff[j], sv + NT * j + 64 * wave);
+        if constexpr (VEXTRA > 0) {
+            if (wave < VEXTRA / 64) lds_dma16(vb, vextra, sv + NT * VLOADS + 64 * wave);
+        }
+    };
+    // this wave's loads of one tile (waves below VEXTRA / 64 issue one more V^T chunk)
+    auto wait_tile = [&]() {
+        if constexpr (VEXTRA > 0) {
+            if (wave < VEXTRA / 64) wait_vmcnt<KLOADS + VLOADS + 1>();
+            else wait_vmcnt<KLOADS + VLOADS>();
+        } else {
+            wait_vmcnt<KLOADS + VLOADS>();
+        }
     };
     if constexpr (!WIN) issue_tile(kstart, sK0, sV0);
 
@@ -161,6 +187,25 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         // back into their slots and each instruction stores whole runs.  The next K/V tile is issued into
         // this LDS once every wave is done with its q (sliding window: the first tile; causal: the second,
         // the first being in flight meanwhile in its own buffer).
+        if constexpr (QREG) {
+            // each lane loads its own row (12 16-byte pieces), rotates dims 0..63 and, for the backward,
+            // stores the rotated row
+            const u16 *qp = a.q + ((size_t)qtl * a.hq + qh) * DQK + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                c0[t] = cs[t];
+                c1[t] = cs[16 + t];
+            }
+            rope_pair(qf[0], qf[2], c0);
+            rope_pair(qf[1], qf[3], c1);
+            if (A.q_rot && qvalid) {
+                u16 *qr = A.q_rot + ((size_t)qt * a.hq + qh) * DQK + 8 * hh;
+#pragma unroll
+                for (int s = 0; s < 12; ++s) st16(qr + 16 * s, qf[s]);
+            }
+        } else {
         const u16 *qbase = a.q + ((size_t)t0 * a.hq + h0) * DQK;
         uint4 *qs = lds + QOFF + 32 * KCH * wave;
 #pragma unroll
@@ -191,6 +236,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
                 if (tok < seq_end)
                     st16u(A.q_rot + ((size_t)tok * a.hq + h0 + rr % GP) * DQK + 8 * kpos(rw, g % KCH), x);
             }
+        }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -316,7 +362,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         // only by these direct loads, so a plain s_barrier suffices.
         issue_tile(min(kstart + BN, klast), sK1, sV1);
         auto step = [&](int it, const uint4 *ck, const uint4 *cv, uint4 *nk, uint4 *nv) {
-            wait_vmcnt<KLOADS + VLOADS>();
+            wait_tile();
             __builtin_amdgcn_s_barrier();
             issue_tile(min(kstart + (it + 2) * BN, klast), nk, nv);
             if (it < nkt) compute_tile(kstart + it * BN, ck, cv);
@@ -336,12 +382,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         for (int it = 0; it < nkt; it += 2) {
             const int k0 = kstart + it * BN;
             issue_tile(min(k0 + BN, klast), sK1, sV1);
-            wait_vmcnt<KLOADS + VLOADS>();
+            wait_tile();
             __builtin_amdgcn_s_barrier();       // tile it is in buffer 0 for every wave
             compute_tile(k0, sK0, sV0);
             __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 0
             issue_tile(min(k0 + 2 * BN, klast), sK0, sV0);
-            wait_vmcnt<KLOADS + VLOADS>();
+            wait_tile();
             __builtin_amdgcn_s_barrier();       // tile it+1 is in buffer 1 for every wave
             if (it + 1 < nkt) compute_tile(k0 + BN, sK1, sV1);
             __builtin_amdgcn_s_barrier();       // every wave is done reading buffer 1
@@ -389,7 +435,7 @@ hipError_t launch_gp(const FwdArgs &A, hipStream_t stream)
     const LayerArgs &a = A.L;
     const int G = a.hq / a.hkv;
     const bool sink = a.sink != nullptr, win = a.window >= 0;
-    const int NW = win ? 4 : 8;
+    const int NW = win ? 4 : 12;
     const int TT = 32 * NW / GP;
     // upper bound on the number of token tiles: sum ceil(len/TT) <= ceil(T/TT) + batch
     const long tiles = (long)(a.T + TT - 1) / TT + a.batch;
@@ -399,8 +445,8 @@ hipError_t launch_gp(const FwdArgs &A, hipStream_t stream)
     trace_begin(win ? "attn_fwd_swa" : "attn_fwd_global", stream);
     if (sink && win) attn_fwd_kernel<4, GP, true, true, 32, 4, 3><<<(unsigned)grid, 256, 0, stream>>>(A);
     else if (win) attn_fwd_kernel<4, GP, false, true, 32, 4, 3><<<(unsigned)grid, 256, 0, stream>>>(A);
-    else if (sink) attn_fwd_kernel<8, GP, true, false, 64, 12, 1><<<(unsigned)grid, 512, 0, stream>>>(A);
-    else attn_fwd_kernel<8, GP, false, false, 64, 12, 1><<<(unsigned)grid, 512, 0, stream>>>(A);
+    else if (sink) attn_fwd_kernel<12, GP, true, false, 32, 4, 1><<<(unsigned)grid, 768, 0, stream>>>(A);
+    else attn_fwd_kernel<12, GP, false, false, 32, 4, 1><<<(unsigned)grid, 768, 0, stream>>>(A);
     trace_end(stream);
     return hipGetLastError();
 }

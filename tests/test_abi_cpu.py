@@ -260,7 +260,7 @@ def _fwd_tile_starts(t0, t_last, kofs, kseq, window, T_pad, BN):
     return starts, computed, khi
 
 
-@pytest.mark.parametrize("window,BN,TT", [(-1, 64, 32), (128, 32, 16), (3, 32, 16)])
+@pytest.mark.parametrize("window,BN,TT", [(-1, 32, 48), (128, 32, 16), (3, 32, 16)])
 def test_fwd_key_tiles_stay_inside_the_prepared_stream(window, BN, TT):
     """Cached prefill with cache index arrays that agree with the sizes, claim more rows than given (the key
     offsets run past the stream) or fewer: every tile the forward issues lies inside the T_pad rows of the
@@ -305,3 +305,14 @@ def test_decode_paged_noalloc_rejects_partials_beyond_its_scratch(L):
                                             64, 4, FAKE, None) == 1          # no page table
     assert L.mimo_attn_decode_paged_noalloc(None, None, None, None, None, None, None, None, None, 0, 0, -1, 1e7,
                                             64, 4, None, None) == 0          # empty batch: nothing to do
+
+
+def test_m0_guard_of_the_build():
+    """The build rejects device code that touches m0 anywhere but in the copy helper's own sequence."""
+    from global_gqa_attention_amd.build import _m0_misuse
+
+    ok = "\ts_mov_b32 m0, s31\n\ts_nop 0\n\tglobal_load_lds_dwordx4 v65, s[12:13]\n\tv_add_u32 v1, v2, v3 ; m0 in a comment\n"
+    assert _m0_misuse(ok) == []
+    assert _m0_misuse("\ts_mov_b32 m0, -1\n\tds_read_b32 v1, v2\n") == ["s_mov_b32 m0, -1"]
+    assert _m0_misuse("\ts_mov_b32 m0, s4\n\ts_nop 0\n\tds_gws_init v1\n") == ["s_mov_b32 m0, s4"]
+    assert _m0_misuse("\ts_mov_b32 s5, m0\n") == ["s_mov_b32 s5, m0"]
