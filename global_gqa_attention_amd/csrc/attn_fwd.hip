@@ -200,11 +200,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
             }
             rope_pair(qf[0], qf[2], c0);
             rope_pair(qf[1], qf[3], c1);
-            if (A.q_rot && qvalid) {
-                u16 *qr = A.q_rot + ((size_t)qt * a.hq + qh) * DQK + 8 * hh;
-#pragma unroll
-                for (int s = 0; s < 12; ++s) st16(qr + 16 * s, qf[s]);
-            }
+            // (the rotated q for the backward is stored at the end: stores issued here would sit in the
+            // same vmcnt queue as the first tiles' copies and delay the ring's waits)
         } else {
         const u16 *qbase = a.q + ((size_t)t0 * a.hq + h0) * DQK;
         uint4 *qs = lds + QOFF + 32 * KCH * wave;
@@ -425,6 +422,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
             const int g = 64 * j + ln, rw = g >> 4, p = g & 15, r = wave * 32 + rw;
             const uint4 x = ws[16 * rw + (p ^ (rw & 15))];
             if (t0 + r / GP < seq_end) st16u(obase + (uint32_t)(((r / GP) * a.hq + r % GP) * DVV + 8 * p), x);
+        }
+    }
+    if constexpr (QREG) {
+        if (A.q_rot && qvalid) {
+            u16 *qr = A.q_rot + ((size_t)qt * a.hq + qh) * DQK + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < 12; ++s) st16(qr + 16 * s, qf[s]);
         }
     }
 }
