@@ -939,7 +939,6 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
 //     lane i, element t <- the 4-element row read by lane 4 t + i / 4, element i % 4.  The MFMA k index
 //     8 hh + 4 r + t of read r (0, 1) stands for key 16 s + 8 r + 4 hh + t in both operands.
 // ------------------------------------------------------------------------------------------------------
-constexpr int DSQ_NS = 5;                // ring stages (four block loads in flight: the kernel streams HBM)
 
 // NH waves per workgroup, one query head each: the NH heads share every k' tile (the k' rows are loaded
 // by the first 768 / 128 = 6 waves, two chunks per lane; every wave loads its own dS block)
@@ -949,13 +948,18 @@ struct DsqTile {
     uint4 ds[NH][128];                   // one stored dS block per wave
 };
 
-template <int NH, bool WIN>
-__global__ __launch_bounds__(64 * NH, 1) void bwd_dq_ds_kernel(const BwdArgs A)
+// NS ring stages, OCC workgroups per CU.  Causal layers: eight heads per workgroup and five stages (140 KB,
+// four block loads in flight: long work items that stream HBM).  Sliding-window layers: four heads and three
+// stages (60 KB), two workgroups per CU: their work items are short (about six key blocks), and a second
+// resident workgroup hides one's start-up under the other's work (0.447 -> 0.414 ms at the 32K batch; the
+// causal layer measured 1.95 ms in the first form and 2.02 ms in this one).
+template <int NH, bool WIN, int NS, int OCC>
+__global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
     constexpr int KL = NH == 4 ? 3 : 2;                  // k' DMAs per lane of a loading wave
     constexpr int KW = 32 * KCH / (64 * KL);             // waves that load k' (4 or 6)
-    __shared__ __attribute__((aligned(16))) DsqTile<NH> ring[DSQ_NS];   // 100 KB (4 heads) / 140 KB (8)
+    __shared__ __attribute__((aligned(16))) DsqTile<NH> ring[NS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1034,25 +1038,23 @@ __global__ __launch_bounds__(64 * NH, 1) void bwd_dq_ds_kernel(const BwdArgs A)
         }
     };
 
-    // ---- ring of DSQ_NS buffers, four block loads in flight: at stage st wait until block st landed (the
-    // three newer sets may still be in flight), barrier (every wave landed its part and finished stage
-    // st-1, whose buffer the next load refills), load block st+4, compute block st.  Every stage loads one
-    // set (the last block again once the blocks run out), so the waits stay uniform.  The buffer index is a
-    // run-time value (one loop body for all stages).
-    issue(0, ring[0]);
-    issue(min(1, nsteps - 1), ring[1]);
-    issue(min(2, nsteps - 1), ring[2]);
-    issue(min(3, nsteps - 1), ring[3]);
+    // ---- ring of NS buffers, NS - 1 block loads in flight: at stage st wait until block st landed (the
+    // NS - 2 newer sets may still be in flight), barrier (every wave landed its part and finished stage
+    // st-1, whose buffer the next load refills), load block st + NS - 1, compute block st.  Every stage loads
+    // one set (the last block again once the blocks run out), so the waits stay uniform.  The buffer index
+    // is a run-time value (one loop body for all stages).
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) issue(min(i, nsteps - 1), ring[i]);
     int cur = 0;
     for (int st = 0; st < nsteps; ++st) {
-        const int fill = cur == 0 ? DSQ_NS - 1 : cur - 1;
+        const int fill = cur == 0 ? NS - 1 : cur - 1;
         // loads per stage: KL + 2 for the k'-loading waves, 2 for the others
-        if (wave < KW) wait_vmcnt<3 * (KL + 2)>();
-        else wait_vmcnt<3 * 2>();
+        if (wave < KW) wait_vmcnt<(NS - 2) * (KL + 2)>();
+        else wait_vmcnt<(NS - 2) * 2>();
         __builtin_amdgcn_s_barrier();
-        issue(min(st + 4, nsteps - 1), ring[fill]);
+        issue(min(st + NS - 1, nsteps - 1), ring[fill]);
         compute(ring[cur]);
-        cur = cur == DSQ_NS - 1 ? 0 : cur + 1;
+        cur = cur == NS - 1 ? 0 : cur + 1;
     }
     wait_vmcnt<0>();
 
@@ -1253,14 +1255,13 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     }
     const int G = a.hq / a.hkv;
     if (A.ds) {
-        const int nh = G % 8 == 0 ? 8 : 4;
+        const int nh = G % 8 == 0 && a.window < 0 ? 8 : 4;
         const long grid = ((long)a.T / 32 + 2L * a.batch) * (G / nh) * a.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         trace_begin(a.window >= 0 ? "bwd_dq_ds_swa" : "bwd_dq_ds_global", stream);
-        if (nh == 8 && a.window >= 0) bwd_dq_ds_kernel<8, true><<<(unsigned)grid, 512, 0, stream>>>(A);
-        else if (nh == 8) bwd_dq_ds_kernel<8, false><<<(unsigned)grid, 512, 0, stream>>>(A);
-        else if (a.window >= 0) bwd_dq_ds_kernel<4, true><<<(unsigned)grid, 256, 0, stream>>>(A);
-        else bwd_dq_ds_kernel<4, false><<<(unsigned)grid, 256, 0, stream>>>(A);
+        if (a.window >= 0) bwd_dq_ds_kernel<4, true, 3, 2><<<(unsigned)grid, 256, 0, stream>>>(A);
+        else if (nh == 8) bwd_dq_ds_kernel<8, false, 5, 1><<<(unsigned)grid, 512, 0, stream>>>(A);
+        else bwd_dq_ds_kernel<4, false, 5, 1><<<(unsigned)grid, 256, 0, stream>>>(A);
         trace_end(stream);
         return hipGetLastError();
     }
