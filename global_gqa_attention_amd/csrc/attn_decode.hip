@@ -18,7 +18,11 @@
 // other wave on its SIMD computes, which kept more bytes in flight than two buffers at four workgroups per
 // CU or deeper rings with fewer.  Each split writes an unnormalised
 // partial (o, running max, running sum); the combine kernel merges the splits with the sink and the new
-// token (whose rotation is computed there in double precision).
+// token (whose rotation is computed there in double precision).  A sliding-window decode (at most four
+// chunks, one split) copies its chunks all at once into four buffers and merges the new token and the
+// sink itself, with no combine kernel.  The query's rotation angles depend only on the position and the
+// dim, so a decode wave computes each of the 32 once (in double precision) and shares them by lane
+// shuffles.
 //
 // The same kernels serve two more forms.  Paged cache (page size 1: SGLang cookbook page "MiMo-V2.6",
 // section 2): cache row r of sequence b is pool row page_table[cu_cache[b] + r]; each lane of the first 32
@@ -56,10 +60,14 @@ __device__ __forceinline__ const u16 *wave_uniform(const u16 *p)
     return (const u16 *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <bool PAGED>
+// NB = 1: one buffer, chunks copied and computed in turn (see the loop).  NB = 4 (decode over a window of
+// at most four chunks, one split): all chunks are copied at once, so the workgroup waits for one HBM round
+// trip instead of four, and with FIN it also merges the new token and the sink and writes the output, so no
+// combine kernel follows.
+template <bool PAGED, int NB, bool FIN>
 __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
 {
-    __shared__ __attribute__((aligned(256))) DecTile ring[1];   // one buffer (see the loop)
+    __shared__ __attribute__((aligned(256))) DecTile ring[NB];
     const int lane = threadIdx.x, hh = lane >> 5, c = lane & 31;
     const int grp = lane >> 4, t4 = (lane & 15) >> 2, m4 = lane & 3;
     const int G = A.hq / A.hkv;
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
         lo = A.window >= 0 ? lim - A.window : min(lim, 0);
     }
 
-    if (ks >= ke) {                          // nothing cached in this split: an empty partial
+    if (!FIN && ks >= ke) {                  // nothing cached in this split: an empty partial
         if (hvalid) {
             if (hh == 0) {
                 A.part_ml[part * 2 + 0] = -INFINITY;
@@ -133,7 +141,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
         k = min(k, klast);
         return A.page_table[c0 + min(k + c, ke - 1)];
     };
-    int tv = PAGED ? table_rows(ks) : 0;
+    int tv = PAGED && ks < ke ? table_rows(ks) : 0;
     auto issue = [&](int k, DecTile &T) __attribute__((always_inline)) {
         k = __builtin_amdgcn_readfirstlane(min(k, klast));   // past the end: the last chunk again (uniform waits)
         if constexpr (PAGED) {
@@ -172,25 +180,76 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
             }
         }
     };
-    issue(ks, ring[0]);
+    if constexpr (NB == 1) {
+        if (ks < ke) issue(ks, ring[0]);
+    } else if (ks < ke) {
+        // all NB chunks at once (the split's last chunk again past its end); paged: the pool rows of every
+        // chunk are read first, so the copies do not wait on table loads issued between them
+        int tvs[NB];
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) tvs[i] = table_rows(ks + CH * i);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if constexpr (PAGED) tv = tvs[i];
+            issue(ks + CH * i, ring[i]);
+        }
+    }
 
-    // rotated query (bf16) as the B operand: column = head, dims 16s + 8hh + t
+    // rotated query (bf16) as the B operand: column = head, dims 16s + 8hh + t.  FIN: also this lane's part
+    // of the new token's score, q' . k_new' with k_new rotated at the same position in fp32
     bf16x8 qf[12];
+    float dot_new = 0.f;
     {
         const u16 *qp = A.q + (((size_t)b * A.nq + ti) * A.hq + h) * DQK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
         const double pos = (double)A.positions[b] + (double)ti;
+        // decode: every column sits at the sequence's position, so the 32 angles of the rotated dims are
+        // computed once (lane l takes dim l % 32) and each lane fetches the 16 it uses; verify columns sit at
+        // their own draft positions and compute theirs
+        float cf = 0.f, sf = 0.f;
+        if (!verify) {
+            double sn, cn;
+            sincos(pos * inv_freq(A.rope_base, lane & 31), &sn, &cn);
+            cf = (float)cn;
+            sf = (float)sn;
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float2 cs[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                double sn, cn;
-                sincos(pos * inv_freq(A.rope_base, 16 * s + 8 * hh + t), &sn, &cn);
-                cs[t] = make_float2((float)cn, (float)sn);
+                if (!verify) {
+                    const int d = 16 * s + 8 * hh + t;
+                    cs[t] = make_float2(__shfl(cf, d, 64), __shfl(sf, d, 64));
+                } else {
+                    double sn, cn;
+                    sincos(pos * inv_freq(A.rope_base, 16 * s + 8 * hh + t), &sn, &cn);
+                    cs[t] = make_float2((float)cn, (float)sn);
+                }
             }
             rope_pair(qf[s], qf[s + 2], cs);
+            if constexpr (FIN) {
+                const u16 *kp = A.k_new + ((size_t)b * A.hkv + kvh) * DQK + 8 * hh;
+                const bf16x8 k0 = ld16(kp + 16 * s), k1 = ld16(kp + 16 * (s + 2));
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float a0 = bf2f(k0[t]), a1 = bf2f(k1[t]);
+                    dot_new += bf2f(qf[s][t]) * (a0 * cs[t].x - a1 * cs[t].y) +
+                               bf2f(qf[s + 2][t]) * (a1 * cs[t].x + a0 * cs[t].y);
+                }
+            }
+        }
+        if constexpr (FIN) {
+            const u16 *kp = A.k_new + ((size_t)b * A.hkv + kvh) * DQK + 8 * hh;
+#pragma unroll
+            for (int s = 4; s < 12; ++s) {
+                const bf16x8 k0 = ld16(kp + 16 * s);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) dot_new += bf2f(qf[s][t]) * bf2f(k0[t]);
+            }
         }
         // every q register is complete before the chunk loop: otherwise the compiler's own load waits for
         // them, placed inside the loop, also stall on the cache loads in flight
@@ -258,17 +317,56 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
         }
     };
 
-    // ---- one buffer: wait for chunk k (the only loads in flight), compute it, wait until every LDS read of
-    // the buffer has returned, then copy chunk k + CH into it (the other wave on the SIMD computes meanwhile)
-    for (int k = ks; k < ke; k += CH) {
+    if constexpr (NB == 1) {
+        // ---- one buffer: wait for chunk k (the only loads in flight), compute it, wait until every LDS read
+        // of the buffer has returned, then copy chunk k + CH into it (the other wave on the SIMD computes
+        // meanwhile)
+        for (int k = ks; k < ke; k += CH) {
+            wait_vmcnt<0>();
+            chunk(k, ring[0]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every read of the buffer has returned
+            if (k + CH < ke) issue(k + CH, ring[0]);
+        }
+    } else if (ks < ke) {
+        // ---- every chunk in flight: chunk i has landed once at most the copies of the later ones are
+        // outstanding (each chunk is CH * (DKC + DVC) / 64 copy instructions, issued in order)
+        constexpr int LC = CH * (DKC + DVC) / 64;
+        static_assert(NB == 4, "the waits below are written for four chunks");
+        wait_vmcnt<3 * LC>();
+        chunk(ks, ring[0]);
+        wait_vmcnt<2 * LC>();
+        if (ks + CH < ke) chunk(ks + CH, ring[1]);
+        wait_vmcnt<LC>();
+        if (ks + 2 * CH < ke) chunk(ks + 2 * CH, ring[2]);
         wait_vmcnt<0>();
-        chunk(k, ring[0]);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every read of the buffer has returned
-        if (k + CH < ke) issue(k + CH, ring[0]);
+        if (ks + 3 * CH < ke) chunk(ks + 3 * CH, ring[3]);
     }
     wait_vmcnt<0>();                        // no load may still target this workgroup's LDS at exit
 
     const float l_tot = pair_sum(l_run);
+    if constexpr (FIN) {
+        // ---- the new token's score (q' . k_new' with k_new rotated at the same position, in fp32) and the
+        // sink join the running max and sum, then out = 0.707 * o / sum in bf16
+        const float s_new = pair_sum(dot_new) * A.scale_log2;
+        const float sk = A.sink ? A.sink[h] * LOG2E : -INFINITY;
+        const float M = fmaxf(fmaxf(m_run, s_new), sk);
+        const float alpha = fast_exp2(m_run - M), w_new = fast_exp2(s_new - M);
+        const float Lt = l_tot * alpha + w_new + (sk > -INFINITY ? fast_exp2(sk - M) : 0.f);
+        const float inv = VSCALE / Lt;
+        const u16 *vp = A.v_new + ((size_t)b * A.hkv + kvh) * DVV + 4 * hh;
+        u16 *out = A.out + (((size_t)b * A.nq + ti) * A.hq + h) * DVV + 4 * hh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const bf16x4 v4 = __builtin_bit_cast(bf16x4, *(const uint2 *)(vp + 32 * i + 8 * jj));
+                bf16x4 w;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) w[t] = f2bf((o[i][4 * jj + t] * alpha + w_new * bf2f(v4[t])) * inv);
+                if (hvalid) *(uint2 *)(out + 32 * i + 8 * jj) = __builtin_bit_cast(uint2, w);
+            }
+        return;
+    }
     if (hvalid) {
         if (hh == 0) {
             A.part_ml[part * 2 + 0] = m_run;
@@ -677,8 +775,22 @@ hipError_t launch_decode(const DecodeArgs &A, hipStream_t stream)
         const unsigned wgs = (unsigned)((long)A.batch * A.hkv * A.splits);
         if (A.page_table) verify_split_kernel<true><<<wgs, 64 * VNW, 0, stream>>>(A);
         else verify_split_kernel<false><<<wgs, 64 * VNW, 0, stream>>>(A);
-    } else if (A.page_table) decode_split_kernel<true><<<(unsigned)waves, 64, 0, stream>>>(A);
-    else decode_split_kernel<false><<<(unsigned)waves, 64, 0, stream>>>(A);
+    } else {
+        // decode over a window of at most four chunks (one split): the chunks are copied all at once and the
+        // split kernel writes the output itself
+        const bool fin = A.k_new != nullptr && A.splits == 1 && A.window >= 0 && A.window <= 4 * CH;
+        if (A.page_table) {
+            if (fin) decode_split_kernel<true, 4, true><<<(unsigned)waves, 64, 0, stream>>>(A);
+            else decode_split_kernel<true, 1, false><<<(unsigned)waves, 64, 0, stream>>>(A);
+        } else {
+            if (fin) decode_split_kernel<false, 4, true><<<(unsigned)waves, 64, 0, stream>>>(A);
+            else decode_split_kernel<false, 1, false><<<(unsigned)waves, 64, 0, stream>>>(A);
+        }
+        if (fin) {
+            trace_end(stream);
+            return hipGetLastError();
+        }
+    }
     trace_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
