@@ -521,14 +521,32 @@ __global__ __launch_bounds__(64 * VNW, 2) void verify_split_kernel(const DecodeA
 #pragma unroll
         for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
         const double pos = (double)A.positions[b] + (double)ti;
+        // the angles depend only on (token, dim): when this wave's 32 columns span at most two draft tokens
+        // (16 or more heads per KV head), lane l computes token t_lo + l / 32, dim l % 32 once (in double
+        // precision) and each lane fetches the 16 it uses; otherwise every lane computes its own
+        const int t_lo = hgrp * 32 / G, t_hi = min(hgrp * 32 + 31, NC - 1) / G;
+        const bool shared = t_hi - t_lo <= 1;
+        float cf = 0.f, sf = 0.f;
+        if (shared) {
+            double sn, cn;
+            sincos(((double)A.positions[b] + (double)(t_lo + (lane >> 5))) * inv_freq(A.rope_base, lane & 31), &sn, &cn);
+            cf = (float)cn;
+            sf = (float)sn;
+        }
+        const int src0 = 32 * (ti - t_lo);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float2 cs[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                double sn, cn;
-                sincos(pos * inv_freq(A.rope_base, 16 * s + 8 * hh + t), &sn, &cn);
-                cs[t] = make_float2((float)cn, (float)sn);
+                if (shared) {
+                    const int d = src0 + 16 * s + 8 * hh + t;
+                    cs[t] = make_float2(__shfl(cf, d, 64), __shfl(sf, d, 64));
+                } else {
+                    double sn, cn;
+                    sincos(pos * inv_freq(A.rope_base, 16 * s + 8 * hh + t), &sn, &cn);
+                    cs[t] = make_float2((float)cn, (float)sn);
+                }
             }
             rope_pair(qf[s], qf[s + 2], cs);
         }
