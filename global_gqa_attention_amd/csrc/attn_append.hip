@@ -12,8 +12,10 @@
 namespace mimo {
 namespace {
 
-// One workgroup of 64 threads per (token, KV head): threads 0..3 rotate K chunk pairs (c, c + 4), threads
-// 4..19 copy K chunks 8..23, threads 20..35 copy the 16 V chunks.  Slots outside the pool are skipped.
+// One workgroup of 64 threads per (token, KV head): threads 0..31 compute the angle of dim t once (fp64),
+// threads 0..3 then rotate K chunk pairs (c, c + 4) with the eight (cos, sin) they fetch by lane shuffles,
+// threads 4..19 copy K chunks 8..23, threads 20..35 copy the 16 V chunks.  Slots outside the pool are
+// skipped.
 __global__ __launch_bounds__(64) void cache_append_kernel(const uint16_t *k, const uint16_t *v, const int32_t *positions,
                                                           const int32_t *slots, int hkv, int pool_rows, double base,
                                                           uint16_t *k_pool, uint16_t *v_pool)
@@ -23,18 +25,19 @@ __global__ __launch_bounds__(64) void cache_append_kernel(const uint16_t *k, con
     if (slot < 0 || slot >= pool_rows) return;
     const u16 *ks = k + ((size_t)i * hkv + kvh) * DQK;
     u16 *kd = k_pool + ((size_t)slot * hkv + kvh) * DQK;
+    float cf = 0.f, sf = 0.f;
+    {
+        const double ang = (double)positions[i] * pow(base, -(double)(t & 31) / (double)NHALF);
+        double sn, cn;
+        sincos(ang, &sn, &cn);
+        cf = (float)cn;
+        sf = (float)sn;
+    }
+    float2 cs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs[e] = make_float2(__shfl(cf, 8 * (t & 3) + e, 64), __shfl(sf, 8 * (t & 3) + e, 64));
     if (t < 4) {
         bf16x8 x0 = ld16(ks + 8 * t), x1 = ld16(ks + 8 * (t + 4));
-        const double pos = (double)positions[i];
-        float2 cs[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = 8 * t + e;
-            const double ang = pos * pow(base, -(double)d / (double)NHALF);
-            double sn, cn;
-            sincos(ang, &sn, &cn);
-            cs[e] = make_float2((float)cn, (float)sn);
-        }
         rope_pair(x0, x1, cs);
         st16(kd + 8 * t, x0);
         st16(kd + 8 * (t + 4), x1);
