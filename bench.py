@@ -429,7 +429,8 @@ def mfma_summary(pmc_dir, title, command):
         raise SystemExit(f"{len(lib)} library dispatches with counters, expected at least {len(order)}")
     print(f"# {title}\n# command: {command}\n# MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; cycles = "
           f"GRBM_GUI_ACTIVE / {nxcc} XCDs; busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {nsimd} SIMDs); clock = cycles / "
-          f"traced duration; durations are those of the counter run (kernels serialised)\n")
+          f"traced duration; durations and clocks are those of the counter run, which runs the kernels serialised "
+          f"and slower than a plain run (compare the kernel-trace summary)\n")
     print(f"{'launch':24s} {'kernel':34s} {'us':>9s} {'MFMA_TFLOP':>11s} {'TFLOP/s':>9s} {'mfma_busy%':>10s} {'GHz':>6s}")
     for name, k in zip(order, lib[-len(order):]):
         rec = vals[k]
