@@ -306,11 +306,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const uint32_t o_or = (uint32_t)((oslot_r * o_row + 8 * swz256t(oslot_r, oslot_p)) * 2);
     // step -> (head, query tile): heads outer, query tiles from the sequence end down.  Every key tile of a
     // sequence walks the same absolute query tiles in the same order, so the workgroups running together
-    // on an XCD read the same q'/dO tiles and mostly hit in L2.
-    auto step_q0 = [&](int step) { return q_lo + (nq - 1 - step % nq) * MQ; };
-    auto issue = [&](int step, DkdvTile &T) {
-        const int h = kvh * G + split * GS + step / nq;
-        const int q0 = step_q0(step);
+    // on an XCD read the same q'/dO tiles and mostly hit in L2.  The stages walk the steps in order, so the
+    // position advances by one tile per stage (no division per stage).
+    struct Pos {
+        int q0, h;   // first query of the step's tile, its query head
+    };
+    const int q_top = q_lo + (nq - 1) * MQ;
+    const Pos first{q_top, kvh * G + split * GS};
+    auto advance = [&](Pos p) {
+        p.q0 -= MQ;
+        if (p.q0 < q_lo) {
+            p.q0 = q_top;
+            ++p.h;
+        }
+        return p;
+    };
+    auto issue = [&](Pos ps, DkdvTile &T) {
+        const int h = ps.h, q0 = ps.q0;
         if (wave < 6) {
             if (q0 + MQ <= A.qr_rows) {
                 const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
@@ -346,12 +358,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int kjl = kvalid ? kj : kb_last;
 
     // Which queries of a step do these keys need?  None (skip), all (no mask), or some (mask).
-    auto visible = [&](int step) {
-        const int q0 = step_q0(step);
+    auto visible = [&](int step, Pos ps) {
+        const int q0 = ps.q0;
         return step < nsteps && !(q0 + MQ - 1 < kw0 || kw0 > kb_last || (WIN && q0 > kw0 + 31 + a.window));
     };
-    auto masked = [&](int step) {
-        const int q0 = step_q0(step);
+    auto masked = [&](Pos ps) {
+        const int q0 = ps.q0;
         return q0 < kw0 + 31 || q0 + MQ - 1 > q_hi || (WIN && q0 + MQ - 1 - kw0 > a.window) || kw0 + 31 > kb_last;
     };
     // mask bound: query qi sees this lane's key iff 0 <= qi - kj <= ub.  Lanes past the tile's last key see
@@ -376,15 +388,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     // writes of the previous stage visible, barrier (every wave has landed its part and finished stage st-1;
     // the buffer of step st-2 is free), load step st+1.  Every stage loads one tile set (the last step's
     // again once the steps run out), so the waits stay uniform.  Both roles pass nsteps + 1 barriers.
-    issue(0, ring[0]);
+    issue(first, ring[0]);
     bool stored = false;
-    auto stage_start = [&](int st, DkdvTile &fill) {
+    // pc: step st, pn: step min(st + 1, nsteps - 1) (the one stage st loads)
+    Pos pc = first, pn = nsteps > 1 ? advance(first) : first;
+    auto stage_start = [&](DkdvTile &fill) {
         if (stored) wait_vmcnt<2>();
         else wait_vmcnt<0>();
         stored = false;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        issue(min(st + 1, nsteps - 1), fill);
+        issue(pn, fill);
+    };
+    auto stage_end = [&](int st) {
+        pc = pn;
+        if (st + 2 <= nsteps - 1) pn = advance(pn);
     };
 
     if (role == 0) {
@@ -425,9 +443,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         const int s16 = seq_start & ~15;
         const int kap = 4 * tile + kq;
         const int64_t ds_head = A.ds ? A.ds_index[a.batch] : 0, ds_seq = A.ds ? A.ds_index[bseq] : 0;
-        auto store_ds = [&](int step, const bf16x8 *sb) {
-            const int h = kvh * G + split * GS + step / nq;
-            const int q0 = step_q0(step);
+        auto store_ds = [&](Pos ps, const bf16x8 *sb) {
+            const int h = ps.h, q0 = ps.q0;
             const int n = (q0 - s16) >> 5;
             const int64_t blk = (int64_t)h * ds_head + ds_seq + ds_rows_before(n, a.window) +
                                 (kap - ds_klo(q0, seq_start, a.window));
@@ -440,9 +457,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[1]), dst + 64 + (lane ^ (8 * hh) ^ 4));
             return true;
         };
-        auto s_step = [&](int st, const DkdvTile &T, uint4 *pslot) {
-            const uint32_t uba = masked(st) ? (uint32_t)ub : 0xffffffffu;
-            const int base = step_q0(st) - kjm;   // qi - kj of this lane's first row
+        auto s_step = [&](Pos ps, const DkdvTile &T, uint4 *pslot) {
+            const uint32_t uba = masked(ps) ? (uint32_t)ub : 0xffffffffu;
+            const int base = ps.q0 - kjm;   // qi - kj of this lane's first row
             constexpr int R = 2 * DK_AHEAD;
             bf16x8 ob[R];
 #pragma unroll
@@ -503,11 +520,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
                                   __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
             pslot[128 + lane] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
             pslot[192 + lane] = make_uint4(sw[4], sw[5], sw[6], sw[7]);
-            if (A.ds) stored = store_ds(st, sb);
+            if (A.ds) stored = store_ds(ps, sb);
         };
         auto stage = [&](int st, const DkdvTile &cur, DkdvTile &fill) {
-            stage_start(st, fill);
-            if (visible(st)) s_step(st, cur, pbuf[st & 1][kq]);
+            stage_start(fill);
+            if (visible(st, pc)) s_step(pc, cur, pbuf[st & 1][kq]);
+            stage_end(st);
         };
         // unrolled by three: the ring's buffers by name (stage st reads ring[st % 3], fills ring[(st+1) % 3])
         for (int st = 0; st <= nsteps; st += 3) {
@@ -524,6 +542,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         // ================= gradient waves (one step behind): dV^T += dO^T P and dK^T += Q'^T dS, with the
         // transposed operands read from the step's row tiles and P, dS from the score wave of these keys
         f32x16 dv[4], dk[6];
+        Pos pg = first;   // step st - 1
 #pragma unroll
         for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
 #pragma unroll
@@ -559,8 +578,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             }
         };
         auto stage = [&](int st, const DkdvTile &prev, DkdvTile &fill) {
-            stage_start(st, fill);
-            if (st >= 1 && visible(st - 1)) g_step(prev, pbuf[(st - 1) & 1][kq]);
+            stage_start(fill);
+            if (st >= 1 && visible(st - 1, pg)) g_step(prev, pbuf[(st - 1) & 1][kq]);
+            pg = pc;
+            stage_end(st);
         };
         // stage st reads ring[(st - 1) % 3] and fills ring[(st + 1) % 3]
         for (int st = 0; st <= nsteps; st += 3) {
