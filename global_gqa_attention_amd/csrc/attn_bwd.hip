@@ -293,17 +293,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int nsteps = nq * GS;
 
     // ---- direct HBM -> LDS loads of one step's tiles (fixed per-lane byte offsets + wave-uniform bases):
-    // q' rows by waves 0..5 (two 16-byte chunks per lane), dO rows by all eight waves (one each), LSE*log2e
-    // and D by waves 6 and 7 (eight lanes each)
+    // all by the gradient waves (4..7), which finish their MFMAs early in each stage, so that the score
+    // waves (the kernel's critical path) issue no loads: q' rows three 16-byte chunks per lane, dO rows two,
+    // LSE*log2e by wave 6 and D by wave 7 (eight lanes each)
     const size_t qr_row = (size_t)a.hq * DQK, o_row = (size_t)a.hq * DVV;
-    uint32_t o_qr[2];
+    const int gw = wave & 3;
+    uint32_t o_qr[3], o_or[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int slot = 384 * j + 64 * min(wave, 5) + lane, r = slot / QCH, p = slot % QCH;
+    for (int j = 0; j < 3; ++j) {
+        const int slot = 256 * j + 64 * gw + lane, r = slot / QCH, p = slot % QCH;
         o_qr[j] = (uint32_t)((r * qr_row + 8 * swz384t(r, p)) * 2);
     }
-    const int oslot_r = tid / OCH, oslot_p = tid % OCH;
-    const uint32_t o_or = (uint32_t)((oslot_r * o_row + 8 * swz256t(oslot_r, oslot_p)) * 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int slot = 256 * j + 64 * gw + lane, r = slot / OCH, p = slot % OCH;
+        o_or[j] = (uint32_t)((r * o_row + 8 * swz256t(r, p)) * 2);
+    }
     // step -> (head, query tile): heads outer, query tiles from the sequence end down.  Every key tile of a
     // sequence walks the same absolute query tiles in the same order, so the workgroups running together
     // on an XCD read the same q'/dO tiles and mostly hit in L2.  The stages walk the steps in order, so the
@@ -323,27 +328,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     };
     auto issue = [&](Pos ps, DkdvTile &T) {
         const int h = ps.h, q0 = ps.q0;
-        if (wave < 6) {
-            if (q0 + MQ <= A.qr_rows) {
-                const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
+        if (q0 + MQ <= A.qr_rows) {
+            const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) lds_dma16(bq, o_qr[j], T.qr + 384 * j + 64 * wave);
-            } else {
-                // a caller's q_rot has exactly T rows: rows past its end are clamped to the last (and masked)
+            for (int j = 0; j < 3; ++j) lds_dma16(bq, o_qr[j], T.qr + 256 * j + 64 * gw);
+        } else {
+            // a caller's q_rot has exactly T rows: rows past its end are clamped to the last (and masked)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int slot = 384 * j + 64 * min(wave, 5) + lane, r = slot / QCH, p = slot % QCH;
-                    const int row = min(q0 + r, A.qr_rows - 1);
-                    lds_dma16(A.W.qr + ((size_t)row * a.hq + h) * DQK + 8 * swz384t(r, p), T.qr + 384 * j + 64 * wave);
-                }
+            for (int j = 0; j < 3; ++j) {
+                const int slot = 256 * j + 64 * gw + lane, r = slot / QCH, p = slot % QCH;
+                const int row = min(q0 + r, A.qr_rows - 1);
+                lds_dma16(A.W.qr + ((size_t)row * a.hq + h) * DQK + 8 * swz384t(r, p), T.qr + 256 * j + 64 * gw);
             }
         }
         if (q0 + MQ <= a.T) {
-            lds_dma16(A.dout + ((size_t)q0 * a.hq + h) * DVV, o_or, T.orow + 64 * wave);
+            const u16 *bo = A.dout + ((size_t)q0 * a.hq + h) * DVV;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) lds_dma16(bo, o_or[j], T.orow + 256 * j + 64 * gw);
         } else {
             // dO is not padded: rows past its end are clamped to the last row (and masked)
-            const int row = min(q0 + oslot_r, a.T - 1);
-            lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256t(oslot_r, oslot_p), T.orow + 64 * wave);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int slot = 256 * j + 64 * gw + lane, r = slot / OCH, p = slot % OCH;
+                const int row = min(q0 + r, a.T - 1);
+                lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256t(r, p), T.orow + 256 * j + 64 * gw);
+            }
         }
         if (wave >= 6) {
             const float *bld = (wave == 6 ? A.lse2 : A.delta) + (size_t)h * A.T_pad + q0;
@@ -382,23 +391,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         return (const char *)tile_ + R * rowbytes + 16 * p + 8 * (m4 & 1);
     };
 
-    // ---- tile ring: at stage st the tiles of steps st (P waves) and st-1 (dS waves) are read and step
-    // st+1 is loaded: wait for this wave's loads (step st's tiles, issued one stage earlier; a dS wave's two
-    // dS stores of the previous stage may stay in flight, as vmcnt completes in issue order), make the P
-    // writes of the previous stage visible, barrier (every wave has landed its part and finished stage st-1;
-    // the buffer of step st-2 is free), load step st+1.  Every stage loads one tile set (the last step's
-    // again once the steps run out), so the waits stay uniform.  Both roles pass nsteps + 1 barriers.
-    issue(first, ring[0]);
-    bool stored = false;
+    // ---- tile ring: at stage st the tiles of steps st (score waves) and st-1 (gradient waves) are read and
+    // step st+1 is loaded: a gradient wave waits for its loads (step st's tiles, issued one stage earlier),
+    // every wave makes its P / dS writes of the previous stage visible, barrier (every gradient wave has
+    // landed its part, every wave has finished stage st-1, so the buffer of step st-2 is free), the
+    // gradient waves load step st+1.  Every stage loads one tile set (the last step's again once the steps
+    // run out), so the waits stay uniform.  Both roles pass nsteps + 1 barriers.  The score waves' dS
+    // stores need no wait (their data registers are the compiler's to protect).
+    if (role == 1) issue(first, ring[0]);
     // pc: step st, pn: step min(st + 1, nsteps - 1) (the one stage st loads)
     Pos pc = first, pn = nsteps > 1 ? advance(first) : first;
+    // a gradient wave waits for its loads of step st (issued one stage earlier), every wave makes its LDS
+    // writes of the previous stage visible, then the barrier; the gradient waves load step st + 1
     auto stage_start = [&](DkdvTile &fill) {
-        if (stored) wait_vmcnt<2>();
-        else wait_vmcnt<0>();
-        stored = false;
+        if (role == 1) wait_vmcnt<0>();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        issue(pn, fill);
+        if (role == 1) issue(pn, fill);
     };
     auto stage_end = [&](int st) {
         pc = pn;
@@ -520,7 +529,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
                                   __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
             pslot[128 + lane] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
             pslot[192 + lane] = make_uint4(sw[4], sw[5], sw[6], sw[7]);
-            if (A.ds) stored = store_ds(ps, sb);
+            if (A.ds) store_ds(ps, sb);
         };
         auto stage = [&](int st, const DkdvTile &cur, DkdvTile &fill) {
             stage_start(fill);
