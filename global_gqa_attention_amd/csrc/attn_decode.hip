@@ -76,13 +76,15 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
     const bool verify = A.k_new == nullptr;
     const int NC = G * A.nq;
     const int ngrp = (NC + 31) / 32;         // the columns in blocks of 32 MFMA columns
+    // workgroup order: KV head fastest, so that the one-wave workgroups of a row range's KV heads are
+    // dispatched together and the heads' slices of each cache row (one contiguous run) are fetched together
     int w = blockIdx.x;
+    const int kvh = w % A.hkv;
+    w /= A.hkv;
     const int split = w % A.splits;
     w /= A.splits;
     const int hgrp = w % ngrp;
-    w /= ngrp;
-    const int kvh = w % A.hkv;
-    const int b = w / A.hkv;
+    const int b = w / ngrp;
     if (b >= A.batch) return;
 
     int c0 = __builtin_amdgcn_readfirstlane(A.cu_cache[b]);
