@@ -410,12 +410,13 @@ __global__ __launch_bounds__(64 * VNW, 2) void verify_split_kernel(const DecodeA
     const int NC = G * A.nq;
     const int ngrp = (NC + 31) / 32;         // the columns in blocks of 32 MFMA columns
     (void)ngrp;                              // one wave per block of 32 columns (at most VNW blocks)
+    // workgroup order: KV head fastest (the heads' slices of each cache row are fetched together)
     int w = blockIdx.x;
-    const int split = w % A.splits;
-    w /= A.splits;
-    const int hgrp = wave;
     const int kvh = w % A.hkv;
-    const int b = w / A.hkv;
+    w /= A.hkv;
+    const int split = w % A.splits;
+    const int hgrp = wave;
+    const int b = w / A.splits;
     if (b >= A.batch) return;
 
     int c0 = __builtin_amdgcn_readfirstlane(A.cu_cache[b]);
