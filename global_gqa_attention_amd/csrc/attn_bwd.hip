@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void row_prep_kernel(const u16 *x, int H, u16 
 {
     __shared__ __attribute__((aligned(16))) u16 sX[64 * (D + 8)];
     constexpr int CH = D / 8;
-    const int tid = threadIdx.x, h = blockIdx.y, t0 = blockIdx.x * 64;
+    const int tid = threadIdx.x, h = blockIdx.x % H, t0 = (blockIdx.x / H) * 64;   // heads fastest
     // load (and rotate) 64 rows: thread handles row tid/4, chunks cg, cg+4, cg+8, ...
     {
         const int rr = tid >> 2, cg = tid & 3, t = t0 + rr;
@@ -1144,8 +1144,9 @@ hipError_t launch_dq(const BwdArgs &A, hipStream_t stream)
 template <int D, bool ROPE>
 hipError_t launch_row_prep(const u16 *x, int H, u16 *rm, u16 *tr, const LayerArgs &a, int T_pad, hipStream_t stream)
 {
-    dim3 grid((T_pad + 63) / 64, H);
-    row_prep_kernel<D, ROPE><<<grid, 256, 0, stream>>>(x, H, rm, tr, a, T_pad);
+    const long grid = (long)((T_pad + 63) / 64) * H;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    row_prep_kernel<D, ROPE><<<(unsigned)grid, 256, 0, stream>>>(x, H, rm, tr, a, T_pad);
     return hipGetLastError();
 }
 

@@ -39,8 +39,8 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const LayerArgs a, KVPrep 
 {
     __shared__ __attribute__((aligned(16))) u16 sV[PT * (DVV + 8)];
     const int tid = threadIdx.x;
-    const int kvh = blockIdx.y;
-    const int t0 = blockIdx.x * PT;
+    const int kvh = blockIdx.x % a.hkv;            // KV head fastest: a token's heads are one contiguous run
+    const int t0 = (blockIdx.x / a.hkv) * PT;
 
     // ---- K: token t0 + tid/4, chunk group tid%4 (chunks cg, cg+4 rotated; 8+cg+4i copied)
     {
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, 
 {
     __shared__ __attribute__((aligned(16))) u16 sV[PT * (DVV + 8)];
     const int tid = threadIdx.x;
-    const int kvh = blockIdx.y;
-    const int t0 = blockIdx.x * PT;
+    const int kvh = blockIdx.x % a.hkv;            // KV head fastest: a token's heads are one contiguous run
+    const int t0 = (blockIdx.x / a.hkv) * PT;
     const int Tk = a.T + C.Tc;
     // source rows of key u: (K row, V row, rotation position or -1 for a cache row).  Returns false when the
     // index arrays do not account for key u (their totals disagree with T and Tc): the key is then zero-filled
@@ -221,7 +221,7 @@ void prep_carve(void *ws, int T, int hkv, KVPrep *p)
 
 hipError_t launch_kv_prep_cached(const LayerArgs &a, const KVPrep &p, const CacheArgs &c, hipStream_t stream)
 {
-    dim3 grid((p.T_pad + PT - 1) / PT, a.hkv);
+    const unsigned grid = (unsigned)((p.T_pad + PT - 1) / PT) * (unsigned)a.hkv;
     trace_begin(a.window >= 0 ? "kv_prep_cached_swa" : "kv_prep_cached_global", stream);
     kv_prep_cached_kernel<<<grid, 256, 0, stream>>>(a, p, c);
     trace_end(stream);
@@ -230,7 +230,7 @@ hipError_t launch_kv_prep_cached(const LayerArgs &a, const KVPrep &p, const Cach
 
 hipError_t launch_kv_prep(const LayerArgs &a, const KVPrep &p, hipStream_t stream)
 {
-    dim3 grid((p.T_pad + PT - 1) / PT, a.hkv);
+    const unsigned grid = (unsigned)((p.T_pad + PT - 1) / PT) * (unsigned)a.hkv;
     trace_begin(a.window >= 0 ? "kv_prep_swa" : "kv_prep_global", stream);
     kv_prep_kernel<<<grid, 256, 0, stream>>>(a, p);
     trace_end(stream);
