@@ -68,7 +68,9 @@ __device__ __forceinline__ int tperm16(int t)
 // spreads the dQ kernel's transposed reads over all LDS banks; each plane is one whole store).  Query tiles of sequence b
 // start at S16 = seq_start & ~15 (tile n: S16 + 32 n ..), key blocks at seq_start (block k: seq_start +
 // 32 k ..).  Row n of a sequence holds the key blocks k_lo(n) .. k_hi(n) that tile n sees: causal rows
-// have n + 1 slots, sliding-window rows ds_row_width(window) slots.
+// have n + 1 slots, sliding-window rows ds_row_width(window) slots.  Slot s of all sequences' rows is
+// numbered ds_index[b] + rows before n + (k - k_lo(n)), and the query heads are the innermost index: block
+// (slot, h) sits at slot * hq + h, so the dQ kernel's NH heads of one step read one contiguous run.
 // ------------------------------------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int ds_row_width(int window) { return (window + 62) / 32 + 1; }
 __device__ __forceinline__ int ds_nq(int seq_start, int seq_end)
@@ -451,12 +453,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         // dS of a step into the stored-dS blocks (query tile n, key block 4 tile + kq; see ds_row_width)
         const int s16 = seq_start & ~15;
         const int kap = 4 * tile + kq;
-        const int64_t ds_head = A.ds ? A.ds_index[a.batch] : 0, ds_seq = A.ds ? A.ds_index[bseq] : 0;
+        const int64_t ds_seq = A.ds ? A.ds_index[bseq] : 0;
         auto store_ds = [&](Pos ps, const bf16x8 *sb) {
             const int h = ps.h, q0 = ps.q0;
             const int n = (q0 - s16) >> 5;
-            const int64_t blk = (int64_t)h * ds_head + ds_seq + ds_rows_before(n, a.window) +
-                                (kap - ds_klo(q0, seq_start, a.window));
+            const int64_t blk = (ds_seq + ds_rows_before(n, a.window) + (kap - ds_klo(q0, seq_start, a.window))) *
+                                    a.hq + h;
             if (blk >= A.ds_cap) return false;   // only with a max_seqlen below the longest sequence
             // streaming stores (the blocks are read back by another kernel); plane P holds sb[P] of every lane
             // at row (lane ^ 8 hh ^ 4 P): each store writes a whole 1 KB plane
@@ -1009,7 +1011,7 @@ __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A
     const int klo = ds_klo(q0, seq_start, a.window);
     const int khi = min(q0 + 31 - seq_start, seq_end - 1 - seq_start) >> 5;
     const int nsteps = khi - klo + 1;
-    const int64_t blk0 = (int64_t)h * A.ds_index[a.batch] + A.ds_index[bseq] + ds_rows_before(n, a.window);
+    const int64_t blk0 = (A.ds_index[bseq] + ds_rows_before(n, a.window)) * a.hq + h;   // step 0's block
     const u16 *ds_row = A.ds + blk0 * 1024;
 
     // ---- loads of one key block: k' rows (swizzled 16-byte chunks) and this wave's dS block
@@ -1028,7 +1030,7 @@ __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A
             for (int j = 0; j < KL; ++j) lds_dma16(bk, o_kr[j], T.kr + 64 * KW * j + 64 * wave);
         }
         // (a block index past the workspace only arises from a max_seqlen below the truth: read block 0)
-        const u16 *bd = blk0 + step < A.ds_cap ? ds_row + (size_t)step * 1024 : A.ds;
+        const u16 *bd = blk0 + (int64_t)step * a.hq < A.ds_cap ? ds_row + (size_t)step * a.hq * 1024 : A.ds;
         lds_dma16_nt(bd, (uint32_t)(16 * lane), T.ds[wave]);
         lds_dma16_nt(bd, (uint32_t)(16 * (64 + lane)), T.ds[wave] + 64);
     };
