@@ -56,11 +56,11 @@ __device__ __forceinline__ int vpos(int d, int q) { return BN == 64 ? swz128(d, 
 // an LDS instruction's offset field, which costs address registers this wave cannot spare).  Sliding-window
 // layers: 4 waves, 32-key tiles double-buffered (40 KB) and KA = 4 so that three workgroups fit on a CU (OCC):
 // these short work items wait mostly on HBM (Q and the first tiles), and more resident workgroups keep more
-// loads in flight.  Sliding-window q passes through LDS first (48 KB at the start of the pool): a lane that
-// loads its own row touches 32 rows per load instruction, while the copy into LDS reads whole runs of rows
-// per instruction; the rotated q for the backward leaves the same way.  The 12-wave causal form has no room
-// to stage its 144 KB of q and loads each lane's row directly (once per work item).  After the key loop, O
-// leaves through LDS in both forms.
+// loads in flight.  q passes through LDS first in both forms: a lane that loads its own row touches 32 rows
+// per load instruction, while the copy into LDS reads whole runs of rows per instruction; the rotated q for
+// the backward leaves the same way.  Sliding window: 48 KB at the start of the pool, the first tile issued
+// after it.  Causal: 144 KB behind the first K tile (156 KB of the CU's 160 KB), that tile's V^T issued once
+// every wave has read its q.  After the key loop, O leaves through LDS in both forms.
 template <int NW, int GP, bool SINK, bool WIN, int BN, int KA, int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
 {
@@ -71,13 +71,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
     constexpr int VLOADS = DVV * VCH / NT;     // ... per V^T tile (every thread)
     constexpr int VEXTRA = DVV * VCH - VLOADS * NT;   // V^T chunks left over: one more for threads below this
     static_assert(KLOADS * NT == BN * KCH && VEXTRA % 64 == 0, "tile split");
-    constexpr bool QREG = NW > 8;              // q straight into registers (no room to stage 12 waves' rows)
     const LayerArgs &a = A.L;
     constexpr int NBUF = NW >= 8 ? 3 : 2;      // LDS stages: three where one workgroup owns the CU
     constexpr int KS = BN * KCH, VS = DVV * VCH;                 // 16-byte chunks of a K and a V^T tile
     // the workgroup's q rows pass through LDS first: sliding window from the start of the pool (the first
-    // tile is issued after them), causal behind the first tile's buffer (the first tile is in flight meanwhile)
-    constexpr int QOFF = WIN ? 0 : KS + VS, QEND = QREG ? 0 : QOFF + BM * KCH;
+    // tile is issued after them), causal behind the first K tile (in flight meanwhile; its V^T comes after)
+    constexpr int QOFF = WIN ? 0 : KS, QEND = QOFF + BM * KCH;
     constexpr int OSTAGE = BM * DVV / 8;                          // the epilogue's O rows (16-byte chunks)
     constexpr int POOL0 = NBUF * (KS + VS) > QEND ? NBUF * (KS + VS) : QEND;
     constexpr int POOL = POOL0 > OSTAGE ? POOL0 : OSTAGE;
@@ -169,7 +168,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
             wait_vmcnt<KLOADS + VLOADS>();
         }
     };
-    if constexpr (!WIN) issue_tile(kstart, sK0, sV0);
+    auto issue_v = [&](int k0, uint4 *sv) {
+        const u16 *vb = vt_base + k0;
+#pragma unroll
+        for (int j = 0; j < VLOADS; ++j) lds_dma16(vb, voff[j], sv + NT * j + 64 * wave);
+        if constexpr (VEXTRA > 0) {
+            if (wave < VEXTRA / 64) lds_dma16(vb, vextra, sv + NT * VLOADS + 64 * wave);
+        }
+    };
+    if constexpr (!WIN) {
+        const u16 *kb = kr_base + (size_t)kstart * kr_row;
+#pragma unroll
+        for (int j = 0; j < KLOADS; ++j) lds_dma16(kb, koff[j], sK0 + NT * j + 64 * wave);
+    }
 
     // ---- this lane's query row, rotated in registers
     const int r = wave * 32 + c;
@@ -184,25 +195,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         // the wave's 32 rows (768 16-byte chunks, GP-row runs contiguous in memory) are copied into LDS by
         // whole runs, chunk slot g by instruction g / 64, swizzled like a K tile; each lane then reads its
         // own row and rotates it.  The rotated q for the backward leaves the same way: the rotated chunks go
-        // back into their slots and each instruction stores whole runs.  The next K/V tile is issued into
-        // this LDS once every wave is done with its q (sliding window: the first tile; causal: the second,
-        // the first being in flight meanwhile in its own buffer).
-        if constexpr (QREG) {
-            // each lane loads its own row (12 16-byte pieces), rotates dims 0..63 and, for the backward,
-            // stores the rotated row
-            const u16 *qp = a.q + ((size_t)qtl * a.hq + qh) * DQK + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 12; ++s) qf[s] = ld16(qp + 16 * s);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                c0[t] = cs[t];
-                c1[t] = cs[16 + t];
-            }
-            rope_pair(qf[0], qf[2], c0);
-            rope_pair(qf[1], qf[3], c1);
-            // (the rotated q for the backward is stored at the end: stores issued here would sit in the
-            // same vmcnt queue as the first tiles' copies and delay the ring's waits)
-        } else {
+        // back into their slots and each instruction stores whole runs.  Once every wave is done with its
+        // q, the loads that this LDS waited for are issued (sliding window: the first tile; causal: the
+        // first tile's V^T, then the second tile).
         const u16 *qbase = a.q + ((size_t)t0 * a.hq + h0) * DQK;
         uint4 *qs = lds + QOFF + 32 * KCH * wave;
 #pragma unroll
@@ -234,10 +229,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
                     st16u(A.q_rot + ((size_t)tok * a.hq + h0 + rr % GP) * DQK + 8 * kpos(rw, g % KCH), x);
             }
         }
-        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         if constexpr (WIN) issue_tile(kstart, sK0, sV0);
+        else issue_v(kstart, sV0);
     }
 
     // this wave's rows sit at key indices [wt0, wt1]; 32-key blocks outside [wklo, wkhi] are skipped
@@ -422,13 +417,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
             const int g = 64 * j + ln, rw = g >> 4, p = g & 15, r = wave * 32 + rw;
             const uint4 x = ws[16 * rw + (p ^ (rw & 15))];
             if (t0 + r / GP < seq_end) st16u(obase + (uint32_t)(((r / GP) * a.hq + r % GP) * DVV + 8 * p), x);
-        }
-    }
-    if constexpr (QREG) {
-        if (A.q_rot && qvalid) {
-            u16 *qr = A.q_rot + ((size_t)qt * a.hq + qh) * DQK + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < 12; ++s) st16(qr + 16 * s, qf[s]);
         }
     }
 }
