@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A)
         float s = 0.f;
         if (t < T && h < hq) {
             const size_t r = (size_t)t * hq + h;
-            const bf16x8 x = ld16(A.dout + r * DVV + 8 * sub);
-            const bf16x8 y = ld16(A.out + r * DVV + 8 * sub);
+            const bf16x8 x = ld16_nt(A.dout + r * DVV + 8 * sub);
+            const bf16x8 y = ld16_nt(A.out + r * DVV + 8 * sub);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s += bf2f(x[e]) * bf2f(y[e]);
         }
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void row_prep_kernel(const u16 *x, int H, u16 
         const u16 *src = x + ((size_t)t * H + h) * D;
 #pragma unroll
         for (int i = 0; i < CH / 4; ++i)
-            v[i] = t < a.T ? ld16(src + 8 * (cg + 4 * i)) : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+            v[i] = t < a.T ? ld16_nt(src + 8 * (cg + 4 * i)) : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
         if (ROPE && t < a.T) {
             const int pos = t - seq_start_of(a.cu, a.batch, t);
             const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;
@@ -686,13 +686,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             for (int j = 0; j < 12; ++j) {
                 const int g = 64 * j + lane, r = g / QCH, p = g % QCH, k = (p & ~7) | ((p & 7) ^ (r & 7));
                 const uint4 x = kst[g];
-                if (kw0 + r <= kb_last) st16u(A.dk + ((size_t)(kw0 + r) * a.hkv + kvh) * DQK + 8 * k, x);
+                if (kw0 + r <= kb_last) st16u_nt(A.dk + ((size_t)(kw0 + r) * a.hkv + kvh) * DQK + 8 * k, x);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int g = 64 * j + lane, r = g >> 4, p = g & 15, k = p ^ (r & 15);
                 const uint4 x = vst[g];
-                if (kw0 + r <= kb_last) st16u(A.dv + ((size_t)(kw0 + r) * a.hkv + kvh) * DVV + 8 * k, x);
+                if (kw0 + r <= kb_last) st16u_nt(A.dv + ((size_t)(kw0 + r) * a.hkv + kvh) * DVV + 8 * k, x);
             }
         }
     }
@@ -718,8 +718,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(const BwdArgs A)
     bf16x8 w;
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = f2bf(acc[e]);
-    if (c8 < DQK / 8) st16(A.dk + ((size_t)t * A.L.hkv + kvh) * DQK + 8 * c8, w);
-    else st16(A.dv + ((size_t)t * A.L.hkv + kvh) * DVV + 8 * (c8 - DQK / 8), w);
+    if (c8 < DQK / 8) st16u_nt(A.dk + ((size_t)t * A.L.hkv + kvh) * DQK + 8 * c8, __builtin_bit_cast(uint4, w));
+    else st16u_nt(A.dv + ((size_t)t * A.L.hkv + kvh) * DVV + 8 * (c8 - DQK / 8), __builtin_bit_cast(uint4, w));
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -958,7 +958,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
         const int g = 64 * j + lane, rw = g / KCH, p = g % KCH, k = (p & ~7) | ((p & 7) ^ (rw & 7));
         const int r = wave * 32 + rw, tok = t0 + r / GP;
         const uint4 x = stg[g];
-        if (tok < seq_end) st16u(A.dq + ((size_t)tok * a.hq + h0 + r % GP) * DQK + 8 * k, x);
+        if (tok < seq_end) st16u_nt(A.dq + ((size_t)tok * a.hq + h0 + r % GP) * DQK + 8 * k, x);
     }
 }
 
@@ -1119,7 +1119,7 @@ __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A
         const int g = 64 * NH * j + tid, R = g / KCH, k = g % KCH, qc = R / NH, w = R % NH;
         const uint4 x = stg[R * KCH + ((k & ~7) | ((k & 7) ^ (qc & 7)))];
         if (q0 + qc >= seq_start && q0 + qc < seq_end)
-            st16u(A.dq + ((size_t)(q0 + qc) * a.hq + h0 + w) * DQK + 8 * k, x);
+            st16u_nt(A.dq + ((size_t)(q0 + qc) * a.hq + h0 + w) * DQK + 8 * k, x);
     }
 }
 

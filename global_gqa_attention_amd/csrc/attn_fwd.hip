@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         for (int i = 0; i < 12; ++i) {
             const int g = 64 * i + lane, rw = g / KCH, rr = wave * 32 + rw;
             const int tk = min(rr / GP, t_last - t0);
-            lds_dma16(qbase, (uint32_t)(((tk * a.hq + rr % GP) * DQK + 8 * kpos(rw, g % KCH)) * 2), qs + 64 * i);
+            lds_dma16_nt(qbase, (uint32_t)(((tk * a.hq + rr % GP) * DQK + 8 * kpos(rw, g % KCH)) * 2), qs + 64 * i);
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
                 const int tok = t0 + rr / GP;
                 const uint4 x = qs[g];
                 if (tok < seq_end)
-                    st16u(A.q_rot + ((size_t)tok * a.hq + h0 + rr % GP) * DQK + 8 * kpos(rw, g % KCH), x);
+                    st16u_nt(A.q_rot + ((size_t)tok * a.hq + h0 + rr % GP) * DQK + 8 * kpos(rw, g % KCH), x);
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
         for (int j = 0; j < 8; ++j) {
             const int g = 64 * j + ln, rw = g >> 4, p = g & 15, r = wave * 32 + rw;
             const uint4 x = ws[16 * rw + (p ^ (rw & 15))];
-            if (t0 + r / GP < seq_end) st16u(obase + (uint32_t)(((r / GP) * a.hq + r % GP) * DVV + 8 * p), x);
+            if (t0 + r / GP < seq_end) st16u_nt(obase + (uint32_t)(((r / GP) * a.hq + r % GP) * DVV + 8 * p), x);
         }
     }
 }

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const LayerArgs a, KVPrep 
         u16 *dst = p.kr + ((size_t)t * a.hkv + kvh) * DQK;
         if (t < a.T) {
             const u16 *src = a.k + ((size_t)t * a.hkv + kvh) * DQK;
-            bf16x8 x0 = ld16(src + 8 * cg), x1 = ld16(src + 8 * (cg + 4));
+            bf16x8 x0 = ld16_nt(src + 8 * cg), x1 = ld16_nt(src + 8 * (cg + 4));
             const int pos = t - seq_start_of(a.cu, a.batch, t);
             const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;
             float2 c8[8];
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const LayerArgs a, KVPrep 
             st16(dst + 8 * cg, x0);
             st16(dst + 8 * (cg + 4), x1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), ldu4(src + 8 * (8 + cg + 4 * i)));
+            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), ldu4_nt(src + 8 * (8 + cg + 4 * i)));
         } else if (t < p.T_pad) {
             const uint4 z = make_uint4(0, 0, 0, 0);
             st16u(dst + 8 * cg, z);
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const LayerArgs a, KVPrep 
         for (int i = 0; i < 4; ++i) {
             const int ch = cg + 4 * i;
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (t < a.T) x = ldu4(a.v + ((size_t)t * a.hkv + kvh) * DVV + 8 * ch);
+            if (t < a.T) x = ldu4_nt(a.v + ((size_t)t * a.hkv + kvh) * DVV + 8 * ch);
             *(uint4 *)(sV + r * (DVV + 8) + 8 * ch) = x;
         }
     }
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, 
         const u16 *src = nullptr, *vs = nullptr;
         int pos = 0;
         if (u < Tk && source(u, src, vs, pos)) {
-            bf16x8 x0 = ld16(src + 8 * cg), x1 = ld16(src + 8 * (cg + 4));
+            bf16x8 x0 = ld16_nt(src + 8 * cg), x1 = ld16_nt(src + 8 * (cg + 4));
             if (pos >= 0) {
                 const float2 *cs = a.rope + (size_t)min(pos, a.rope_len - 1) * NHALF + 8 * cg;   // pos >= 0 here
                 float2 c8[8];
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, 
             st16(dst + 8 * cg, x0);
             st16(dst + 8 * (cg + 4), x1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), ldu4(src + 8 * (8 + cg + 4 * i)));
+            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), ldu4_nt(src + 8 * (8 + cg + 4 * i)));
         } else if (u < p.T_pad) {
             const uint4 z = make_uint4(0, 0, 0, 0);
             st16u(dst + 8 * cg, z);
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void kv_prep_cached_kernel(const LayerArgs a, 
         for (int i = 0; i < 4; ++i) {
             const int ch = cg + 4 * i;
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (have) x = ldu4(vs + 8 * ch);
+            if (have) x = ldu4_nt(vs + 8 * ch);
             *(uint4 *)(sV + r * (DVV + 8) + 8 * ch) = x;
         }
     }
