@@ -234,8 +234,9 @@ def setup_layers(ga, torch, mi, dev):
         g["max_seqlen"] = max(d["lengths"])
         g["out"] = torch.empty(T, hq, 128, dtype=torch.bfloat16, device=dev)
         g["lse"] = torch.empty(hq, T, dtype=torch.float32, device=dev)
-        # the forward's rotated q, handed to the backward (a training step keeps it like out and lse)
+        # the forward's rotated q and k, handed to the backward (a training step keeps them like out and lse)
         g["q_rot"] = torch.empty(T, hq, 192, dtype=torch.bfloat16, device=dev)
+        g["k_rot"] = torch.empty(T, hkv, 192, dtype=torch.bfloat16, device=dev)
         g["grads"] = (torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"]),
                       torch.empty(hq, dtype=torch.float32, device=dev) if g["sink"] is not None else None)
         # the workspace that keeps the dS blocks (the dQ kernel reads them back instead of recomputing)
@@ -250,9 +251,10 @@ def setup_layers(ga, torch, mi, dev):
     def step():
         for g in layers.values():
             ga.fwd(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], g["max_seqlen"], g["window"], g["rope_base"],
-                   out=g["out"], lse=g["lse"], q_rot=g["q_rot"])
+                   out=g["out"], lse=g["lse"], q_rot=g["q_rot"], k_rot=g["k_rot"])
             ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], dout, g["cu_seqlens"], g["max_seqlen"],
-                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"], q_rot=g["q_rot"])
+                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"], q_rot=g["q_rot"],
+                   k_rot=g["k_rot"])
 
     return thd, dout_cpu, layers, step
 
@@ -494,7 +496,7 @@ def run_bwd_paths(ga, torch, layers, reps=10):
         for path, ws in (("stored_dS", g["ws"]), ("least", least)):
             call = lambda: ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], g["dout"], g["cu_seqlens"],  # noqa
                                   g["max_seqlen"], g["window"], g["rope_base"], workspace=ws, grads=g["grads"],
-                                  q_rot=g["q_rot"])
+                                  q_rot=g["q_rot"], k_rot=g["k_rot"])
             for _ in range(2):
                 call()
             torch.cuda.synchronize()
@@ -583,6 +585,7 @@ def run_shards(ga, torch, thd, dout_cpu, steps=5):
         g["out"] = torch.empty(T, 16, 128, dtype=torch.bfloat16, device=dev)
         g["lse"] = torch.empty(16, T, dtype=torch.float32, device=dev)
         g["q_rot"] = torch.empty(T, 16, 192, dtype=torch.bfloat16, device=dev)
+        g["k_rot"] = torch.empty(T, hkv, 192, dtype=torch.bfloat16, device=dev)
         g["grads"] = (torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"]),
                       torch.empty(16, dtype=torch.float32, device=dev) if g["sink"] is not None else None)
         g["ws"] = torch.empty(ga.bwd_workspace_size(T, 16, hkv, g["window"], len(d["lengths"]), g["max_seqlen"]),
@@ -594,9 +597,10 @@ def run_shards(ga, torch, thd, dout_cpu, steps=5):
     def step():
         for g in layers.values():
             ga.fwd(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], g["max_seqlen"], g["window"], g["rope_base"],
-                   out=g["out"], lse=g["lse"], q_rot=g["q_rot"])
+                   out=g["out"], lse=g["lse"], q_rot=g["q_rot"], k_rot=g["k_rot"])
             ga.bwd(g["q"], g["k"], g["v"], g["sink"], g["out"], g["lse"], dout, g["cu_seqlens"], g["max_seqlen"],
-                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"], q_rot=g["q_rot"])
+                   g["window"], g["rope_base"], workspace=g["ws"], grads=g["grads"], q_rot=g["q_rot"],
+                   k_rot=g["k_rot"])
     for _ in range(2):
         step()
     torch.cuda.synchronize()

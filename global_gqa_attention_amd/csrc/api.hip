@@ -220,8 +220,8 @@ void mimo_attn_release(void)
 mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
-                            int32_t n_kv_heads, void *out, float *lse, void *q_rot, void *workspace,
-                            size_t workspace_bytes, void *stream)
+                            int32_t n_kv_heads, void *out, float *lse, void *q_rot, void *k_rot,
+                            void *workspace, size_t workspace_bytes, void *stream)
 {
     mimo_status_t s = check_layer(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, window, rope_base,
                                   n_q_heads, n_kv_heads);
@@ -238,6 +238,7 @@ mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const f
     hipStream_t st = (hipStream_t)stream;
     mimo::FwdArgs a{};
     mimo::prep_carve(workspace, total_tokens, n_kv_heads, &a.P);
+    a.P.k_rot = (uint16_t *)k_rot;
     s = rope_table(rope_base, max_seqlen, st, &a.L.rope, &a.L.rope_len);
     if (s != MIMO_OK) return s;
     a.L.q = (const uint16_t *)q;
@@ -400,7 +401,7 @@ size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, in
 
 mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const float *sink,
                             const void *out, const float *lse, const void *dout, const void *q_rot,
-                            const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
+                            const void *k_rot, const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
                             int32_t n_kv_heads, void *dq, void *dk, void *dv, float *dsink,
                             void *workspace, size_t workspace_bytes, void *stream)
@@ -457,6 +458,12 @@ mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const f
     if (q_rot) {   // the forward's rotated q replaces the workspace copy (read only)
         a.W.qr = (uint16_t *)q_rot;
         a.qr_rows = total_tokens;
+    }
+    a.kr_rows = a.T_pad;
+    a.kr_given = k_rot != nullptr && stored_ds;
+    if (a.kr_given) {   // the forward's rotated k replaces the workspace's row copy (read only)
+        a.W.kr = (uint16_t *)k_rot;
+        a.kr_rows = total_tokens;
     }
     if (stored_ds) a.ds_cap = (int64_t)((ds_need - (size_t)((char *)a.ds - (char *)workspace)) / 2048);
     hipError_t e = mimo::launch_bwd(a, st);

@@ -1026,8 +1026,20 @@ __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A
         const int kb = seq_start + 32 * (klo + step);
         const u16 *bk = A.W.kr + ((size_t)kb * a.hkv + kvh) * DQK;
         if (wave < KW) {
+            if (kb + 32 <= A.kr_rows) {
 #pragma unroll
-            for (int j = 0; j < KL; ++j) lds_dma16(bk, o_kr[j], T.kr + 64 * KW * j + 64 * wave);
+                for (int j = 0; j < KL; ++j) lds_dma16(bk, o_kr[j], T.kr + 64 * KW * j + 64 * wave);
+            } else {
+                // a caller's k_rot has exactly T rows: rows past its end are clamped to the last (their dS
+                // entries are zero)
+#pragma unroll
+                for (int j = 0; j < KL; ++j) {
+                    const int slot = 64 * KW * j + 64 * wave + lane, r = slot / KCH, p = slot % KCH;
+                    const int row = min(kb + r, A.kr_rows - 1);
+                    lds_dma16(A.W.kr + ((size_t)row * a.hkv + kvh) * DQK + 8 * (p ^ (((r >> 1) & 1) << 2)),
+                              T.kr + 64 * KW * j + 64 * wave);
+                }
+            }
         }
         // (a block index past the workspace only arises from a max_seqlen below the truth: read block 0)
         const u16 *bd = blk0 + (int64_t)step * a.hq < A.ds_cap ? ds_row + (size_t)step * a.hq * 1024 : A.ds;
@@ -1256,11 +1268,13 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
         trace_end(stream);
         if (e != hipSuccess) return e;
     }
-    trace_begin(a.window >= 0 ? "bwd_prep_k_swa" : "bwd_prep_k_global", stream);
-    // the transposed k' copy serves only the dQ kernel that recomputes S and dP (least workspace)
-    e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.ds ? nullptr : A.W.krt, a, A.T_pad, stream);
-    trace_end(stream);
-    if (e != hipSuccess) return e;
+    if (!A.kr_given) {
+        trace_begin(a.window >= 0 ? "bwd_prep_k_swa" : "bwd_prep_k_global", stream);
+        // the transposed k' copy serves only the dQ kernel that recomputes S and dP (least workspace)
+        e = launch_row_prep<DQK, true>(a.k, a.hkv, A.W.kr, A.ds ? nullptr : A.W.krt, a, A.T_pad, stream);
+        trace_end(stream);
+        if (e != hipSuccess) return e;
+    }
 
     if (A.ds) {
         trace_begin(a.window >= 0 ? "bwd_ds_index_swa" : "bwd_ds_index_global", stream);

@@ -55,10 +55,20 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const LayerArgs a, KVPrep 
 #pragma unroll
             for (int i = 0; i < 8; ++i) c8[i] = cs[i];
             rope_pair(x0, x1, c8);
+            uint4 rest[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rest[i] = ldu4_nt(src + 8 * (8 + cg + 4 * i));
             st16(dst + 8 * cg, x0);
             st16(dst + 8 * (cg + 4), x1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), ldu4_nt(src + 8 * (8 + cg + 4 * i)));
+            for (int i = 0; i < 4; ++i) st16u(dst + 8 * (8 + cg + 4 * i), rest[i]);
+            if (p.k_rot) {   // the rotated rows once more, for the backward
+                u16 *kd = p.k_rot + ((size_t)t * a.hkv + kvh) * DQK;
+                st16u_nt(kd + 8 * cg, __builtin_bit_cast(uint4, x0));
+                st16u_nt(kd + 8 * (cg + 4), __builtin_bit_cast(uint4, x1));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st16u_nt(kd + 8 * (8 + cg + 4 * i), rest[i]);
+            }
         } else if (t < p.T_pad) {
             const uint4 z = make_uint4(0, 0, 0, 0);
             st16u(dst + 8 * cg, z);
@@ -214,6 +224,7 @@ size_t prep_bytes(int T, int hkv)
 void prep_carve(void *ws, int T, int hkv, KVPrep *p)
 {
     p->T_pad = prep_tpad(T);
+    p->k_rot = nullptr;
     p->kr = (uint16_t *)ws;
     const size_t kr = ((size_t)p->T_pad * hkv * DQK * 2 + 255) & ~(size_t)255;
     p->vt = (uint16_t *)((char *)ws + kr);

@@ -19,6 +19,7 @@ struct LayerArgs {
 struct KVPrep {
     uint16_t *kr;                  // bf16 [T_pad, hkv, 192]: K with RoPE applied
     uint16_t *vt;                  // bf16 [hkv, 128, T_pad]: V transposed, 4-token chunks permuted
+    uint16_t *k_rot;               // bf16 [T, hkv, 192]: a copy of kr's first T rows for the caller, or nullptr
     int T_pad;                     // tokens rounded up to 16, plus 64 zero-filled
 };
 inline int prep_tpad(int T) { return (T + 15) / 16 * 16 + 64; }
@@ -79,6 +80,8 @@ struct BwdArgs {
     int T_pad;
     int qr_rows;                   // rows of W.qr that may be read: T_pad (prepared here) or T (the caller's)
     bool qr_given;                 // W.qr is the forward's q_rot: no prep pass for q
+    int kr_rows;                   // rows of W.kr that may be read: T_pad (prepared here) or T (the caller's)
+    bool kr_given;                 // W.kr is the forward's k_rot: no prep pass for k
     int splits;                    // query heads of a group are split over this many key-tile workgroups
     // stored-dS path (nullptr: dQ recomputes S and dP): the dK/dV kernel writes every 32 x 32 bf16 block of
     // dS it computes, the dQ kernel reads them back.  ds_index[b] = first block of sequence b within a head,

@@ -63,6 +63,8 @@ typedef enum {
  *   q_rot bf16 [total_tokens, n_q_heads, 192] or NULL: when given, receives q with RoPE applied, exactly
  *         the values the scores use; a training caller passes it on to mimo_attn_bwd, which then skips
  *         rotating q again
+ *   k_rot bf16 [total_tokens, n_kv_heads, 192] or NULL: when given, receives k with RoPE applied (the keys
+ *         the scores use), for mimo_attn_bwd in the same way
  *   workspace: device memory of at least mimo_attn_fwd_workspace_size() bytes, owned by the caller; needs
  *   no initialisation and must not be shared with a concurrent call.
  * Source: miles docs "MiMo-V2.6-Flash" sections 1, 5.1, 5.4; miles PR "feat(models): add MiMo-V2.6-Flash-RL
@@ -70,8 +72,8 @@ typedef enum {
 mimo_status_t mimo_attn_fwd(const void *q, const void *k, const void *v, const float *sink,
                             const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
-                            int32_t n_kv_heads, void *out, float *lse, void *q_rot, void *workspace,
-                            size_t workspace_bytes, void *stream);
+                            int32_t n_kv_heads, void *out, float *lse, void *q_rot, void *k_rot,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace mimo_attn_fwd needs: RoPE-rotated K and per-head transposed V (about
  * 640 * n_kv_heads bytes per token), which the kernels then stream from HBM straight into LDS. */
@@ -100,6 +102,9 @@ size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, in
  *   dout  bf16 [total_tokens, n_q_heads, 128]  upstream gradient dO
  *   q_rot bf16 [total_tokens, n_q_heads, 192]  the forward's q_rot output for these q and positions, or
  *         NULL (the backward then rotates q itself into the workspace); read only
+ *   k_rot bf16 [total_tokens, n_kv_heads, 192]  the forward's k_rot output for these k and positions, or
+ *         NULL; read only.  The stored-dS path then reads it instead of rotating k into the workspace (the
+ *         least-workspace path needs a transposed copy and still prepares its own)
  *   dq    bf16 [total_tokens, n_q_heads, 192]  gradient w.r.t. the un-rotated q
  *   dk    bf16 [total_tokens, n_kv_heads, 192] gradient w.r.t. the un-rotated k (summed over the group)
  *   dv    bf16 [total_tokens, n_kv_heads, 128] gradient w.r.t. the unscaled v (summed over the group)
@@ -114,7 +119,7 @@ size_t mimo_attn_bwd_workspace_size_fast(int32_t total_tokens, int32_t batch, in
  * fused attention carries the sink in training). */
 mimo_status_t mimo_attn_bwd(const void *q, const void *k, const void *v, const float *sink,
                             const void *out, const float *lse, const void *dout, const void *q_rot,
-                            const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
+                            const void *k_rot, const int32_t *cu_seqlens, int32_t batch, int32_t total_tokens,
                             int32_t max_seqlen, int32_t window, double rope_base, int32_t n_q_heads,
                             int32_t n_kv_heads, void *dq, void *dk, void *dv, float *dsink,
                             void *workspace, size_t workspace_bytes, void *stream);

@@ -51,10 +51,10 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails ho
 
 def fwd(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, sink=None, cu=FAKE, batch=1, T=16, max_seqlen=16, window=128,
-             base=1e4, hq=64, hkv=8, out=FAKE, lse=None, q_rot=None, ws=FAKE, wsb=1 << 30)
+             base=1e4, hq=64, hkv=8, out=FAKE, lse=None, q_rot=None, k_rot=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return L.mimo_attn_fwd(a["q"], a["k"], a["v"], a["sink"], a["cu"], a["batch"], a["T"], a["max_seqlen"],
-                           a["window"], a["base"], a["hq"], a["hkv"], a["out"], a["lse"], a["q_rot"], a["ws"],
+                           a["window"], a["base"], a["hq"], a["hkv"], a["out"], a["lse"], a["q_rot"], a["k_rot"], a["ws"],
                            a["wsb"], None)
 
 
@@ -75,7 +75,7 @@ def test_empty_batch_is_a_no_op(L):
 def bwd(L, **kw):
     a = dict(sink=None, dsink=None, ws=FAKE, wsb=1 << 30, hkv=8, T=16, window=128)
     a.update(kw)
-    return L.mimo_attn_bwd(FAKE, FAKE, FAKE, a["sink"], FAKE, FAKE, FAKE, None, FAKE, 1, a["T"], 16, a["window"],
+    return L.mimo_attn_bwd(FAKE, FAKE, FAKE, a["sink"], FAKE, FAKE, FAKE, None, None, FAKE, 1, a["T"], 16, a["window"],
                            1e4, 64, a["hkv"], FAKE, FAKE, FAKE, a["dsink"], a["ws"], a["wsb"], None)
 
 
@@ -230,7 +230,7 @@ def test_key_stream_offset_limits(L):
     assert L.mimo_attn_bwd_workspace_size_fast(bwd_max + 1, 1, bwd_max + 1, 4, 1, -1) == 0
     assert fwd(L, T=fwd_max + 1, max_seqlen=fwd_max + 1, hq=1, hkv=1) == 2
     assert b"32-bit" in L.mimo_attn_last_error()
-    assert L.mimo_attn_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1, bwd_max + 1, bwd_max + 1, -1,
+    assert L.mimo_attn_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, FAKE, 1, bwd_max + 1, bwd_max + 1, -1,
                            1e4, 1, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 62, None) == 2
     assert L.mimo_attn_prefill_cached(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 16, fwd_max, 16,
                                       fwd_max + 16, -1, 1e4, 1, 1, FAKE, None, FAKE, 1 << 62, None) == 2

@@ -32,7 +32,7 @@ def _given_outputs(d, rows=None):
     return torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(l).to(torch.float32)
 
 
-def _run_bwd(ga, d, O, L, dO, path="fast", q_rot=None):
+def _run_bwd(ga, d, O, L, dO, path="fast", q_rot=None, k_rot=None):
     dev = "cuda"
     sink = None if d["sink"] is None else d["sink"].to(dev)
     T, hq, hkv = d["q"].shape[0], d["q"].shape[1], d["k"].shape[1]
@@ -43,7 +43,8 @@ def _run_bwd(ga, d, O, L, dO, path="fast", q_rot=None):
         n = ga.bwd_workspace_size(T, hq, hkv, d["window"])
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     g = ga.bwd(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), sink, O.to(dev), L.to(dev), dO.to(dev),
-               d["cu_seqlens"].to(dev), maxl, d["window"], d["rope_base"], workspace=ws, q_rot=q_rot)
+               d["cu_seqlens"].to(dev), maxl, d["window"], d["rope_base"], workspace=ws, q_rot=q_rot,
+               k_rot=k_rot)
     torch.cuda.synchronize()
     return [None if x is None else x.cpu() for x in g]
 
@@ -236,6 +237,38 @@ def test_bwd_with_forward_q_rot(lengths, hkv, window, path):
     dO = mi.dout_like(sum(lengths), 4)
     a = _run_bwd(ga, d, O, L, dO, path)
     b = _run_bwd(ga, d, O, L, dO, path, q_rot=qr)
+    for x, y in zip(a, b):
+        assert (x is None and y is None) or torch.equal(x, y)
+
+
+@pytest.mark.parametrize("lengths,hkv,window", [([33, 1, 31, 47, 16, 17], 8, 3), ([700, 333, 95], 4, -1),
+                                                ([129, 64, 250], 8, 128)])
+@pytest.mark.parametrize("path", ["fast", "least"])
+def test_bwd_with_forward_k_rot(lengths, hkv, window, path):
+    """Handing the backward the forward's rotated k (with q_rot too) gives bitwise the gradients of the
+    backward's own rotation passes, including the key tiles of the dQ kernel that reach past the T rows of
+    the caller's buffer (clamped); the least-workspace path ignores it.  The k_rot output itself is RoPE
+    applied at each key's position in its own sequence (the oracle's fp64 rotation, to one bf16 rounding)."""
+    ga = _gpu()
+    d = mi.make_layer(lengths, 64, hkv, 13, window >= 0)
+    d.update(window=window, rope_base=1e4)
+    print(f"case k_rot bwd lengths={lengths} path={path}", flush=True)
+    dev = "cuda"
+    qr = torch.empty(d["q"].shape, dtype=torch.bfloat16, device=dev)
+    kr = torch.full(d["k"].shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    sink = None if d["sink"] is None else d["sink"].to(dev)
+    O, L = ga.fwd(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), sink, d["cu_seqlens"].to(dev), max(lengths),
+                  window, 1e4, q_rot=qr, k_rot=kr)
+    O, L = O.cpu(), L.cpu()
+    T = sum(lengths)
+    pos = np.concatenate([np.arange(n) for n in lengths]).astype(np.int32)
+    ref = oracle.rope(d["k"].reshape(T * hkv, 192), np.repeat(pos, hkv), 1e4)
+    got = kr.cpu().float().numpy().reshape(T * hkv, 192)
+    assert np.isfinite(got).all()
+    assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6).all()
+    dO = mi.dout_like(T, 4)
+    a = _run_bwd(ga, d, O, L, dO, path, q_rot=qr)
+    b = _run_bwd(ga, d, O, L, dO, path, q_rot=qr, k_rot=kr)
     for x, y in zip(a, b):
         assert (x is None and y is None) or torch.equal(x, y)
 
