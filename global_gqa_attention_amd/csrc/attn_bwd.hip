@@ -964,8 +964,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
 
 // ------------------------------------------------------------------------------------------------------
 // 5b. dQ from the stored dS blocks: dQ^T += K'^T dS^T per 32-key block, no recomputation.  A workgroup owns
-//     one query tile (32 queries) of four query heads of one KV group (one head per wave) and walks the key
-//     blocks the tile sees.  Per block the four waves share one row-major k' tile (32 keys x 192) and each
+//     one query tile (32 queries) of NH query heads of one KV group (one head per wave) and walks the key
+//     blocks the tile sees.  Per block the NH waves share one row-major k' tile (32 keys x 192) and each
 //     loads its head's dS block; both MFMA operands come out of LDS through ds_read_b64_tr_b16, which hands
 //     every lane of a 16-lane group one 16-bit column element of four rows read by four other lanes:
 //     lane i, element t <- the 4-element row read by lane 4 t + i / 4, element i % 4.  The MFMA k index
@@ -973,15 +973,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const BwdArgs A)
 // ------------------------------------------------------------------------------------------------------
 
 // NH waves per workgroup, one query head each: the NH heads share every k' tile (the k' rows are loaded
-// by the first 768 / 128 = 6 waves, two chunks per lane; every wave loads its own dS block)
+// by the first 768 / 128 = 6 waves, two chunks per lane, or 4 waves, three, when NH = 4; every wave loads
+// its own dS block)
 template <int NH>
 struct DsqTile {
     uint4 kr[32 * KCH];                  // k' rows, 16-byte chunk q of row r at q ^ (4 ((r >> 1) & 1))
     uint4 ds[NH][128];                   // one stored dS block per wave
 };
 
-// NS ring stages, OCC workgroups per CU.  Causal layers: eight heads per workgroup and five stages (140 KB,
-// four block loads in flight: long work items that stream HBM).  Sliding-window layers: four heads and three
+// NS ring stages, OCC workgroups per CU.  Causal layers: all sixteen heads of a KV group per workgroup when
+// the group has sixteen (four waves per SIMD, at most 128 registers) and three stages (132 KB), so that each
+// k' tile is copied into LDS once per query tile instead of twice (1.93 -> 1.70 ms at the 32K batch); eight
+// heads and five stages (140 KB, four block loads in flight) for groups of eight.  Sliding-window layers: four heads and three
 // stages (60 KB), two workgroups per CU: their work items are short (about six key blocks), and a second
 // resident workgroup hides one's start-up under the other's work (0.447 -> 0.414 ms at the 32K batch; the
 // causal layer measured 1.95 ms in the first form and 2.02 ms in this one).
@@ -1108,10 +1111,15 @@ __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A
     const int qt = q0 + c;
     const float2 *qcs = a.rope + (size_t)min(max(qt - seq_start, 0), a.rope_len - 1) * NHALF;
     rope_back(dq[0], dq[1], qcs, hh);
-    __syncthreads();                        // every wave is done reading the ring
+    // (sixteen heads' rows do not fit in the ring at once: two rounds of eight)
+    constexpr int ER = NH > 8 ? 2 : 1, NHR = NH / ER;
     uint4 *stg = (uint4 *)ring;
-    {
-        u16 *row = (u16 *)(stg + (c * NH + wave) * KCH) + 4 * hh;
+    const int h0 = kvh * G + hg * NH;
+#pragma unroll
+    for (int rd = 0; rd < ER; ++rd) {
+    __syncthreads();                        // every wave is done reading the ring
+    if (wave / NHR == rd) {
+        u16 *row = (u16 *)(stg + (c * NHR + wave % NHR) * KCH) + 4 * hh;
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
 #pragma unroll
@@ -1125,13 +1133,13 @@ __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A
         }
     }
     __syncthreads();
-    const int h0 = kvh * G + hg * NH;
 #pragma unroll
-    for (int j = 0; j < 32 * KCH / 64; ++j) {
-        const int g = 64 * NH * j + tid, R = g / KCH, k = g % KCH, qc = R / NH, w = R % NH;
+    for (int j = 0; j < 32 * NHR * KCH / (64 * NH); ++j) {
+        const int g = 64 * NH * j + tid, R = g / KCH, k = g % KCH, qc = R / NHR, w = R % NHR;
         const uint4 x = stg[R * KCH + ((k & ~7) | ((k & 7) ^ (qc & 7)))];
         if (q0 + qc >= seq_start && q0 + qc < seq_end)
-            st16u_nt(A.dq + ((size_t)(q0 + qc) * a.hq + h0 + w) * DQK + 8 * k, x);
+            st16u_nt(A.dq + ((size_t)(q0 + qc) * a.hq + h0 + rd * NHR + w) * DQK + 8 * k, x);
+    }
     }
 }
 
@@ -1302,11 +1310,12 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     }
     const int G = a.hq / a.hkv;
     if (A.ds) {
-        const int nh = G % 8 == 0 && a.window < 0 ? 8 : 4;
+        const int nh = G % 16 == 0 && a.window < 0 ? 16 : G % 8 == 0 && a.window < 0 ? 8 : 4;
         const long grid = ((long)a.T / 32 + 2L * a.batch) * (G / nh) * a.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         trace_begin(a.window >= 0 ? "bwd_dq_ds_swa" : "bwd_dq_ds_global", stream);
         if (a.window >= 0) bwd_dq_ds_kernel<4, true, 3, 2><<<(unsigned)grid, 256, 0, stream>>>(A);
+        else if (nh == 16) bwd_dq_ds_kernel<16, false, 3, 1><<<(unsigned)grid, 1024, 0, stream>>>(A);
         else if (nh == 8) bwd_dq_ds_kernel<8, false, 5, 1><<<(unsigned)grid, 512, 0, stream>>>(A);
         else bwd_dq_ds_kernel<4, false, 5, 1><<<(unsigned)grid, 256, 0, stream>>>(A);
         trace_end(stream);
