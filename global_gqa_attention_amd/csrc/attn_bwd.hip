@@ -984,10 +984,12 @@ struct DsqTile {
 // NS ring stages, OCC workgroups per CU.  Causal layers: all sixteen heads of a KV group per workgroup when
 // the group has sixteen (four waves per SIMD, at most 128 registers) and three stages (132 KB), so that each
 // k' tile is copied into LDS once per query tile instead of twice (1.93 -> 1.70 ms at the 32K batch); eight
-// heads and five stages (140 KB, four block loads in flight) for groups of eight.  Sliding-window layers: four heads and three
-// stages (60 KB), two workgroups per CU: their work items are short (about six key blocks), and a second
-// resident workgroup hides one's start-up under the other's work (0.447 -> 0.414 ms at the 32K batch; the
-// causal layer measured 1.95 ms in the first form and 2.02 ms in this one).
+// heads and five stages (140 KB, four block loads in flight) for groups of eight.  Sliding-window layers:
+// eight heads (four for groups of four) and two stages (56 KB), two workgroups per CU: their work items are
+// short (about six key blocks), and a second resident workgroup hides one's start-up under the other's work
+// (four heads, three stages: 0.447 -> 0.414 ms at the 32K batch, against 2.02 ms for 1.95 on the causal
+// layer; eight heads, two stages: 0.405 -> 0.367 ms; eight heads, three stages, one workgroup: 0.42 ms).
+// Where the ring cannot hold every head's dq rows at once, they leave in two or four rounds.
 template <int NH, bool WIN, int NS, int OCC>
 __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A)
 {
@@ -1111,8 +1113,9 @@ __global__ __launch_bounds__(64 * NH, OCC) void bwd_dq_ds_kernel(const BwdArgs A
     const int qt = q0 + c;
     const float2 *qcs = a.rope + (size_t)min(max(qt - seq_start, 0), a.rope_len - 1) * NHALF;
     rope_back(dq[0], dq[1], qcs, hh);
-    // (sixteen heads' rows do not fit in the ring at once: two rounds of eight)
-    constexpr int ER = NH > 8 ? 2 : 1, NHR = NH / ER;
+    constexpr int RING = NS * (int)sizeof(DsqTile<NH>), ROWS = 32 * KCH * 16;   // bytes of one head's tile
+    constexpr int ER = NH * ROWS <= RING ? 1 : (NH / 2) * ROWS <= RING ? 2 : 4, NHR = NH / ER;
+    static_assert(NH % ER == 0 && NHR * ROWS <= RING, "dq staging");
     uint4 *stg = (uint4 *)ring;
     const int h0 = kvh * G + hg * NH;
 #pragma unroll
@@ -1310,11 +1313,12 @@ hipError_t launch_bwd(const BwdArgs &A, hipStream_t stream)
     }
     const int G = a.hq / a.hkv;
     if (A.ds) {
-        const int nh = G % 16 == 0 && a.window < 0 ? 16 : G % 8 == 0 && a.window < 0 ? 8 : 4;
+        const int nh = G % 16 == 0 && a.window < 0 ? 16 : G % 8 == 0 ? 8 : 4;
         const long grid = ((long)a.T / 32 + 2L * a.batch) * (G / nh) * a.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         trace_begin(a.window >= 0 ? "bwd_dq_ds_swa" : "bwd_dq_ds_global", stream);
-        if (a.window >= 0) bwd_dq_ds_kernel<4, true, 3, 2><<<(unsigned)grid, 256, 0, stream>>>(A);
+        if (a.window >= 0 && nh == 8) bwd_dq_ds_kernel<8, true, 2, 2><<<(unsigned)grid, 512, 0, stream>>>(A);
+        else if (a.window >= 0) bwd_dq_ds_kernel<4, true, 3, 2><<<(unsigned)grid, 256, 0, stream>>>(A);
         else if (nh == 16) bwd_dq_ds_kernel<16, false, 3, 1><<<(unsigned)grid, 1024, 0, stream>>>(A);
         else if (nh == 8) bwd_dq_ds_kernel<8, false, 5, 1><<<(unsigned)grid, 512, 0, stream>>>(A);
         else bwd_dq_ds_kernel<4, false, 5, 1><<<(unsigned)grid, 256, 0, stream>>>(A);
