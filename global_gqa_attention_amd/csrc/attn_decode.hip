@@ -151,13 +151,13 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
             for (int j = 0; j < CH * DKC / 64; ++j) {
                 const int slot = 64 * j + lane, r = slot / DKC, q = slot % DKC;
                 const int row = __shfl(tv, r, 64);
-                lds_dma16(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
+                lds_dma16_nt(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
             }
 #pragma unroll
             for (int j = 0; j < CH * DVC / 64; ++j) {
                 const int slot = 64 * j + lane, r = slot / DVC, q = slot % DVC;
                 const int row = __shfl(tv, r, 64);
-                lds_dma16(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
+                lds_dma16_nt(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
             }
             tv = table_rows(k + CH);
         } else if (k + CH <= ke) {
@@ -172,13 +172,13 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
             for (int j = 0; j < CH * DKC / 64; ++j) {
                 const int slot = 64 * j + lane, r = slot / DKC, q = slot % DKC;
                 const int row = c0 + min(k + r, ke - 1);
-                lds_dma16(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
+                lds_dma16_nt(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
             }
 #pragma unroll
             for (int j = 0; j < CH * DVC / 64; ++j) {
                 const int slot = 64 * j + lane, r = slot / DVC, q = slot % DVC;
                 const int row = c0 + min(k + r, ke - 1);
-                lds_dma16(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
+                lds_dma16_nt(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
             }
         }
     };
@@ -486,13 +486,13 @@ __global__ __launch_bounds__(64 * VNW, 2) void verify_split_kernel(const DecodeA
             for (int jj = 0; jj < KJ; ++jj) {
                 const int j = VNW * jj + wave, slot = 64 * j + lane, r = slot / DKC, q = slot % DKC;
                 const int row = stab[min(k + r, ke - 1) - ks];
-                lds_dma16(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
+                lds_dma16_nt(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
             }
 #pragma unroll
             for (int jj = 0; jj < VJ; ++jj) {
                 const int j = VNW * jj + wave, slot = 64 * j + lane, r = slot / DVC, q = slot % DVC;
                 const int row = stab[min(k + r, ke - 1) - ks];
-                lds_dma16(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
+                lds_dma16_nt(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
             }
         } else if (k + CH <= ke) {
             const u16 *kb = wave_uniform(A.k_cache + ((size_t)(c0 + k) * A.hkv + kvh) * DQK);
@@ -506,13 +506,13 @@ __global__ __launch_bounds__(64 * VNW, 2) void verify_split_kernel(const DecodeA
             for (int jj = 0; jj < KJ; ++jj) {
                 const int j = VNW * jj + wave, slot = 64 * j + lane, r = slot / DKC, q = slot % DKC;
                 const int row = c0 + min(k + r, ke - 1);
-                lds_dma16(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
+                lds_dma16_nt(A.k_cache + ((size_t)row * A.hkv + kvh) * DQK + 8 * swz384(r, q), T.k + 64 * j);
             }
 #pragma unroll
             for (int jj = 0; jj < VJ; ++jj) {
                 const int j = VNW * jj + wave, slot = 64 * j + lane, r = slot / DVC, q = slot % DVC;
                 const int row = c0 + min(k + r, ke - 1);
-                lds_dma16(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
+                lds_dma16_nt(A.v_cache + ((size_t)row * A.hkv + kvh) * DVV + 8 * swz256t(r, q), T.v + 64 * j);
             }
         }
     };

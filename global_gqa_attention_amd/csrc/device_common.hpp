@@ -83,6 +83,16 @@ __device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, void
                  : "memory", "m0");
 }
 
+// The per-lane-address copy with the non-temporal hint, for data read once.
+__device__ __forceinline__ void lds_dma16_nt(const void *gsrc, void *lds_wave_base)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(m0), "v"(gsrc)
+                 : "memory", "m0");
+}
+
 // The same with the non-temporal hint, for data read once (keeps it from displacing reused lines in L2).
 __device__ __forceinline__ void lds_dma16_nt(const void *sbase, uint32_t voff, void *lds_wave_base)
 {
