@@ -16,7 +16,8 @@
 //   2. bwd_dsink: one 1024-thread workgroup per head, fixed-order tree sum (only when a sink is given).
 //   3. row_prep:  DMA-ready copies in the workspace: q' (rotated) row-major, k' (rotated) row-major and
 //                 transposed (the transposed copy keeps each 16-token group's 4-token chunks in the order
-//                 (0, 2, 1, 3), the order in which the score registers hold tokens).
+//                 (0, 2, 1, 3), the order in which the score registers hold tokens).  Not run for q when the
+//                 forward's rotated q is given, nor for k when its rotated k is given on the stored-dS path.
 //   4. bwd_dkdv:  key-major.  A workgroup owns 128 keys of one KV head (32 per wave; the key is the MFMA
 //                 column, so each lane owns one key with its rotated k and v resident in registers) and
 //                 walks every (query head of the group, 32-query tile) that sees them: S = Q'K'^T and
@@ -24,7 +25,8 @@
 //                 LSE/D stream HBM -> LDS with global_load_lds (three-stage ring, XOR-swizzled); the
 //                 transposed operands of dV and dK come from the same tiles through ds_read_b64_tr_b16.
 //                 With the stored-dS workspace it also writes every dS block it computes.
-//   5. bwd_dq:    either from the stored dS blocks (5b: dQ^T += K'^T dS^T, no recomputation), or
+//   5. bwd_dq:    either from the stored dS blocks (5b: dQ^T += K'^T dS^T, no recomputation; one query tile of
+//                 up to sixteen heads per workgroup, which share each k' tile), or
 //                 query-major like the forward: S^T = K'Q'^T, P^T, dP^T = V dO^T, dS^T, then
 //                 dQ^T += K'^T dS^T with k' (both layouts) and v streamed HBM -> LDS.
 // dq and dk leave through the transposed rotation in their epilogues.  Rows that a lane owns (the dK/dV score
