@@ -58,6 +58,8 @@ def _run_bwd(ga, d, O, L, dO, path="fast", q_rot=None, k_rot=None):
     ([100, 29], 12, 4, 40, 1e4, True),
     ([100, 29], 8, 1, -1, 1e4, False),
     ([33, 1, 31, 47, 16, 17], 32, 8, 3, 1e4, True),
+    ([129, 64, 250], 64, 4, 128, 1e4, True),    # 16 heads per KV head on a sliding-window layer
+    ([300, 77], 64, 2, -1, 1e7, False),         # 32 heads per KV head on a causal layer
 ])
 @pytest.mark.parametrize("path", ["fast", "least"])
 def test_bwd_small_full(lengths, hq, hkv, window, base, sink, path):
