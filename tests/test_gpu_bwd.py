@@ -271,8 +271,9 @@ def test_bwd_with_forward_k_rot(lengths, hkv, window, path):
     dO = mi.dout_like(T, 4)
     a = _run_bwd(ga, d, O, L, dO, path, q_rot=qr)
     b = _run_bwd(ga, d, O, L, dO, path, q_rot=qr, k_rot=kr)
-    for x, y in zip(a, b):
-        assert (x is None and y is None) or torch.equal(x, y)
+    c = _run_bwd(ga, d, O, L, dO, path, k_rot=kr)          # k handed over, q rotated by the backward
+    for x, y, z in zip(a, b, c):
+        assert (x is None and y is None and z is None) or (torch.equal(x, y) and torch.equal(x, z))
 
 
 @pytest.mark.parametrize("window,hkv,sink", [(128, 4, True), (-1, 4, False)])
