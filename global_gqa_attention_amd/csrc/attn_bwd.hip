@@ -456,11 +456,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         const int s16 = seq_start & ~15;
         const int kap = 4 * tile + kq;
         const int64_t ds_seq = A.ds ? A.ds_index[bseq] : 0;
-        auto store_ds = [&](Pos ps, const bf16x8 *sb) {
-            const int h = ps.h, q0 = ps.q0;
-            const int n = (q0 - s16) >> 5;
-            const int64_t blk = (ds_seq + ds_rows_before(n, a.window) + (kap - ds_klo(q0, seq_start, a.window))) *
-                                    a.hq + h;
+        // block index of a position (the first one only; later ones follow by the steps below)
+        auto blk_of = [&](Pos ps) -> int64_t {
+            const int n = (ps.q0 - s16) >> 5;
+            return (ds_seq + ds_rows_before(n, a.window) + (kap - ds_klo(ps.q0, seq_start, a.window))) * a.hq + ps.h;
+        };
+        // The block of the next position: the next head starts at the top again (heads are the innermost
+        // index: one block further than the previous head's top); one query tile down removes row n of the
+        // sequence's rows (causal: n slots; sliding window: ds_row_width slots, less the key block that
+        // leaves the window's lower edge, whose first slot index k_lo rises by one when q0 - window -
+        // seq_start >= 32).
+        const int64_t blk_top = A.ds ? blk_of(first) : 0;
+        const int rw = a.window >= 0 ? ds_row_width(a.window) : 0;
+        auto blk_next = [&](int64_t b, Pos p, Pos np) -> int64_t {
+            if (np.h != p.h) return blk_top + (np.h - first.h);
+            if (a.window < 0) return b - (int64_t)((p.q0 - s16) >> 5) * a.hq;
+            return b - (int64_t)(rw - (p.q0 - a.window - seq_start >= 32 ? 1 : 0)) * a.hq;
+        };
+        int64_t bc = blk_top, bn = blk_top;   // blocks of pc and pn
+        if (A.ds && nsteps > 1) bn = blk_next(blk_top, first, pn);
+        auto store_ds = [&](int64_t blk, const bf16x8 *sb) {
             if (blk >= A.ds_cap) return false;   // only with a max_seqlen below the longest sequence
             // streaming stores (the blocks are read back by another kernel); plane P holds sb[P] of every lane
             // at row (lane ^ 8 hh ^ 4 P): each store writes a whole 1 KB plane
@@ -533,11 +548,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
                                   __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
             pslot[128 + lane] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
             pslot[192 + lane] = make_uint4(sw[4], sw[5], sw[6], sw[7]);
-            if (A.ds) store_ds(ps, sb);
+            if (A.ds) store_ds(bc, sb);
         };
         auto stage = [&](int st, const DkdvTile &cur, DkdvTile &fill) {
             stage_start(fill);
             if (visible(st, pc)) s_step(pc, cur, pbuf[st & 1][kq]);
+            // stage_end's position update, with the block indices beside it
+            bc = bn;
+            if (A.ds && st + 2 <= nsteps - 1) bn = blk_next(bn, pn, advance(pn));
             stage_end(st);
         };
         // unrolled by three: the ring's buffers by name (stage st reads ring[st % 3], fills ring[(st+1) % 3])
