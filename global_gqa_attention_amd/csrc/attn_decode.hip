@@ -22,7 +22,9 @@
 // chunks, one split) copies its chunks all at once into four buffers and merges the new token and the
 // sink itself, with no combine kernel.  The query's rotation angles depend only on the position and the
 // dim, so a decode wave computes each of the 32 once (in double precision) and shares them by lane
-// shuffles.
+// shuffles.  Per chunk, only a chunk that reaches past the split's rows or past some column's visible rows
+// evaluates the mask, and the running max is a lazy reference that moves only when a chunk's max exceeds
+// it by 2^8, so most chunks skip the rescale of the output accumulator (both wave-uniform branches).
 //
 // The same kernels serve two more forms.  Paged cache (page size 1: SGLang cookbook page "MiMo-V2.6",
 // section 2): cache row r of sequence b is pool row page_table[cu_cache[b] + r]; each lane of the first 32
@@ -38,6 +40,7 @@ namespace mimo {
 namespace {
 
 constexpr int CH = 32;            // cache rows per chunk
+constexpr float RESCALE_TH = 8.f; // keep a stale running max until a chunk's max exceeds it by 2^8
 
 __device__ __forceinline__ double inv_freq(double base, int d) { return pow(base, -(double)d / (double)NHALF); }
 
@@ -109,6 +112,9 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
         lim = n - A.nq + ti;
         lo = A.window >= 0 ? lim - A.window : min(lim, 0);
     }
+    // rows that every column of the wave may see: [lo_max, lim_min] (wave-uniform)
+    const int lim_min = verify ? n - A.nq : n - 1;
+    const int lo_max = verify && A.window >= 0 ? n - 1 - A.window : 0;
 
     if (!FIN && ks >= ke) {                  // nothing cached in this split: an empty partial
         if (hvalid) {
@@ -285,35 +291,46 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(const DecodeArgs A)
             sacc = mfma32(kop[s % KR], qf[s], sacc);
             if (s + KR < 12) kop[s % KR] = kread(s + KR);
         }
+        // only a chunk that reaches past the split's rows or past some column's visible rows evaluates the
+        // mask (a wave-uniform branch)
         float mx = -INFINITY;
+        if (!(k + CH <= ke && k + CH - 1 <= lim_min && k >= lo_max)) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int key = k + 8 * (j >> 2) + 4 * hh + (j & 3);
-            const bool ok = key < ke && (uint32_t)(key - lo) <= (uint32_t)(lim - lo);
-            const float sv = ok ? sacc[j] * A.scale_log2 : -INFINITY;
-            sacc[j] = sv;
-            mx = fmaxf(mx, sv);
+            for (int j = 0; j < 16; ++j) {
+                const int key = k + 8 * (j >> 2) + 4 * hh + (j & 3);
+                const bool ok = key < ke && (uint32_t)(key - lo) <= (uint32_t)(lim - lo);
+                sacc[j] = ok ? sacc[j] : -INFINITY;
+            }
         }
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        // a verify column may see none of a chunk's keys: keep it at (max -inf, sum 0) without NaNs
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_ref);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+        mx = pair_max(mx) * A.scale_log2;
+        // lazy reference: it moves only when the chunk's max exceeds it by 2^8 (probabilities stay below 2^8),
+        // so most chunks skip the rescale of o and l (exact either way: numerator and denominator share it)
+        const bool grow = mx > m_run + RESCALE_TH;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            // (lanes that do not grow keep alpha = 1: their m_run may still be -inf)
+            const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] *= alpha;
+            m_run = grow ? mx : m_run;
+        }
+        // a verify column may see none of the keys so far: keep it at (max -inf, sum 0) without NaNs
+        const float nref = m_run == -INFINITY ? 0.f : -m_run;
         float psum = 0.f;
         bf16x8 pf[2];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float pj = fast_exp2(sacc[j] - m_ref);
+            const float pj = fast_exp2(__builtin_fmaf(sacc[j], A.scale_log2, nref));
             psum += pj;
             pf[j >> 3][j & 7] = f2bf(pj);
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        l_run += psum;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bf16x8 v0 = tr_pair(vtr(T, 0, 0, i), vtr(T, 0, 1, i));
             const bf16x8 v1 = tr_pair(vtr(T, 1, 0, i), vtr(T, 1, 1, i));
-            o[i] *= alpha;
             o[i] = mfma32(v0, pf[0], o[i]);
             o[i] = mfma32(v1, pf[1], o[i]);
         }
@@ -441,6 +458,9 @@ __global__ __launch_bounds__(64 * VNW, 2) void verify_split_kernel(const DecodeA
         lim = n - A.nq + ti;
         lo = A.window >= 0 ? lim - A.window : min(lim, 0);
     }
+    // rows that every column of the wave may see: [lo_max, lim_min] (wave-uniform)
+    const int lim_min = verify ? n - A.nq : n - 1;
+    const int lo_max = verify && A.window >= 0 ? n - 1 - A.window : 0;
 
     if (ks >= ke) {                          // nothing cached in this split: an empty partial
         if (hvalid) {
@@ -581,33 +601,44 @@ __global__ __launch_bounds__(64 * VNW, 2) void verify_split_kernel(const DecodeA
         bf16x8 vop[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) vop[m] = tr_pair(vtr(T, m & 1, 0, m >> 1), vtr(T, m & 1, 1, m >> 1));
+        // only a chunk that reaches past the split's rows or past some column's visible rows evaluates the
+        // mask (a wave-uniform branch)
         float mx = -INFINITY;
+        if (!(k + CH <= ke && k + CH - 1 <= lim_min && k >= lo_max)) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int key = k + 8 * (j >> 2) + 4 * hh + (j & 3);
-            const bool ok = key < ke && (uint32_t)(key - lo) <= (uint32_t)(lim - lo);
-            const float sv = ok ? sacc[j] * A.scale_log2 : -INFINITY;
-            sacc[j] = sv;
-            mx = fmaxf(mx, sv);
+            for (int j = 0; j < 16; ++j) {
+                const int key = k + 8 * (j >> 2) + 4 * hh + (j & 3);
+                const bool ok = key < ke && (uint32_t)(key - lo) <= (uint32_t)(lim - lo);
+                sacc[j] = ok ? sacc[j] : -INFINITY;
+            }
         }
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        // a verify column may see none of a chunk's keys: keep it at (max -inf, sum 0) without NaNs
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_ref);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+        mx = pair_max(mx) * A.scale_log2;
+        // lazy reference: it moves only when the chunk's max exceeds it by 2^8 (probabilities stay below 2^8),
+        // so most chunks skip the rescale of o and l (exact either way: numerator and denominator share it)
+        const bool grow = mx > m_run + RESCALE_TH;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            // (lanes that do not grow keep alpha = 1: their m_run may still be -inf)
+            const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] *= alpha;
+            m_run = grow ? mx : m_run;
+        }
+        // a verify column may see none of the keys so far: keep it at (max -inf, sum 0) without NaNs
+        const float nref = m_run == -INFINITY ? 0.f : -m_run;
         float psum = 0.f;
         bf16x8 pf[2];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float pj = fast_exp2(sacc[j] - m_ref);
+            const float pj = fast_exp2(__builtin_fmaf(sacc[j], A.scale_log2, nref));
             psum += pj;
             pf[j >> 3][j & 7] = f2bf(pj);
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        l_run += psum;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            o[i] *= alpha;
             o[i] = mfma32(vop[2 * i], pf[0], o[i]);
             o[i] = mfma32(vop[2 * i + 1], pf[1], o[i]);
         }
