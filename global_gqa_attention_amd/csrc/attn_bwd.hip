@@ -269,9 +269,11 @@ template <bool WIN>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
 {
     const LayerArgs &a = A.L;
-    __shared__ __attribute__((aligned(16))) DkdvTile ring[3];          // tiles of steps st-1, st, st+1
+    // tiles of stages st-1, st, st+1 (sliding window: a ring of three for each half of the keys, ring[3 g + k];
+    // each half's three tiles lie within 64 KB, the reach of an LDS instruction's offset field)
+    __shared__ __attribute__((aligned(16))) DkdvTile ring[WIN ? 6 : 3];
     __shared__ __attribute__((aligned(16))) uint4 pbuf[2][4][256];     // P and dS (bf16) of a step: 4 planes x 64 lanes
-    __shared__ __attribute__((aligned(16))) uint4 kstage[4 * 32 * QCH]; // the score waves' k' rows, at the start
+    __shared__ __attribute__((aligned(16))) uint4 kstage_own[WIN ? 1 : 4 * 32 * QCH];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -294,7 +296,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     const int q_lo = kb0 & ~15;
     const int q_hi = WIN ? min(seq_end - 1, kb_last + a.window) : seq_end - 1;
     const int nq = (q_hi - q_lo + MQ) / MQ;
-    const int nsteps = nq * GS;
+    const int q_top = q_lo + (nq - 1) * MQ;
+    // Sliding window: the two halves of the key tile (waves 0, 1: keys kb0 .. kb0 + 63; waves 2, 3: the rest)
+    // see query ranges 64 apart, so in a stage each half takes a tile of its own: of the tiles counted from
+    // the top, half g walks only jlo_g .. jlo_g + n_g - 1, the ones that its keys see, and a head takes as many
+    // stages as the half with more tiles (about six instead of eight or nine with a 128-key window, in which
+    // a 32-key block sees five tiles).  Causal layers: both halves walk all nq tiles together.
+    const int half_g = (wave & 3) >> 1;   // this wave's half of the keys (both roles)
+    int nS = nq, qb_g = q_top, n_g = nq;    // stages per head; the half's first tile (its q0) and tile count
+    if constexpr (WIN) {
+        auto half = [&](int kg0, int &lo, int &n) {
+            if (kg0 > kb_last) {
+                lo = 0;
+                n = 0;
+                return;
+            }
+            const int kg1 = min(kg0 + 63, kb_last);
+            // tile j (first query q_top - 32 j) is seen iff q0 <= kg1 + window and q0 + 31 >= kg0
+            lo = max(0, (q_top - kg1 - a.window + MQ - 1) >> 5);
+            const int hi = min(nq - 1, (q_top + MQ - 1 - kg0) >> 5);
+            n = max(0, hi - lo + 1);
+        };
+        int lo0, n0, lo1, n1;
+        half(kb0, lo0, n0);
+        half(kb0 + 64, lo1, n1);
+        nS = max(n0, n1);
+        qb_g = q_top - MQ * (half_g ? lo1 : lo0);
+        n_g = half_g ? n1 : n0;
+    }
+    const int nsteps = nS * GS;
 
     // ---- direct HBM -> LDS loads of one step's tiles (fixed per-lane byte offsets + wave-uniform bases):
     // all by the gradient waves (4..7), which finish their MFMAs early in each stage, so that the score
@@ -302,15 +332,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     // LSE*log2e by wave 6 and D by wave 7 (eight lanes each)
     const size_t qr_row = (size_t)a.hq * DQK, o_row = (size_t)a.hq * DVV;
     const int gw = wave & 3;
+    // Sliding window: each half's tile is loaded by that half's two gradient waves (4, 5 and 6, 7), so chunk
+    // slot 128 j + 64 (wave & 1) + lane; slots 384 (q') and 256 (dO) further on are the rows 16 further on,
+    // which have the same swizzle, so the per-lane offsets of j serve j + 3 (q') and j + 2 (dO) as well.
+    const int gslot = WIN ? 64 * (wave & 1) : 64 * gw, gstride = WIN ? 128 : 256;
     uint32_t o_qr[3], o_or[2];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-        const int slot = 256 * j + 64 * gw + lane, r = slot / QCH, p = slot % QCH;
+        const int slot = gstride * j + gslot + lane, r = slot / QCH, p = slot % QCH;
         o_qr[j] = (uint32_t)((r * qr_row + 8 * swz384t(r, p)) * 2);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int slot = 256 * j + 64 * gw + lane, r = slot / OCH, p = slot % OCH;
+        const int slot = gstride * j + gslot + lane, r = slot / OCH, p = slot % OCH;
         o_or[j] = (uint32_t)((r * o_row + 8 * swz256t(r, p)) * 2);
     }
     // step -> (head, query tile): heads outer, query tiles from the sequence end down.  Every key tile of a
@@ -320,7 +354,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     struct Pos {
         int q0, h;   // first query of the step's tile, its query head
     };
-    const int q_top = q_lo + (nq - 1) * MQ;
     const Pos first{q_top, kvh * G + split * GS};
     auto advance = [&](Pos p) {
         p.q0 -= MQ;
@@ -363,6 +396,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             if (lane < 8) lds_dma16(bld, (uint32_t)(16 * lane), (uint4 *)T.ld + 8 * (wave - 6));
         }
     };
+    // sliding window: one half's tile by its two gradient waves (LSE*log2e by the first, D by the second)
+    // The tile's LDS address is passed through an empty asm so that the compiler forms each copy's m0 value
+    // next to its copy instead of keeping all of them (eleven per tile, three ring slots) in scalar registers.
+    auto issue_w = [&](Pos ps, DkdvTile &T) {
+        const int h = ps.h, q0 = ps.q0;
+        uint32_t tb = (uint32_t)(uintptr_t)(lds_void *)&T + 16 * gslot;
+        asm volatile("" : "+s"(tb));
+        constexpr uint32_t OQ = offsetof(DkdvTile, qr), OO = offsetof(DkdvTile, orow), OL = offsetof(DkdvTile, ld);
+        if (q0 + MQ <= A.qr_rows) {
+            const u16 *bq = A.W.qr + ((size_t)q0 * a.hq + h) * DQK;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) lds_dma16_m0(bq, o_qr[j], tb + OQ + 16 * 128 * j);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) lds_dma16_m0(bq + 16 * qr_row, o_qr[j], tb + OQ + 16 * 128 * (j + 3));
+        } else {
+            // rows past the end (rare): lane laundered so that these per-lane addresses are formed here, not
+            // kept in registers across the loop
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int j = 0; j < 6; ++j) {
+                const int slot = 128 * j + gslot + ln, r = slot / QCH, p = slot % QCH;
+                const int row = min(q0 + r, A.qr_rows - 1);
+                lds_dma16(A.W.qr + ((size_t)row * a.hq + h) * DQK + 8 * swz384t(r, p), T.qr + 128 * j + gslot);
+            }
+        }
+        if (q0 + MQ <= a.T) {
+            const u16 *bo = A.dout + ((size_t)q0 * a.hq + h) * DVV;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) lds_dma16_m0(bo, o_or[j], tb + OO + 16 * 128 * j);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) lds_dma16_m0(bo + 16 * o_row, o_or[j], tb + OO + 16 * 128 * (j + 2));
+        } else {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int slot = 128 * j + gslot + ln, r = slot / OCH, p = slot % OCH;
+                const int row = min(q0 + r, a.T - 1);
+                lds_dma16(A.dout + (size_t)row * o_row + (size_t)h * DVV + 8 * swz256t(r, p), T.orow + 128 * j + gslot);
+            }
+        }
+        const float *bld = ((wave & 1) == 0 ? A.lse2 : A.delta) + (size_t)h * A.T_pad + q0;
+        if (lane < 8) lds_dma16_m0(bld, (uint32_t)(16 * lane), tb - 16 * gslot + OL + 16 * 8 * (wave & 1));
+    };
 
     // ---- this wave's keys
     const int kw0 = kb0 + 32 * kq;
@@ -402,7 +480,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
     // gradient waves load step st+1.  Every stage loads one tile set (the last step's again once the steps
     // run out), so the waits stay uniform.  Both roles pass nsteps + 1 barriers.  The score waves' dS
     // stores need no wait (their data registers are the compiler's to protect).
-    if (role == 1) issue(first, ring[0]);
     // pc: step st, pn: step min(st + 1, nsteps - 1) (the one stage st loads)
     Pos pc = first, pn = nsteps > 1 ? advance(first) : first;
     // a gradient wave waits for its loads of step st (issued one stage earlier), every wave makes its LDS
@@ -417,6 +494,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         pc = pn;
         if (st + 2 <= nsteps - 1) pn = advance(pn);
     };
+    // Sliding window: a stage is (j, head), j = 0 .. nS - 1; the half's tile at stage j has q0 = qb_g - 32 j
+    // while j < n_g (none after).  Slot k of the ring is ring[k] (keys kb0 .. kb0 + 63) and ring[3 + k]
+    // (the rest) -- ring[3 g + k] for half g; a half's tile is loaded only at the stages where it has one.
+    struct St {
+        int j, h;
+    };
+    auto st_next = [&](St s) {
+        if (++s.j == nS) {
+            s.j = 0;
+            ++s.h;
+        }
+        return s;
+    };
+    auto pos_of = [&](St s) { return Pos{qb_g - MQ * max(0, min(s.j, n_g - 1)), s.h}; };
+    St sc{0, first.h};            // stage st
+    St sn = st_next(sc);          // stage st + 1 (the one stage st loads)
+    auto stage_start_w = [&](int st, DkdvTile &fill) {
+        if (role == 1) wait_vmcnt<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if (role == 1 && st + 1 < nsteps && sn.j < n_g) issue_w(pos_of(sn), fill);
+    };
+    auto stage_end_w = [&]() {
+        sc = sn;
+        sn = st_next(sn);
+    };
+    if (role == 1) {
+        if constexpr (WIN) {
+            if (n_g > 0) issue_w(pos_of(sc), ring[3 * half_g]);
+        } else {
+            issue(first, ring[0]);
+        }
+    }
 
     if (role == 0) {
         // ================= score waves: S = Q'K'^T and dP = dO V^T, then P and dS = P (0.707 dP - D); P and
@@ -427,7 +537,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             // g / 64; k' into its staging array, v into the hand-over buffers, which no wave writes before
             // the first stage's barrier), then each lane reads its own row: a lane that loads its own row
             // touches 32 rows per load instruction
-            uint4 *ks = kstage + 32 * QCH * kq;
+            // (sliding window: in the half's ring slots 1 and 2, first filled after the first barrier)
+            uint4 *ks = WIN ? (uint4 *)&ring[3 * (kq >> 1) + 1] + 32 * QCH * (kq & 1) : kstage_own + 32 * QCH * kq;
             uint4 *vs = &pbuf[0][0][0] + 32 * OCH * kq;
             const u16 *kbase = A.W.kr + ((size_t)kb0 * a.hkv + kvh) * DQK;
             const u16 *vbase = a.v + ((size_t)kb0 * a.hkv + kvh) * DVV;
@@ -558,13 +669,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             if (A.ds && st + 2 <= nsteps - 1) bn = blk_next(bn, pn, advance(pn));
             stage_end(st);
         };
+        auto stage_w = [&](int st, int cs, int fs) {
+            stage_start_w(st, ring[3 * half_g + fs]);
+            if (sc.j < n_g) {
+                const Pos ps = pos_of(sc);
+                if (visible(st, ps)) {
+                    if (A.ds) bc = blk_of(ps);
+                    s_step(ps, ring[3 * half_g + cs], pbuf[st & 1][kq]);
+                }
+            }
+            stage_end_w();
+        };
         // unrolled by three: the ring's buffers by name (stage st reads ring[st % 3], fills ring[(st+1) % 3])
-        for (int st = 0; st <= nsteps; st += 3) {
-            stage(st, ring[0], ring[1]);
-            if (st + 1 > nsteps) break;
-            stage(st + 1, ring[1], ring[2]);
-            if (st + 2 > nsteps) break;
-            stage(st + 2, ring[2], ring[0]);
+        if constexpr (WIN) {
+            for (int st = 0; st <= nsteps; st += 3) {
+                stage_w(st, 0, 1);
+                if (st + 1 > nsteps) break;
+                stage_w(st + 1, 1, 2);
+                if (st + 2 > nsteps) break;
+                stage_w(st + 2, 2, 0);
+            }
+        } else {
+            for (int st = 0; st <= nsteps; st += 3) {
+                stage(st, ring[0], ring[1]);
+                if (st + 1 > nsteps) break;
+                stage(st + 1, ring[1], ring[2]);
+                if (st + 2 > nsteps) break;
+                stage(st + 2, ring[2], ring[0]);
+            }
         }
         wait_vmcnt<0>();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -614,13 +746,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
             pg = pc;
             stage_end(st);
         };
+        St sg = sc;   // stage st - 1
+        auto stage_w = [&](int st, int ps_, int fs) {
+            stage_start_w(st, ring[3 * half_g + fs]);
+            if (st >= 1 && sg.j < n_g) {
+                const Pos ps = pos_of(sg);
+                if (visible(st - 1, ps)) g_step(ring[3 * half_g + ps_], pbuf[(st - 1) & 1][kq]);
+            }
+            sg = sc;
+            stage_end_w();
+        };
         // stage st reads ring[(st - 1) % 3] and fills ring[(st + 1) % 3]
-        for (int st = 0; st <= nsteps; st += 3) {
-            stage(st, ring[2], ring[1]);
-            if (st + 1 > nsteps) break;
-            stage(st + 1, ring[0], ring[2]);
-            if (st + 2 > nsteps) break;
-            stage(st + 2, ring[1], ring[0]);
+        if constexpr (WIN) {
+            for (int st = 0; st <= nsteps; st += 3) {
+                stage_w(st, 2, 1);
+                if (st + 1 > nsteps) break;
+                stage_w(st + 1, 0, 2);
+                if (st + 2 > nsteps) break;
+                stage_w(st + 2, 1, 0);
+            }
+        } else {
+            for (int st = 0; st <= nsteps; st += 3) {
+                stage(st, ring[2], ring[1]);
+                if (st + 1 > nsteps) break;
+                stage(st + 1, ring[0], ring[2]);
+                if (st + 2 > nsteps) break;
+                stage(st + 2, ring[1], ring[0]);
+            }
         }
         wait_vmcnt<0>();
         // ---- epilogue: dv = 0.707 dV^T, dk = R^T dK^T / sqrt(192) (fp32 partials with several head splits).

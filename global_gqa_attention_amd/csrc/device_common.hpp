@@ -83,6 +83,15 @@ __device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, void
                  : "memory", "m0");
 }
 
+// The saddr copy with the LDS destination given as its 32-bit LDS address (the m0 value itself).
+__device__ __forceinline__ void lds_dma16_m0(const void *sbase, uint32_t voff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 // The per-lane-address copy with the non-temporal hint, for data read once.
 __device__ __forceinline__ void lds_dma16_nt(const void *gsrc, void *lds_wave_base)
 {
