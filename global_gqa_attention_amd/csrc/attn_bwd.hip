@@ -347,20 +347,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         const int slot = gstride * j + gslot + lane, r = slot / OCH, p = slot % OCH;
         o_or[j] = (uint32_t)((r * o_row + 8 * swz256t(r, p)) * 2);
     }
-    // step -> (head, query tile): heads outer, query tiles from the sequence end down.  Every key tile of a
-    // sequence walks the same absolute query tiles in the same order, so the workgroups running together
-    // on an XCD read the same q'/dO tiles and mostly hit in L2.  The stages walk the steps in order, so the
-    // position advances by one tile per stage (no division per stage).
+    // Causal step -> (query tile, head): query tiles from the sequence end down, the workgroup's heads inner.
+    // Every key tile of a sequence walks the same absolute query tiles in the same order from the top, so
+    // the workgroups running together on an XCD stay on the same q'/dO tiles (a key tile nearer the end of
+    // the sequence only stops earlier) and mostly hit in L2.  The stages walk the steps in order, so the
+    // position advances by one head per stage (no division per stage).  (Sliding window: see below.)
     struct Pos {
         int q0, h;   // first query of the step's tile, its query head
     };
     const Pos first{q_top, kvh * G + split * GS};
+    const int h_end = first.h + GS;
     auto advance = [&](Pos p) {
-        p.q0 -= MQ;
-        if (p.q0 < q_lo) {
-            p.q0 = q_top;
-            ++p.h;
-        }
+        ++p.h;
+        const bool wrap = p.h == h_end;
+        p.h = wrap ? first.h : p.h;
+        p.q0 = wrap ? p.q0 - MQ : p.q0;
         return p;
     };
     auto issue = [&](Pos ps, DkdvTile &T) {
@@ -567,22 +568,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs A)
         const int s16 = seq_start & ~15;
         const int kap = 4 * tile + kq;
         const int64_t ds_seq = A.ds ? A.ds_index[bseq] : 0;
-        // block index of a position (the first one only; later ones follow by the steps below)
+        // block index of a position (sliding window: at every step; causal: the first one only, later ones
+        // follow by the steps below)
         auto blk_of = [&](Pos ps) -> int64_t {
             const int n = (ps.q0 - s16) >> 5;
             return (ds_seq + ds_rows_before(n, a.window) + (kap - ds_klo(ps.q0, seq_start, a.window))) * a.hq + ps.h;
         };
-        // The block of the next position: the next head starts at the top again (heads are the innermost
-        // index: one block further than the previous head's top); one query tile down removes row n of the
-        // sequence's rows (causal: n slots; sliding window: ds_row_width slots, less the key block that
-        // leaves the window's lower edge, whose first slot index k_lo rises by one when q0 - window -
-        // seq_start >= 32).
+        // Causal: the block of the next position.  The next head of the same tile is the next block (heads
+        // are the innermost index); one query tile down, back at the first head, removes row n of the
+        // sequence's rows (n slots) and the GS - 1 heads walked.
         const int64_t blk_top = A.ds ? blk_of(first) : 0;
-        const int rw = a.window >= 0 ? ds_row_width(a.window) : 0;
         auto blk_next = [&](int64_t b, Pos p, Pos np) -> int64_t {
-            if (np.h != p.h) return blk_top + (np.h - first.h);
-            if (a.window < 0) return b - (int64_t)((p.q0 - s16) >> 5) * a.hq;
-            return b - (int64_t)(rw - (p.q0 - a.window - seq_start >= 32 ? 1 : 0)) * a.hq;
+            if (np.q0 == p.q0) return b + 1;
+            return b - (int64_t)((p.q0 - s16) >> 5) * a.hq - (GS - 1);
         };
         int64_t bc = blk_top, bn = blk_top;   // blocks of pc and pn
         if (A.ds && nsteps > 1) bn = blk_next(blk_top, first, pn);
