@@ -1367,7 +1367,6 @@ static int dkv_splits(int hq, int hkv, int window)
 {
     const int G = hq / hkv;
     if (window >= 0) return 1;
-    if (G % 4 == 0 && G >= 8) return 4;
     if (G % 2 == 0 && G >= 4) return 2;
     return 1;
 }

@@ -30,8 +30,6 @@ def k_lo(q0, seq_start, window):
 def splits_for(G, window):
     if window >= 0:
         return 1
-    if G % 4 == 0 and G >= 8:
-        return 4
     if G % 2 == 0 and G >= 4:
         return 2
     return 1
