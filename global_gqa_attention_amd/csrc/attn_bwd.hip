@@ -1362,19 +1362,21 @@ hipError_t launch_zero_f32(float *p, int n, hipStream_t stream)
 // (bf16), dk|dv partials when splits > 1, and for the stored-dS path the block index and the dS blocks; each
 // part 256-byte aligned
 // Causal layers with large groups split each key tile's query heads over several workgroups, so that the
-// first key tiles of a long sequence (which every later query sees) do not set the kernel's length alone.
-static int dkv_splits(int hq, int hkv, int window)
+// first key tiles of a long sequence (which every later query sees) do not set the kernel's length alone:
+// two splits where the 128-key tiles of all KV heads number 1024 or more (2048 workgroups, eight per CU),
+// else four where the group allows (the per-GPU shapes of a head split: one or two KV heads).
+static int dkv_splits(int T, int hq, int hkv, int window)
 {
     const int G = hq / hkv;
-    if (window >= 0) return 1;
-    if (G % 2 == 0 && G >= 4) return 2;
-    return 1;
+    if (window >= 0 || G % 2 || G < 4) return 1;
+    const long tiles = ((long)T + NKB - 1) / NKB * hkv;
+    return tiles >= 1024 || G % 4 ? 2 : 4;
 }
 
 size_t bwd_workspace_bytes(int T, int hq, int hkv, int window)
 {
     const size_t tp = (size_t)prep_tpad(T);
-    const int sp = dkv_splits(hq, hkv, window);
+    const int sp = dkv_splits(T, hq, hkv, window);
     return 2 * al(tp * hq * 4) + al(tp * hq * DQK * 2) + al(tp * hkv * DQK * 2) + al(tp * hkv * DQK * 2) +
            (sp > 1 ? al((size_t)sp * tp * hkv * (DQK + DVV) * 4) : 0);
 }
@@ -1412,7 +1414,7 @@ void bwd_carve(void *ws, int T, int hq, int hkv, BwdArgs *A, bool stored_ds, int
     p += al(tp * hkv * DQK * 2);
     A->W.krt = (u16 *)p;
     p += al(tp * hkv * DQK * 2);
-    A->splits = dkv_splits(hq, hkv, A->L.window);
+    A->splits = dkv_splits(T, hq, hkv, A->L.window);
     A->dkv_part = A->splits > 1 ? (float *)p : nullptr;
     if (A->splits > 1) p += al((size_t)A->splits * tp * hkv * (DQK + DVV) * 4);
     A->ds = nullptr;

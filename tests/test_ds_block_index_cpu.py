@@ -27,18 +27,18 @@ def k_lo(q0, seq_start, window):
     return max(0, q0 - window - seq_start) // 32 if window >= 0 else 0
 
 
-def splits_for(G, window):
-    if window >= 0:
-        return 1
-    if G % 2 == 0 and G >= 4:
-        return 2
-    return 1
+def split_counts(G):
+    """The head-split counts the causal kernel can choose for a group of G query heads (attn_bwd.hip:
+    dkv_splits; which one depends on the number of key tiles)."""
+    if G % 2 or G < 4:
+        return [1]
+    return [2, 4] if G % 4 == 0 else [2]
 
 
-def walk(seq_start, seq_end, tile, kq, window, hq, hkv, kvh, split, ds_seq):
+def walk(seq_start, seq_end, tile, kq, window, hq, hkv, kvh, split, ds_seq, splits):
     """Every step of one score wave: assert the carried index equals the closed form; returns the count."""
     G = hq // hkv
-    GS = G // splits_for(G, window)
+    GS = G // splits
     kb0 = seq_start + tile * NKB
     kb_last = min(kb0 + NKB - 1, seq_end - 1)
     q_lo = kb0 & ~15
@@ -89,7 +89,6 @@ def test_carried_block_index_matches_layout(hq, hkv):
     window = -1
     rng = np.random.default_rng(999 + 7 * hq + hkv)
     G = hq // hkv
-    sp = splits_for(G, window)
     steps = 0
     for _ in range(6):
         seq_start = int(rng.integers(0, 5000))
@@ -99,6 +98,7 @@ def test_carried_block_index_matches_layout(hq, hkv):
         for tile in range(ntiles):
             for kq in range(4):
                 kvh = int(rng.integers(0, hkv))
-                split = int(rng.integers(0, sp))
-                steps += walk(seq_start, seq_end, tile, kq, window, hq, hkv, kvh, split, ds_seq)
+                for sp in split_counts(G):
+                    split = int(rng.integers(0, sp))
+                    steps += walk(seq_start, seq_end, tile, kq, window, hq, hkv, kvh, split, ds_seq, sp)
     assert steps > 0
