@@ -60,6 +60,8 @@ def _run_bwd(ga, d, O, L, dO, path="fast", q_rot=None, k_rot=None):
     ([33, 1, 31, 47, 16, 17], 32, 8, 3, 1e4, True),
     ([129, 64, 250], 64, 4, 128, 1e4, True),    # 16 heads per KV head on a sliding-window layer
     ([300, 77], 64, 2, -1, 1e7, False),         # 32 heads per KV head on a causal layer
+    ([200, 131, 67], 16, 2, 63, 1e4, True),     # windows near 64: the two halves of a key tile see
+    ([190, 300], 16, 2, 65, 1e4, True),         # query ranges 64 apart, so their tile spans just touch
 ])
 @pytest.mark.parametrize("path", ["fast", "least"])
 def test_bwd_small_full(lengths, hq, hkv, window, base, sink, path):
