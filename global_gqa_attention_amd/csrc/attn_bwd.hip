@@ -24,7 +24,9 @@
 //                 dP = dO V^T, P and dS, then dV^T += dO^T P and dK^T += Q'^T dS.  The q' and dO row tiles and
 //                 LSE/D stream HBM -> LDS with global_load_lds (three-stage ring, XOR-swizzled); the
 //                 transposed operands of dV and dK come from the same tiles through ds_read_b64_tr_b16.
-//                 With the stored-dS workspace it also writes every dS block it computes.
+//                 Causal layers walk query tiles outer and the workgroup's heads inner; with a window the
+//                 two halves of the key tile each walk only the tiles their keys see, one tile each per
+//                 stage.  With the stored-dS workspace it also writes every dS block it computes.
 //   5. bwd_dq:    either from the stored dS blocks (5b: dQ^T += K'^T dS^T, no recomputation; one query tile of
 //                 up to sixteen heads per workgroup, which share each k' tile), or
 //                 query-major like the forward: S^T = K'Q'^T, P^T, dP^T = V dO^T, dS^T, then
