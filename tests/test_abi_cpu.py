@@ -316,3 +316,22 @@ def test_m0_guard_of_the_build():
     assert _m0_misuse("\ts_mov_b32 m0, -1\n\tds_read_b32 v1, v2\n") == ["s_mov_b32 m0, -1"]
     assert _m0_misuse("\ts_mov_b32 m0, s4\n\ts_nop 0\n\tds_gws_init v1\n") == ["s_mov_b32 m0, s4"]
     assert _m0_misuse("\ts_mov_b32 s5, m0\n") == ["s_mov_b32 s5, m0"]
+
+
+def test_causal_backward_head_split_rule(L):
+    """The causal backward's fp32 dK/dV partials (the only part of its workspace that a sliding-window layer
+    does not have) follow the head-split rule: two splits where the 128-key tiles of all KV heads number at
+    least 1024, four below that, none for groups under four query heads."""
+    def tpad(T):
+        return (T + 15) // 16 * 16 + 64
+
+    def al(n):
+        return (n + 255) // 256 * 256
+
+    for T, hq, hkv in [(32768, 64, 4), (65536, 64, 4), (16384, 64, 4), (32768, 16, 1), (32768, 16, 2),
+                       (4000, 64, 8), (131072, 16, 1), (32768, 12, 4), (32768, 24, 4)]:
+        G = hq // hkv
+        tiles = -(-T // 128) * hkv
+        splits = 1 if G % 2 or G < 4 else (2 if tiles >= 1024 or G % 4 else 4)
+        part = L.mimo_attn_bwd_workspace_size(T, hq, hkv, -1) - L.mimo_attn_bwd_workspace_size(T, hq, hkv, 128)
+        assert part == (al(splits * tpad(T) * hkv * 1280) if splits > 1 else 0), (T, hq, hkv, splits)
