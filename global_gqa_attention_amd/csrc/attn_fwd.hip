@@ -276,17 +276,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
                 if (s + KA < 12) kop[s % KA] = ld16(kt + (kr_ * KCH + kpos(kr_, 2 * (s + KA) + hh)) * 8);
             }
             // V^T operand m = 2 i + s (rows 32 i + c, k-step s); KA == 12: all eight read before the softmax,
-            // else two at a time during the P V MFMAs (fewer registers)
+            // else the first two before it (they land while the softmax runs) and the rest two ahead of the
+            // P V MFMAs (fewer registers)
             auto vread = [&](int m) {
                 const int d = 32 * (m >> 1) + c;
                 return ld16(vtt + (d * VCH + vpos<BN>(d, 4 * kb + 2 * (m & 1) + hh)) * 8);
             };
             constexpr int VA = KA == 12 ? 8 : 2;
             bf16x8 vop[VA];
-            if constexpr (VA == 8) {
 #pragma unroll
-                for (int m = 0; m < 8; ++m) vop[m] = vread(m);
-            }
+            for (int m = 0; m < VA; ++m) vop[m] = vread(m);
             __builtin_amdgcn_sched_barrier(0);
             float sv[16];
             float mxa = -INFINITY, mxb = -INFINITY;
@@ -332,10 +331,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_fwd_kernel(const FwdArgs A)
             l_run += ps0 + ps1;
             const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3])),
                                   __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]))};
-            if constexpr (VA < 8) {
-#pragma unroll
-                for (int m = 0; m < VA; ++m) vop[m] = vread(m);
-            }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 o[m >> 1] = mfma32(vop[m % VA], pf[m & 1], o[m >> 1]);
